@@ -1,0 +1,173 @@
+"""Gated DeltaNet layer on MI355X (gfx950): Python binding of libgdn.so.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI (``include/gdn.h``).  PyTorch provides device memory and the
+current stream.  The names mirror the C entry points:
+
+* ``gdn_chunk_fwd_workspace_size(n_seqs, total_tokens, h_qk, h_v)``
+* ``gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace)``
+* ``gdn_chunk_fwd_stages(..., stage_mask)`` (prep = 1, state = 2, out = 4)
+* ``gdn_recurrent_step(q, k, v, g, beta, n_requests, tokens_per_request, state_in,
+  state_out, out, intermediate_states, save_intermediate_states)``
+
+There is no fallback: if ``libgdn.so`` is missing or a call fails, a
+``GDNError`` is raised.  Build the library with
+``python -m hybrid_linear_attention_gdn_amd.build``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_SUCCESS = 0
+GDN_ERR_INVALID_VALUE = 1
+GDN_ERR_NOT_SUPPORTED = 2
+GDN_ERR_MISALIGNED = 3
+GDN_ERR_WORKSPACE = 4
+GDN_ERR_LAUNCH = 5
+
+EXPORTED_SYMBOLS = (
+    "gdn_chunk_fwd_workspace_size",
+    "gdn_chunk_fwd",
+    "gdn_chunk_fwd_stages",
+    "gdn_recurrent_step",
+    "gdn_status_string",
+    "gdn_get_last_error",
+)
+
+
+class GDNError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class gdn_dims(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32),
+                ("total_tokens", ctypes.c_int64),
+                ("n_heads_qk", ctypes.c_int32),
+                ("n_heads_v", ctypes.c_int32),
+                ("d_k", ctypes.c_int32),
+                ("d_v", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise GDNError(-1, f"{path} not found: build it with `python -m hybrid_linear_attention_gdn_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, c32, c64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    dims_p = ctypes.POINTER(gdn_dims)
+    lib.gdn_chunk_fwd_workspace_size.argtypes = [dims_p, ctypes.POINTER(sz)]
+    lib.gdn_chunk_fwd_workspace_size.restype = ctypes.c_int
+    lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, dims_p, vp, sz, vp]
+    lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_stages.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, dims_p, vp, sz, ctypes.c_int, vp]
+    lib.gdn_chunk_fwd_stages.restype = ctypes.c_int
+    lib.gdn_recurrent_step.argtypes = [vp, vp, vp, vp, vp, c32, c32, vp, vp, vp, vp, ctypes.c_int, dims_p, vp]
+    lib.gdn_recurrent_step.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_get_last_error.argtypes = []
+    lib.gdn_get_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(lib, status: int, what: str) -> None:
+    if status != GDN_SUCCESS:
+        name = lib.gdn_status_string(status).decode()
+        detail = lib.gdn_get_last_error().decode()
+        raise GDNError(status, f"{what}: {name}: {detail}")
+
+
+def _ptr(x) -> Optional[int]:
+    """Device address of a tensor, an int address as is, None for NULL."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream, *tensors) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    for t in tensors:
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def make_dims(n_seqs: int, total_tokens: int, h_qk: int, h_v: int, d_k: int = 128, d_v: int = 128) -> gdn_dims:
+    return gdn_dims(int(n_seqs), int(total_tokens), int(h_qk), int(h_v), int(d_k), int(d_v))
+
+
+def gdn_chunk_fwd_workspace_size(n_seqs: int, total_tokens: int, h_qk: int, h_v: int,
+                                 d_k: int = 128, d_v: int = 128) -> int:
+    lib = load_library()
+    dims = make_dims(n_seqs, total_tokens, h_qk, h_v, d_k, d_v)
+    out = ctypes.c_size_t(0)
+    _check(lib, lib.gdn_chunk_fwd_workspace_size(ctypes.byref(dims), ctypes.byref(out)),
+           "gdn_chunk_fwd_workspace_size")
+    return int(out.value)
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace,
+                  *, dims: Optional[gdn_dims] = None, workspace_bytes: Optional[int] = None,
+                  stream=None) -> None:
+    """Chunked prefill.  Tensors are device tensors (or raw int addresses with ``dims``)."""
+    lib = load_library()
+    if dims is None:
+        dims = make_dims(cu_seqlens.shape[0] - 1, q.shape[0], q.shape[1], v.shape[1], q.shape[2], v.shape[2])
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                           _ptr(initial_state), _ptr(out), _ptr(final_state), ctypes.byref(dims),
+                           _ptr(workspace), int(workspace_bytes),
+                           _stream(stream, q, out, cu_seqlens))
+    _check(lib, st, "gdn_chunk_fwd")
+
+
+def gdn_chunk_fwd_stages(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace,
+                         stage_mask: int, *, dims: Optional[gdn_dims] = None,
+                         workspace_bytes: Optional[int] = None, stream=None) -> None:
+    """Selected stages of the chunked prefill (1 = prep, 2 = state, 4 = out)."""
+    lib = load_library()
+    if dims is None:
+        dims = make_dims(cu_seqlens.shape[0] - 1, q.shape[0], q.shape[1], v.shape[1], q.shape[2], v.shape[2])
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_chunk_fwd_stages(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                  _ptr(initial_state), _ptr(out), _ptr(final_state), ctypes.byref(dims),
+                                  _ptr(workspace), int(workspace_bytes), int(stage_mask),
+                                  _stream(stream, q, out, cu_seqlens))
+    _check(lib, st, "gdn_chunk_fwd_stages")
+
+
+def gdn_recurrent_step(q, k, v, g, beta, n_requests: int, tokens_per_request: int,
+                       state_in, state_out, out, intermediate_states, save_intermediate_states: bool,
+                       *, dims: Optional[gdn_dims] = None, stream=None) -> None:
+    """Per-token update for decode / speculative verify (see include/gdn.h)."""
+    lib = load_library()
+    if dims is None:
+        dims = make_dims(n_requests, n_requests * tokens_per_request, q.shape[1], v.shape[1],
+                         q.shape[2], v.shape[2])
+    st = lib.gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                int(n_requests), int(tokens_per_request),
+                                _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(intermediate_states),
+                                1 if save_intermediate_states else 0, ctypes.byref(dims),
+                                _stream(stream, q, state_in, out))
+    _check(lib, st, "gdn_recurrent_step")

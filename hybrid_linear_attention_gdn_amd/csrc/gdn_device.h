@@ -1,0 +1,109 @@
+// Device-side definitions shared by the gfx950 Gated DeltaNet kernels.
+//
+// Matrix-core tiles use v_mfma_f32_16x16x32_f16 (wave64).  Operand fragment
+// of that instruction: lane l holds 8 values of row/column (l % 16) for the
+// 8 contraction slots of lane group (l / 16).  Accumulator: lane l holds rows
+// 4 * (l / 16) + e, e = 0..3, of column (l % 16).  A contraction index may be
+// permuted freely as long as both operands use the same permutation; the
+// kernels use that to feed accumulators back as operands without an LDS
+// round trip (see the slot maps below).
+//
+// bfloat16 inputs are widened to fp16 on load.  Every bf16 value in
+// [2^-14, 65504] is exact in fp16 (8 significant bits fit in 11); smaller
+// magnitudes lose at most 2^-25 absolutely.  fp16 operands keep derived
+// quantities (the UT-transform rows, corrected writes U', chunk states) to an
+// 11-bit mantissa, where bf16 would carry only 8: in a numerical model of the
+// chunkwise form bf16 operands cost ~2.8e-3 relative L2 on outputs and
+// ~2.1e-3 on states, fp16 ~3.5e-4 on both.  fp16 and bf16 share the MFMA
+// peak rate on CDNA4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kChunk = 64;  // tokens per chunk
+constexpr int kDim = 128;   // d_k = d_v
+
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+// Per (chunk slot, value head) element counts of the workspace regions.
+constexpr size_t kWElems = 16 * 64 * 8;    // -W, A-operand fragments [p][qq][lane][8]
+constexpr size_t kUElems = 8 * 4 * 64 * 4;  // U, accumulator fragments [ct][p][lane][4]
+constexpr size_t kUpElems = 8 * 2 * 64 * 8; // U', B-operand fragments [ct][qq][lane][8]
+constexpr size_t kHcElems = 8 * 4 * 64 * 8; // chunk state, B-operand fragments [ct][qq][lane][8]
+constexpr size_t kGElems = 64;              // decay cumsum
+
+struct ChunkWorkspace {
+    f16* w;
+    f16* u;
+    f16* up;
+    f16* hc;
+    float* gcum;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(u16x8 b) {
+    f16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = static_cast<f16>(bf16_to_f32(b[i]));
+    return r;
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// exp(x) through the hardware base-2 exponential; used for decay factors
+// exp(G_r - G_s) with non-positive arguments (relative error ~1e-6).
+__device__ __forceinline__ float exp_f(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+__device__ __forceinline__ f16x8 cat_to_f16(f32x4 lo, f32x4 hi) {
+    f16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = static_cast<f16>(lo[e]);
+        r[e + 4] = static_cast<f16>(hi[e]);
+    }
+    return r;
+}
+
+// Chunk slots.  Sequence n owns slots n + cu[n] / 64 ... + ceil(len_n / 64) - 1;
+// consecutive sequences never overlap because the base grows by at least
+// 1 + floor(len_n / 64) >= ceil(len_n / 64).  Slots in the gaps are unused.
+// The slot count needed is at most N + T / 64 + 1, known on the host.
+__device__ __forceinline__ int slot_base(const int32_t* cu, int n) {
+    return n + cu[n] / kChunk;
+}
+
+// Map a chunk slot to (sequence, first token, length).  Returns false for an
+// unused slot.  Every thread computes the same answer (uniform loads).
+__device__ __forceinline__ bool resolve_slot(const int32_t* __restrict__ cu, int n_seqs, int slot,
+                                             int& seq, int& t0, int& len) {
+    int lo = 0, hi = n_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (slot_base(cu, mid) <= slot) lo = mid; else hi = mid - 1;
+    }
+    const int c = slot - slot_base(cu, lo);
+    const int start = cu[lo], end = cu[lo + 1];
+    const int first = start + c * kChunk;
+    if (c < 0 || first >= end) return false;
+    seq = lo;
+    t0 = first;
+    len = min(kChunk, end - first);
+    return true;
+}
+
+}  // namespace gdn

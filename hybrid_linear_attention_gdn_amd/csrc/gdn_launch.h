@@ -1,0 +1,25 @@
+// Host-side launchers of the gfx950 kernels (called by the C ABI layer).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_device.h"
+
+namespace gdn {
+
+// Enqueues prep, state and output kernels of the chunked prefill on `stream`.
+hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const float* g, const float* beta, const int32_t* cu,
+                            int n_seqs, int64_t total_tokens, int h_qk, int h_v,
+                            const float* s0, float* out, float* s_final,
+                            const ChunkWorkspace& ws, int n_slots, int stage_mask,
+                            hipStream_t stream);
+
+// Enqueues the per-token recurrent update on `stream`.
+hipError_t launch_recurrent_step(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const float* g, const float* beta, int n_req, int n_tok,
+                                 int h_qk, int h_v, const float* s_in, float* s_out,
+                                 float* out, float* inter, int save, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,171 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet layer library, libgdn.so.
+ *
+ * The layer is the gated delta rule (Yang, Kautz, Hatamizadeh, "Gated Delta
+ * Networks: Improving Mamba2 with Delta Rule", ICLR 2025).  For every
+ * sequence and value head, with state S (d_v x d_k), alpha_t = exp(g_t):
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t.
+ *
+ * The pages this library follows use it as the linear-attention layer of a
+ * hybrid model: the "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page, section
+ * 2 ("GDN prefill"), runs the prefill chunkwise with chunk length 64 in three
+ * stages (intra-chunk preparation, inter-chunk state recurrence, output), the
+ * entry point gdn_chunk_fwd below; its section 1 describes the speculative
+ * verify step of 1 + K query tokens per request, and the "Qwen3.8-27B on one
+ * RTX 3090" page keeps a fixed-size recurrent state per request plus one
+ * state snapshot per speculative token (section on the 131,072-token limit),
+ * the entry point gdn_recurrent_step below.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, owned
+ *    by the caller.  The library allocates nothing, keeps no device state and
+ *    is re-entrant; calls are asynchronous on `stream` (a hipStream_t, NULL =
+ *    the default stream).
+ *  - Layouts are dense, row-major, token-major:
+ *      q, k : [T, H_qk, d_k]  bfloat16      v : [T, H_v, d_v]  bfloat16
+ *      g    : [T, H_v] float32 natural-log decay (alpha = exp(g), g <= 0)
+ *      beta : [T, H_v] float32
+ *      out  : [T, H_v, d_v] float32
+ *      state: [N, H_v, d_k, d_v] float32, element [a][b] = S[b][a] (d_v contiguous)
+ *    Value head h reads q/k head h / (H_v / H_qk) (contiguous groups).
+ *  - Every pointer must be 16-byte aligned (GDN_ERR_MISALIGNED otherwise).
+ *  - Supported sizes: d_k = d_v = 128; H_v a positive multiple of H_qk.
+ *    Other head dims return GDN_ERR_NOT_SUPPORTED.
+ *  - Validation reads only host values (no device reads, no synchronisation).
+ *    Device-content preconditions are documented, not checked: cu_seqlens is
+ *    nondecreasing with cu_seqlens[0] = 0 and cu_seqlens[N] = T; g <= 0; all
+ *    inputs finite and, since matrix-core operands are fp16, |q|, |k|, |v|
+ *    below 65504 and states and outputs well inside fp16 range.
+ *  - Errors: a gdn_status is returned, no exception crosses the ABI, nothing
+ *    is printed, nothing aborts.  gdn_get_last_error() gives the detail of
+ *    the calling thread's last failure.  There is no fallback path: a
+ *    failed launch returns GDN_ERR_LAUNCH with the HIP error text.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_SUCCESS = 0,
+    GDN_ERR_INVALID_VALUE = 1, /* null pointer, negative or inconsistent size */
+    GDN_ERR_NOT_SUPPORTED = 2, /* head dims other than 128 */
+    GDN_ERR_MISALIGNED = 3,    /* a pointer is not 16-byte aligned */
+    GDN_ERR_WORKSPACE = 4,     /* workspace missing or smaller than required */
+    GDN_ERR_LAUNCH = 5         /* HIP reported an error at launch */
+} gdn_status;
+
+/* Host-side problem sizes.  n_seqs and total_tokens are host copies of
+ * what cu_seqlens holds on the device (N and cu_seqlens[N]). */
+typedef struct {
+    int32_t n_seqs;
+    int64_t total_tokens;
+    int32_t n_heads_qk;
+    int32_t n_heads_v;
+    int32_t d_k;
+    int32_t d_v;
+} gdn_dims;
+
+/*
+ * Workspace bytes gdn_chunk_fwd needs for `dims` (device memory the caller
+ * allocates; contents undefined before and after a call).  It holds the
+ * intra-chunk products of the chunkwise form (W, U, corrected U', the
+ * per-chunk incoming states and the decay cumsums), one 64-token chunk slot
+ * per chunk: at most N + T/64 + 1 slots, about 82 KB per slot and value head.
+ */
+gdn_status gdn_chunk_fwd_workspace_size(const gdn_dims* dims, size_t* bytes);
+
+/*
+ * Chunked prefill (chunk length 64) over a packed batch of N sequences
+ * (tokens cu_seqlens[n] .. cu_seqlens[n+1]-1).  Follows the three-stage split
+ * of the "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page, section 2:
+ *   gdn_chunk_prep  -- decay cumsum, masked K K^T, (I + A)^{-1}, W and U;
+ *   gdn_chunk_state -- inter-chunk recurrence, state held in matrix-core
+ *                      accumulators, next chunk prefetched;
+ *   gdn_chunk_out   -- intra-chunk causal term plus Q S.
+ *  q, k, v       bf16 device tensors, layouts above.
+ *  g, beta       float32 [T, H_v].
+ *  cu_seqlens    int32 [N + 1], device.
+ *  initial_state float32 [N, H_v, d_k, d_v] or NULL (zeros).
+ *  out           float32 [T, H_v, d_v], written for every token.
+ *  final_state   float32 [N, H_v, d_k, d_v] or NULL (not written); may alias
+ *                initial_state (in-place state update).
+ *  workspace     device buffer of at least gdn_chunk_fwd_workspace_size bytes.
+ * Empty sequences are allowed (their final state equals the initial state).
+ */
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
+                         const float* g, const float* beta,
+                         const int32_t* cu_seqlens,
+                         const float* initial_state,
+                         float* out,
+                         float* final_state,
+                         const gdn_dims* dims,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Runs only the selected stages of gdn_chunk_fwd, for callers that time or
+ * schedule the stages one by one.  stage_mask bits: 1 = gdn_chunk_prep,
+ * 2 = gdn_chunk_state, 4 = gdn_chunk_out (7 = gdn_chunk_fwd).  A stage reads
+ * what earlier stages left in the same workspace; run them in order, on the
+ * same inputs and workspace, or the results are undefined (memory accesses
+ * stay in bounds regardless, since every index comes from cu_seqlens and the
+ * launch grid, never from workspace contents).  Arguments as gdn_chunk_fwd;
+ * a mask outside 1..7 returns GDN_ERR_INVALID_VALUE.
+ */
+gdn_status gdn_chunk_fwd_stages(const void* q, const void* k, const void* v,
+                                const float* g, const float* beta,
+                                const int32_t* cu_seqlens,
+                                const float* initial_state,
+                                float* out,
+                                float* final_state,
+                                const gdn_dims* dims,
+                                void* workspace, size_t workspace_bytes,
+                                int stage_mask,
+                                void* stream);
+
+/*
+ * Per-token recurrent update for decode (tokens_per_request = 1) and
+ * speculative verify (1 + K tokens per request).  Requests are packed
+ * request-major: token i of request r is row r * tokens_per_request + i of
+ * q, k, v, g, beta and out.  dims->n_seqs must equal n_requests and
+ * dims->total_tokens must equal n_requests * tokens_per_request.
+ *  state_in            float32 [R, H_v, d_k, d_v]; read only.
+ *  state_out           float32 [R, H_v, d_k, d_v], the state after the last
+ *                      token; may alias state_in; may be NULL only when
+ *                      save_intermediate_states is nonzero.
+ *  out                 float32 [R * n, H_v, d_v].
+ *  intermediate_states float32 [R, n, H_v, d_k, d_v]: slot [r][i] is the
+ *                      state right after token i of request r, the rollback
+ *                      point if the verifier accepts exactly i + 1 tokens.
+ *                      Required iff save_intermediate_states is nonzero.
+ */
+gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v,
+                              const float* g, const float* beta,
+                              int32_t n_requests, int32_t tokens_per_request,
+                              const float* state_in,
+                              float* state_out,
+                              float* out,
+                              float* intermediate_states,
+                              int save_intermediate_states,
+                              const gdn_dims* dims,
+                              void* stream);
+
+/* Static text for a status code. */
+const char* gdn_status_string(gdn_status s);
+
+/* Detail of the calling thread's last failing call ("" if none). */
+const char* gdn_get_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

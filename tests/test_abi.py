@@ -1,0 +1,213 @@
+"""C-ABI tests that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch.
+
+Only failing-validation paths are exercised here (plus the pure host
+workspace-size query and the zero-sequence no-op); no call in this file
+reaches a kernel launch, so fake device addresses are safe.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import hybrid_linear_attention_gdn_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+FAKE = 0x7f0000000000          # 16-byte aligned fake device address (never dereferenced)
+MIS = FAKE + 4                 # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        import hybrid_linear_attention_gdn_amd.build as b
+        b.build()
+    return gdn.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(gdn.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_exported_symbols_have_c_linkage():
+    out = os.popen(f"nm -D --defined-only {gdn.LIB_PATH}").read()
+    names = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in names, f"{name} not exported unmangled"
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.gdn_status_string(s)
+    assert lib.gdn_status_string(99) == b"unknown status"
+
+
+def dims(n=1, T=64, hqk=2, hv=4, dk=128, dv=128):
+    return gdn.make_dims(n, T, hqk, hv, dk, dv)
+
+
+def ws_size(lib, d):
+    out = ctypes.c_size_t(0)
+    st = lib.gdn_chunk_fwd_workspace_size(ctypes.byref(d), ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_formula(lib):
+    st, b = ws_size(lib, dims(n=1, T=4000, hqk=16, hv=32))
+    assert st == 0
+    slots = 1 + 4000 // 64 + 1
+    per = (8192 + 8192 + 8192 + 16384) * 2 + 64 * 4
+    assert b >= slots * 32 * per
+    assert b < slots * 32 * per + 5 * 256
+
+
+@pytest.mark.parametrize("d,code", [
+    (dims(dk=64, dv=64), gdn.GDN_ERR_NOT_SUPPORTED),
+    (dims(dk=128, dv=64), gdn.GDN_ERR_NOT_SUPPORTED),
+    (dims(hqk=3, hv=4), gdn.GDN_ERR_INVALID_VALUE),
+    (dims(hqk=0), gdn.GDN_ERR_INVALID_VALUE),
+    (dims(n=-1), gdn.GDN_ERR_INVALID_VALUE),
+    (dims(T=-5), gdn.GDN_ERR_INVALID_VALUE),
+    (dims(n=0, T=10), gdn.GDN_ERR_INVALID_VALUE),
+    (dims(T=2**31), gdn.GDN_ERR_INVALID_VALUE),
+    (dims(dk=0), gdn.GDN_ERR_INVALID_VALUE),
+])
+def test_workspace_size_rejects_bad_dims(lib, d, code):
+    st, _ = ws_size(lib, d)
+    assert st == code
+    assert lib.gdn_get_last_error()
+
+
+def test_workspace_size_null_args(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_workspace_size(None, ctypes.byref(out)) == gdn.GDN_ERR_INVALID_VALUE
+    d = dims()
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(d), None) == gdn.GDN_ERR_INVALID_VALUE
+
+
+def chunk_call(lib, d, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, s0=None, out=FAKE, fin=None,
+                ws=FAKE, wsb=None)
+    args.update(over)
+    if args["wsb"] is None:
+        args["wsb"] = ws_size(lib, d)[1]
+    return lib.gdn_chunk_fwd(args["q"], args["k"], args["v"], args["g"], args["beta"], args["cu"],
+                             args["s0"], args["out"], args["fin"], ctypes.byref(d), args["ws"],
+                             args["wsb"], None)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "cu", "out"])
+def test_chunk_fwd_rejects_null(lib, name):
+    assert chunk_call(lib, dims(), **{name: None}) == gdn.GDN_ERR_INVALID_VALUE
+    assert name.replace("cu", "cu_seqlens") in lib.gdn_get_last_error().decode()
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "cu", "out", "s0", "fin"])
+def test_chunk_fwd_rejects_misaligned(lib, name):
+    assert chunk_call(lib, dims(), **{name: MIS}) == gdn.GDN_ERR_MISALIGNED
+
+
+def test_chunk_fwd_workspace_checks(lib):
+    d = dims()
+    assert chunk_call(lib, d, ws=None) == gdn.GDN_ERR_WORKSPACE
+    need = ws_size(lib, d)[1]
+    assert chunk_call(lib, d, wsb=need - 1) == gdn.GDN_ERR_WORKSPACE
+    assert chunk_call(lib, d, ws=FAKE + 16) == gdn.GDN_ERR_MISALIGNED
+
+
+def test_chunk_fwd_rejects_unsupported_dims(lib):
+    assert chunk_call(lib, dims(dk=64, dv=64), wsb=1 << 30) == gdn.GDN_ERR_NOT_SUPPORTED
+    assert chunk_call(lib, dims(hqk=3, hv=4), wsb=1 << 30) == gdn.GDN_ERR_INVALID_VALUE
+
+
+def test_chunk_fwd_zero_sequences_is_a_noop(lib):
+    d = dims(n=0, T=0)
+    assert chunk_call(lib, d, q=None, k=None, v=None, g=None, beta=None, cu=None, out=None,
+                      ws=None, wsb=0) == gdn.GDN_SUCCESS
+    assert lib.gdn_get_last_error() == b""
+
+
+def step_call(lib, d, R=2, n=3, save=1, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s_in=FAKE, s_out=FAKE, out=FAKE,
+                inter=FAKE if save else None)
+    args.update(over)
+    return lib.gdn_recurrent_step(args["q"], args["k"], args["v"], args["g"], args["beta"], R, n,
+                                  args["s_in"], args["s_out"], args["out"], args["inter"], save,
+                                  ctypes.byref(d), None)
+
+
+def sdims(R=2, n=3, **kw):
+    return dims(n=R, T=R * n, **kw)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "s_in", "out"])
+def test_recurrent_step_rejects_null(lib, name):
+    assert step_call(lib, sdims(), **{name: None}) == gdn.GDN_ERR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "s_in", "s_out", "out", "inter"])
+def test_recurrent_step_rejects_misaligned(lib, name):
+    assert step_call(lib, sdims(), **{name: MIS}) == gdn.GDN_ERR_MISALIGNED
+
+
+def test_recurrent_step_save_flag_consistency(lib):
+    assert step_call(lib, sdims(), save=1, inter=None) == gdn.GDN_ERR_INVALID_VALUE
+    assert step_call(lib, sdims(), save=0, inter=FAKE) == gdn.GDN_ERR_INVALID_VALUE
+    assert step_call(lib, sdims(), save=0, s_out=None) == gdn.GDN_ERR_INVALID_VALUE
+
+
+def test_recurrent_step_dims_must_match_counts(lib):
+    assert step_call(lib, dims(n=3, T=6)) == gdn.GDN_ERR_INVALID_VALUE
+    assert step_call(lib, dims(n=2, T=7)) == gdn.GDN_ERR_INVALID_VALUE
+    assert lib.gdn_recurrent_step(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 3, FAKE, FAKE, FAKE, FAKE, 1,
+                                  ctypes.byref(dims(n=-1, T=0)), None) == gdn.GDN_ERR_INVALID_VALUE
+    assert step_call(lib, sdims(dk=64, dv=64)) == gdn.GDN_ERR_NOT_SUPPORTED
+
+
+def test_recurrent_step_zero_requests_is_a_noop(lib):
+    assert lib.gdn_recurrent_step(None, None, None, None, None, 0, 6, None, None, None, None, 0,
+                                  ctypes.byref(dims(n=0, T=0)), None) == gdn.GDN_SUCCESS
+
+
+def test_binding_raises_with_detail(lib):
+    with pytest.raises(gdn.GDNError) as e:
+        gdn.gdn_chunk_fwd_workspace_size(1, 64, 2, 4, 64, 64)
+    assert e.value.status == gdn.GDN_ERR_NOT_SUPPORTED
+    assert "128" in str(e.value)
+
+
+def test_last_error_is_thread_local(lib):
+    import threading
+    assert ws_size(lib, dims(dk=64, dv=64))[0] == gdn.GDN_ERR_NOT_SUPPORTED
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.gdn_get_last_error()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == b""
+    assert lib.gdn_get_last_error() != b""
+
+
+def test_stages_rejects_bad_mask(lib):
+    d = dims()
+    need = ws_size(lib, d)[1]
+    for mask in (0, 8, -1):
+        assert lib.gdn_chunk_fwd_stages(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                        ctypes.byref(d), FAKE, need, mask, None) == gdn.GDN_ERR_INVALID_VALUE

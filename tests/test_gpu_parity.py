@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Tolerances: relative L2 <= 2e-3 on outputs and <= 1e-3 on states (final and
+per-token snapshots), with bf16 q, k, v shared by both sides.  The oracle runs
+in fp64 on the same bf16-rounded inputs.
+"""
+
+import numpy as np
+import pytest
+
+import gdn_inputs as gi
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from gpu_util import OUT_TOL, STATE_TOL, DevInputs, chunk_fwd, recurrent_step, rel_l2  # noqa: E402
+
+
+def _print_case(name, x):
+    print(f"[case] {name}: N={x.n_seqs} T={x.total_tokens} Hqk={x.h_qk} Hv={x.h_v} "
+          f"lengths={list(map(int, x.lengths))[:12]}", flush=True)
+
+
+def check_chunk(x, name, poison=True, **kw):
+    _print_case(name, x)
+    d = DevInputs(x)
+    out, fin = chunk_fwd(d, poison=poison, **kw)
+    ro, rf, _ = oracle.forward_inputs(x, precision="f64")
+    o, f = out.cpu().numpy(), fin.cpu().numpy()
+    assert np.isfinite(o).all() and np.isfinite(f).all()
+    eo, ef = rel_l2(o, ro), rel_l2(f, rf)
+    print(f"[result] {name}: out rel-L2 {eo:.3e}  state rel-L2 {ef:.3e}", flush=True)
+    assert eo <= OUT_TOL, eo
+    assert ef <= STATE_TOL, ef
+    return out, fin
+
+
+# ------------------------------------------------------------ recurrent step
+
+def test_verify_8req_6tok_with_snapshots():
+    x = gi.verify_8x6()
+    _print_case("verify_8x6", x)
+    d = DevInputs(x)
+    out, s_out, inter = recurrent_step(d, 8, 6, save=True)
+    ro, rf, rs = oracle.forward_inputs(x, precision="f64", record_states=True)
+    assert rel_l2(out.cpu().numpy(), ro) <= OUT_TOL
+    assert rel_l2(s_out.cpu().numpy(), rf) <= STATE_TOL
+    snaps = inter.cpu().numpy().reshape(48, x.h_v, 128, 128)
+    assert rel_l2(snaps, rs) <= STATE_TOL
+    # every rollback slot individually
+    for t in range(48):
+        assert rel_l2(snaps[t], rs[t]) <= STATE_TOL
+    # the last snapshot of each request is its final state, bitwise
+    np.testing.assert_array_equal(inter[:, -1].cpu().numpy(), s_out.cpu().numpy())
+
+
+def test_decode_single_token_in_place():
+    x = gi.make_inputs([1] * 16, 16, 32, 128, 128, seed=5, state_std=0.02)
+    d = DevInputs(x)
+    s_ref = d.s0.clone()
+    out = torch.empty((16, 32, 128), dtype=torch.float32, device="cuda")
+    import hybrid_linear_attention_gdn_amd as gdn
+    gdn.gdn_recurrent_step(d.q, d.k, d.v, d.g, d.beta, 16, 1, d.s0, d.s0, out, None, False)
+    torch.cuda.synchronize()
+    ro, rf, _ = oracle.forward(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, s_ref.cpu().numpy())
+    assert rel_l2(out.cpu().numpy(), ro) <= OUT_TOL
+    assert rel_l2(d.s0.cpu().numpy(), rf) <= STATE_TOL
+
+
+@pytest.mark.parametrize("hqk,hv", [(1, 1), (2, 8), (4, 4)])
+def test_recurrent_step_head_groupings(hqk, hv):
+    x = gi.make_inputs([4] * 3, hqk, hv, 128, 128, seed=8, state_std=0.02)
+    d = DevInputs(x)
+    out, s_out, inter = recurrent_step(d, 3, 4, save=True)
+    ro, rf, rs = oracle.forward_inputs(x, record_states=True)
+    assert rel_l2(out.cpu().numpy(), ro) <= OUT_TOL
+    assert rel_l2(s_out.cpu().numpy(), rf) <= STATE_TOL
+    assert rel_l2(inter.cpu().numpy().reshape(rs.shape), rs) <= STATE_TOL
+
+
+# ------------------------------------------------------------ chunked prefill
+
+@pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 128, 200, 257])
+def test_chunk_small_lengths(T):
+    x = gi.make_inputs([T], 2, 4, 128, 128, seed=T, state_std=0.02)
+    check_chunk(x, f"small_T{T}")
+
+
+@pytest.mark.parametrize("hqk,hv", [(1, 1), (1, 4), (3, 6)])
+def test_chunk_head_groupings(hqk, hv):
+    x = gi.make_inputs([150, 64, 3], hqk, hv, 128, 128, seed=hv, state_std=0.02)
+    check_chunk(x, f"groups_{hqk}x{hv}")
+
+
+def test_chunk_prefill_4000():
+    x = gi.prefill_4000()
+    out, fin = check_chunk(x, "prefill_4000")
+    # NULL initial state and an explicit zero state give identical bits
+    d = DevInputs(x)
+    zeros = torch.zeros((1, 32, 128, 128), dtype=torch.float32, device="cuda")
+    out2, fin2 = chunk_fwd(d, initial_state=zeros)
+    assert torch.equal(out, out2) and torch.equal(fin, fin2)
+
+
+def test_chunk_varlen_8():
+    x = gi.varlen_8()
+    check_chunk(x, "varlen_8")
+
+
+def test_chunk_slow_decay():
+    check_chunk(gi.slow_decay(4000), "slow_decay_T4000")
+
+
+def test_chunk_no_decay_small_beta():
+    check_chunk(gi.no_decay_small_beta(4000), "no_decay_T4000")
+
+
+def test_chunk_k_scaled_reading():
+    """The alternative input reading (k also scaled by 1/sqrt(d_k)) passes the same gate."""
+    x = gi.make_inputs([1000, 300], 16, 32, 128, 128, seed=4, state_std=0.02, k_scale=True)
+    check_chunk(x, "k_scaled")
+
+
+def test_chunk_zero_length_sequences():
+    x = gi.make_inputs([0, 70, 0, 5, 0], 2, 4, 128, 128, seed=12, state_std=0.02)
+    out, fin = check_chunk(x, "zero_length")
+    f = fin.cpu().numpy()
+    for n in (0, 2, 4):
+        np.testing.assert_array_equal(f[n], x.initial_state[n])
+
+
+def test_chunk_all_sequences_empty():
+    x = gi.make_inputs([0, 0], 2, 4, 128, 128, seed=1, state_std=0.02)
+    d = DevInputs(x)
+    import hybrid_linear_attention_gdn_amd as gdn
+    fin = torch.full((2, 4, 128, 128), float("nan"), device="cuda")
+    out = torch.empty((0, 4, 128), device="cuda")
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(2, 0, 2, 4), dtype=torch.uint8, device="cuda")
+    gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.g, d.beta, d.cu, d.s0, out, fin, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(fin.cpu().numpy(), x.initial_state)
+
+
+def test_chunk_packed_equals_separate_bitwise():
+    x = gi.make_inputs([130, 64, 1, 700], 16, 32, 128, 128, seed=21, state_std=0.02)
+    out, fin = chunk_fwd(DevInputs(x))
+    for n in range(x.n_seqs):
+        y = x.slice_seq(n)
+        o, f = chunk_fwd(DevInputs(y))
+        a, b = int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1])
+        assert torch.equal(out[a:b], o)
+        assert torch.equal(fin[n:n + 1], f)
+
+
+def test_chunk_deterministic():
+    x = gi.make_inputs([1000, 77], 16, 32, 128, 128, seed=3, state_std=0.02)
+    d = DevInputs(x)
+    o1, f1 = chunk_fwd(d)
+    o2, f2 = chunk_fwd(d, poison=True)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_chunk_final_state_may_alias_initial():
+    x = gi.make_inputs([333, 65], 2, 4, 128, 128, seed=6, state_std=0.02)
+    d = DevInputs(x)
+    ref_out, ref_fin = chunk_fwd(d)
+    import hybrid_linear_attention_gdn_amd as gdn
+    from gpu_util import workspace_for
+    s = d.s0.clone()
+    out = torch.empty_like(ref_out)
+    gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.g, d.beta, d.cu, s, out, s, workspace_for(x))
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(s, ref_fin)
+
+
+def test_chunk_without_final_state():
+    x = gi.make_inputs([100], 2, 4, 128, 128, seed=9, state_std=0.02)
+    d = DevInputs(x)
+    ref_out, _ = chunk_fwd(d)
+    out, fin = chunk_fwd(d, want_final=False)
+    assert fin is None and torch.equal(out, ref_out)
+
+
+def test_chunk_writes_stay_in_bounds():
+    """Guard bands around out and final_state stay untouched (NaN-free, bit pattern kept)."""
+    x = gi.make_inputs([190, 3], 2, 4, 128, 128, seed=2, state_std=0.02)
+    d = DevInputs(x)
+    import hybrid_linear_attention_gdn_amd as gdn
+    from gpu_util import workspace_for
+    G = 4096
+    out_buf = torch.full((G + x.total_tokens * 4 * 128 + G,), 7.0, device="cuda")
+    fin_buf = torch.full((G + 2 * 4 * 128 * 128 + G,), 7.0, device="cuda")
+    out = out_buf[G:G + x.total_tokens * 4 * 128].view(x.total_tokens, 4, 128)
+    fin = fin_buf[G:G + 2 * 4 * 128 * 128].view(2, 4, 128, 128)
+    gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.g, d.beta, d.cu, d.s0, out, fin, workspace_for(x))
+    torch.cuda.synchronize()
+    for buf, n in ((out_buf, out.numel()), (fin_buf, fin.numel())):
+        assert torch.all(buf[:G] == 7.0) and torch.all(buf[G + n:] == 7.0)
+    ro, rf, _ = oracle.forward_inputs(x)
+    assert rel_l2(out.cpu().numpy(), ro) <= OUT_TOL
+    assert rel_l2(fin.cpu().numpy(), rf) <= STATE_TOL
+
+
+def test_recurrent_chain_matches_chunked():
+    """Two independent GPU paths agree on short sequences."""
+    x = gi.make_inputs([256], 16, 32, 128, 128, seed=14, state_std=0.02)
+    d = DevInputs(x)
+    co, cf = chunk_fwd(d)
+    ro, rf, _ = recurrent_step(d, 1, 256, save=False)
+    assert rel_l2(co.cpu().numpy(), ro.cpu().numpy()) <= OUT_TOL
+    assert rel_l2(cf.cpu().numpy(), rf.cpu().numpy()) <= STATE_TOL
+
+
+def test_long_context_131072_sampled():
+    """Full-size long-context prefill; the oracle checks sampled value heads over the
+    whole sequence and all heads over the first 2048 tokens."""
+    x = gi.long_131072()
+    _print_case("long_131072", x)
+    d = DevInputs(x)
+    out, fin = chunk_fwd(d)
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(fin).all())
+    heads = [0, 1, 22, 23]                    # two GVA pairs
+    qk = sorted({h // 2 for h in heads})
+    sub_q, sub_k = x.q[:, qk], x.k[:, qk]
+    ro, rf, _ = oracle.forward(sub_q, sub_k, x.v[:, heads], x.g[:, heads], x.beta[:, heads],
+                               x.cu_seqlens, None, precision="f64", n_threads=4)
+    o = out[:, heads].cpu().numpy()
+    f = fin[:, heads].cpu().numpy()
+    eo, ef = rel_l2(o, ro), rel_l2(f, rf)
+    print(f"[result] long_131072 heads {heads}: out {eo:.3e} state {ef:.3e}", flush=True)
+    assert eo <= OUT_TOL and ef <= STATE_TOL
+    P = 2048
+    po, _, _ = oracle.forward(x.q[:P], x.k[:P], x.v[:P], x.g[:P], x.beta[:P], [0, P], None)
+    assert rel_l2(out[:P].cpu().numpy(), po) <= OUT_TOL
