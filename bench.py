@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one chunked prefill (gdn_chunk_fwd: prep, state, out) of one GDN
+layer over T = 4000 tokens, 32 value heads / 16 q-k heads, d = 128, bf16
+inputs, fp32 state and output, zero initial state -- the one-layer,
+4000-token workload of the "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page,
+section 2.  Inputs are synthetic, seeded and resident in HBM before timing.
+
+Printed as one JSON line:
+  value      prefill tokens/s per layer over the K timed steps (warm, back to back)
+  roofline   the dominant prefill kernel: algorithmic work per launch / its
+             mean launch time (HIP events on the launch stream), vs MI355X peak
+  verify     the speculative-verify leg (8 requests x 6 tokens, per-token state
+             snapshots kept) timed the same way, as a fraction of HBM bandwidth
+  cpu_baseline  the CPU oracle (fp32 token recurrence) on host cores
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_F16 = 2.5e15      # dense fp16/bf16 matrix-core FLOP/s (MI355X)
+PEAK_HBM = 8.0e12           # HBM3E bytes/s (MI355X)
+PAGES_MS_T4000 = 1.35       # pages' hand-written CUDA kernel, 2x RTX 2080 Ti (context only)
+
+H_V, H_QK, D, C = 32, 16, 128, 64
+
+
+def algorithmic_work():
+    """Per-token algorithmic flops and bytes of each prefill stage (config dims).
+
+    Flops count each causal (triangular) product at half and the K K^T / Q K^T
+    Grams once per q/k head.  Bytes count each tensor a stage must read or
+    write once (fp16 intermediates, bf16 inputs, fp32 g/beta/output)."""
+    prep_f = H_V * (C * (D + D) + C * C / 3) + H_QK * (C * D)
+    state_f = H_V * (4 * D * D)
+    out_f = H_V * (2 * D * D + C * D) + H_QK * (C * D)
+    qk_b = H_QK * D * 2          # one of q or k, bf16
+    v_b = H_V * D * 2
+    gb_b = H_V * 4               # one of g or beta
+    f16_row = H_V * D * 2        # one of W, U, U' per token
+    hc_b = H_V * D * D * 2 / C   # fp16 chunk state, per token
+    out_b = H_V * D * 4
+    prep_b = qk_b + v_b + 2 * gb_b + 2 * f16_row + gb_b
+    state_b = 2 * f16_row + qk_b + gb_b + f16_row + hc_b
+    out_b_tot = 2 * qk_b + gb_b + hc_b + f16_row + out_b
+    return {
+        "prep": (prep_f, prep_b),
+        "state": (state_f, state_b),
+        "out": (out_f, out_b_tot),
+        "layer": (prep_f + state_f + out_f, 2 * qk_b + v_b + 2 * gb_b + out_b),
+    }
+
+
+def time_launches(fn, n, torch):
+    """Mean time per launch of fn() over n back-to-back launches (events on the current stream)."""
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(n):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / n
+
+
+def cpu_baseline(x, budget_s: float):
+    import oracle
+    cores = min(16, os.cpu_count() or 1)
+    reps, t = 0, 0.0
+    t0 = time.perf_counter()
+    while True:
+        oracle.forward_inputs(x, precision="f32", n_threads=cores)
+        reps += 1
+        t = time.perf_counter() - t0
+        if t >= budget_s or reps >= 100000:
+            break
+    return {"value": x.total_tokens * reps / t, "unit": "tokens/s per layer", "cores": cores,
+            "kind": "oracle",
+            "sample": f"fp32 token recurrence, {x.name}, all {x.h_v} value heads, {reps} run(s), "
+                      f"{t:.1f} s wall, threads over (sequence, value head)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-time budget of the CPU-oracle baseline (0 skips it)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer's path runs on a single MI355X "
+              "(heads or sequences would shard across GPUs with no exchange); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gdn_inputs as gi
+    import hybrid_linear_attention_gdn_amd as gdn
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf = torch.bfloat16
+
+    # ---------------- prefill workload (resident in HBM)
+    x = gi.prefill_4000()
+    T = x.total_tokens
+    q = torch.from_numpy(x.q).to(dev, bf)
+    k = torch.from_numpy(x.k).to(dev, bf)
+    v = torch.from_numpy(x.v).to(dev, bf)
+    g = torch.from_numpy(x.g).to(dev)
+    beta = torch.from_numpy(x.beta).to(dev)
+    cu = torch.from_numpy(x.cu_seqlens).to(dev)
+    out = torch.empty((T, H_V, D), device=dev)
+    fin = torch.empty((1, H_V, D, D), device=dev)
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(1, T, H_QK, H_V), dtype=torch.uint8, device=dev)
+
+    def step():
+        gdn.gdn_chunk_fwd(q, k, v, g, beta, cu, None, out, fin, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_step = time_launches(step, args.steps, torch)
+
+    stage_t = {}
+    for name, mask in (("prep", 1), ("state", 2), ("out", 4)):
+        stage_t[name] = time_launches(
+            lambda m=mask: gdn.gdn_chunk_fwd_stages(q, k, v, g, beta, cu, None, out, fin, ws, m),
+            args.steps, torch)
+    step()
+    torch.cuda.synchronize()
+
+    work = algorithmic_work()
+    state_bytes = H_V * D * D * 4          # one fp32 state per sequence (final state written)
+    per_seq = {"prep": 0, "state": state_bytes, "out": 0, "layer": state_bytes}
+    dom = max(stage_t, key=stage_t.get)
+    f_tok, b_tok = work[dom]
+    flops, nbytes = f_tok * T, b_tok * T + per_seq[dom]
+    t_dom = stage_t[dom]
+    if flops / PEAK_MFMA_F16 >= nbytes / PEAK_HBM:
+        roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": PEAK_MFMA_F16 / 1e12,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": nbytes / t_dom / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = f"gdn_chunk_{dom}"
+    roof["mean_launch_us"] = t_dom * 1e6
+    roof["algorithmic_flops_per_launch"] = flops
+    roof["algorithmic_bytes_per_launch"] = nbytes
+
+    f_layer, b_layer = work["layer"]
+    prefill = {
+        "ms_per_layer": t_step * 1e3,
+        "pct_mfma_peak": 100 * f_layer * T / t_step / PEAK_MFMA_F16,
+        "pct_hbm_peak": 100 * (b_layer * T + per_seq["layer"]) / t_step / PEAK_HBM,
+        "algorithmic_flops": f_layer * T,
+        "algorithmic_bytes": b_layer * T + per_seq["layer"],
+        "stage_us": {n: t * 1e6 for n, t in stage_t.items()},
+        "stage_pct_of_roofline": {
+            n: 100 * max(work[n][0] * T / PEAK_MFMA_F16, (work[n][1] * T + per_seq[n]) / PEAK_HBM) / stage_t[n]
+            for n in stage_t},
+    }
+
+    # ---------------- verify workload: 8 requests x (1 + 5) tokens, snapshots kept
+    y = gi.verify_8x6()
+    R, n_tok = 8, 6
+    vq = torch.from_numpy(y.q).to(dev, bf)
+    vk = torch.from_numpy(y.k).to(dev, bf)
+    vv = torch.from_numpy(y.v).to(dev, bf)
+    vg = torch.from_numpy(y.g).to(dev)
+    vb = torch.from_numpy(y.beta).to(dev)
+    s_in = torch.from_numpy(y.initial_state).to(dev)
+    vout = torch.empty((R * n_tok, H_V, D), device=dev)
+    inter = torch.empty((R, n_tok, H_V, D, D), device=dev)
+
+    def vstep():
+        gdn.gdn_recurrent_step(vq, vk, vv, vg, vb, R, n_tok, s_in, None, vout, inter, True)
+
+    for _ in range(args.warmup):
+        vstep()
+    t_verify = time_launches(vstep, args.steps, torch)
+    state_b = H_V * D * D * 4
+    v_bytes = R * state_b + R * n_tok * state_b + R * n_tok * (2 * H_QK * D * 2 + H_V * D * 2 + 2 * H_V * 4 + H_V * D * 4)
+    verify = {
+        "workload": y.name,
+        "us_per_step": t_verify * 1e6,
+        "tokens_per_s": R * n_tok / t_verify,
+        "algorithmic_bytes": v_bytes,
+        "achieved_GBps": v_bytes / t_verify / 1e9,
+        "pct_hbm_peak": 100 * v_bytes / t_verify / PEAK_HBM,
+    }
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(x, args.cpu_seconds)
+
+    value = T / t_step
+    line = {
+        "metric": "GDN prefill tokens/s per layer (T=4000) & %MFMA peak; verify %HBM BW",
+        "value": value,
+        "unit": "tokens/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": value / (4000 / (PAGES_MS_T4000 * 1e-3)),
+        "vs_baseline_note": "pages' 1.35 ms per 4000-token layer on 2x RTX 2080 Ti (TP=2); context, not a target",
+        "dtype": "f16",
+        "dtype_note": "bf16 inputs widened to fp16 matrix-core operands, fp32 accumulation, state and output",
+        "data": "synthetic",
+        "config": {"workload": x.name, "global_batch": 1, "seq_len": T, "n_heads_v": H_V,
+                   "n_heads_qk": H_QK, "d_k": D, "d_v": D, "chunk": C, "initial_state": "zeros (NULL)",
+                   "parallelism": "single GPU"},
+        "prefill": prefill,
+        "roofline": roof,
+        "verify": verify,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
