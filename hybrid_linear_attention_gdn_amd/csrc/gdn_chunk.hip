@@ -49,8 +49,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     __shared__ __attribute__((aligned(16))) f16 KsT[kDim * kTS];   // K^T [dim][pos]
     __shared__ __attribute__((aligned(16))) f16 VsT[kDim * kTS];   // V^T [dim][pos]
     __shared__ __attribute__((aligned(16))) float Ab[kChunk * kTS]; // A fp32, then TW | TU fp16
+    __shared__ __attribute__((aligned(16))) float Tb[kChunk * kTS]; // Tm = (I + A)^{-1} fp32
     __shared__ float Gs[kChunk];
     __shared__ float Bs[kChunk];
+    __shared__ float Bw[kChunk];                                     // beta e^G
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -83,8 +85,25 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     }
     __syncthreads();
 
-    // ---- decay cumsum within the chunk (wave 0, one lane per position)
+    // ---- K^T as A-operand fragments of the state update K^T X, written once
+    //      per (slot, q/k head) by the first value head of the group:
+    //      fragment (i, qq), lane (gq, ln) = K^T[16 i + ln][p(gq, s)] for K-step qq
     const size_t wsidx = (size_t)slot * h_v + h;
+    if (h % (h_v / h_qk) == 0) {
+        f16* kdst = ws.kt + ((size_t)slot * h_qk + j) * kKtElems;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int f = wave + 4 * it;          // fragment index i * 2 + qq
+            const int i = f >> 1, qq = f & 1;
+            const f16* krow = KsT + (16 * i + ln) * kTS + 32 * qq + 4 * gq;
+            const f16x4 lo = *reinterpret_cast<const f16x4*>(krow);
+            const f16x4 hi = *reinterpret_cast<const f16x4*>(krow + 16);
+            const f16x8 fr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            *reinterpret_cast<f16x8*>(kdst + ((size_t)f * 64 + lane) * 8) = fr;
+        }
+    }
+
+    // ---- decay cumsum within the chunk (wave 0, one lane per position)
     if (wave == 0) {
         float x = Gs[lane];
 #pragma unroll
@@ -92,8 +111,14 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
             const float y = __shfl_up(x, off, 64);
             if (lane >= off) x += y;
         }
+        const float gc = __shfl(x, kChunk - 1, 64);
+        const float eg = exp_f(x);
         Gs[lane] = x;
-        ws.gcum[wsidx * kGElems + lane] = x;
+        Bw[lane] = Bs[lane] * eg;
+        float* gdst = ws.gcum + wsidx * kGElems;
+        gdst[lane] = exp_f(gc - x);
+        gdst[64 + lane] = eg;
+        gdst[128 + lane] = x;
     }
     __syncthreads();
 
@@ -130,29 +155,72 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     }
     __syncthreads();
 
-    // ---- Tm = (I + A)^{-1} by forward substitution, one column per lane (wave 0).
-    //      x_r = delta_rs - sum_{t<r} A_rt x_t; x_t = 0 for t < s by induction.
-    f16* TWs = reinterpret_cast<f16*>(Ab);          // [pos][t], Tm diag(beta e^G)
-    f16* TUs = TWs + kChunk * kTS;                  // [pos][t], Tm diag(beta)
-    if (wave == 0) {
-        const int s = lane;
-        float x[kChunk];
+    // ---- Tm = (I + A)^{-1}, blocked by 16 (A strictly lower triangular).
+    //  (1) Diagonal blocks Tm_ii = (I + A_ii)^{-1}: wave i, lane c % 16 holds
+    //      column c; x_r = delta_rc - sum_{t<r} A_rt x_t (x_t = 0 for t < c).
+    //  (2) Below the diagonal, block column j on wave j, rows i = j+1..3:
+    //      Tm_ij = -Tm_ii sum_{k=j}^{i-1} A_ik Tm_kj, with 16x16x16 products on
+    //      the matrix cores (split fp16 operands, ~fp32 accuracy).  A product's
+    //      accumulator is already the B operand of the next one, so the column
+    //      chain never leaves registers.
+    {
+        const int ib = wave;
+        float x[16];
 #pragma unroll
-        for (int r = 0; r < kChunk; ++r) {
-            float acc = (r == s) ? 1.f : 0.f;
-            const float* arow = Ab + r * kTS;
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == ln) ? 1.f : 0.f;
+            const float* arow = Ab + (16 * ib + r) * kTS + 16 * ib;
 #pragma unroll
             for (int t = 0; t < r; ++t) acc -= arow[t] * x[t];
             x[r] = acc;
         }
-        // all reads of A by this wave are complete before its writes below
-        const float bw = Bs[s] * exp_f(Gs[s]);
-        const float bu = Bs[s];
+        if (gq == 0) {
 #pragma unroll
-        for (int r = 0; r < kChunk; ++r) {
-            TWs[r * kTS + s] = static_cast<f16>(x[r] * bw);
-            TUs[r * kTS + s] = static_cast<f16>(x[r] * bu);
+            for (int r = 0; r < 16; ++r) Tb[(16 * ib + r) * kTS + 16 * ib + ln] = x[r];
         }
+    }
+    __syncthreads();
+    if (wave < 3) {
+        const int jb = wave;
+        f32x4 tcol[4];     // Tm_{k, jb} in accumulator (= B operand) layout, k >= jb
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) tcol[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            if (kb == jb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tcol[kb][e] = Tb[(16 * kb + 4 * gq + e) * kTS + 16 * kb + ln];
+            }
+#pragma unroll
+        for (int i2 = 1; i2 < 4; ++i2) {
+            if (i2 <= jb) continue;
+            f32x4 xs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < i2; ++kb) {
+                if (kb < jb) continue;
+                const f32x4 aik = *reinterpret_cast<const f32x4*>(Ab + (16 * i2 + ln) * kTS + 16 * kb + 4 * gq);
+                xs = mfma_split16(aik, tcol[kb], xs);
+            }
+            const f32x4 tii = *reinterpret_cast<const f32x4*>(Tb + (16 * i2 + ln) * kTS + 16 * i2 + 4 * gq);
+            const f32x4 y = mfma_split16(tii, xs, f32x4{0.f, 0.f, 0.f, 0.f});
+            tcol[i2] = -y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Tb[(16 * i2 + 4 * gq + e) * kTS + 16 * jb + ln] = -y[e];
+        }
+    }
+    __syncthreads();
+
+    // ---- TW = Tm diag(beta e^G), TU = Tm diag(beta) in fp16 over the dead A
+    //      buffer; blocks above the diagonal are zero.
+    f16* TWs = reinterpret_cast<f16*>(Ab);          // [pos][t]
+    f16* TUs = TWs + kChunk * kTS;                  // [pos][t]
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int idx = tid + 256 * it;
+        const int r = idx >> 6, t = idx & 63;
+        const float tm = ((t >> 4) > (r >> 4)) ? 0.f : Tb[r * kTS + t];
+        TWs[r * kTS + t] = static_cast<f16>(tm * Bw[t]);
+        TUs[r * kTS + t] = static_cast<f16>(tm * Bs[t]);
     }
     __syncthreads();
 
@@ -214,14 +282,140 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 // ---------------------------------------------------------------------------
 // Stage 2: inter-chunk state recurrence.  One workgroup per (sequence, value
 // head, 64-column block); wave w owns 16 state columns for the whole sequence
-// and keeps them in accumulators (8 tiles of 16 d_k rows).  The next chunk's
-// -W fragments, K and decay cumsum are fetched into registers while the
-// current chunk is computed, then committed to the other LDS buffer.
+// and keeps them in accumulator registers (8 tiles of 16 d_k rows).
+//
+// Per chunk the workgroup reads 42 KB: -W fragments (16 KB), K^T fragments
+// (16 KB), the U fragments of its 4 column tiles (8 KB) and the decay
+// vectors.  They arrive by direct global-to-LDS copies (no registers) into a
+// ring of three LDS stages, two chunks ahead of the chunk being computed.
+// Every wave issues the same fixed number of copies per chunk, so one
+// explicit memory-counter wait plus a barrier makes a stage complete.
+//
+// Each chunk's results for the output stage (its incoming state and U') are
+// stored at the top of the next chunk from one of two register sets that
+// alternate, so a store always has a whole chunk to retire before its data
+// registers are rewritten; vector-memory counters retire in order and a
+// store's data registers cannot be reused before it has.
 // ---------------------------------------------------------------------------
+constexpr int kStages = 3;
+constexpr int kStageU = 4 * 4 * 64 * 4;          // halves: U fragments of 4 column tiles
+constexpr int kCopiesPerChunk = 4 + 4 + 2 + 2;    // per wave: -W, K^T, U, decay vectors
+
+struct StateStage {
+    f16 w[kWElems];
+    f16 k[kKtElems];
+    f16 u[kStageU];
+    float g[4][2 * kChunk];   // per-wave copy of e^{G_C - G_r} and e^{G_r}
+};
+
+// s_waitcnt with vmcnt = N and the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One chunk's copies for this wave: 1 KB pieces (16 B per lane) of -W, K^T
+// and U, and the two 256 B decay vectors (4 B per lane) into the wave's copy.
+__device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace& ws, size_t wsidx,
+                                           size_t ktidx, int cb, int wave, int lane) {
+    const f16* wsrc = ws.w + wsidx * kWElems;
+    const f16* ksrc = ws.kt + ktidx * kKtElems;
+    const f16* usrc = ws.u + wsidx * kUElems + (size_t)cb * kStageU;
+    const float* gsrc = ws.gcum + wsidx * kGElems;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int piece = wave * 4 + i;
+        __builtin_amdgcn_global_load_lds(wsrc + (piece * 64 + lane) * 8, st.w + piece * 512, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ksrc + (piece * 64 + lane) * 8, st.k + piece * 512, 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int piece = wave * 2 + i;
+        __builtin_amdgcn_global_load_lds(usrc + (piece * 64 + lane) * 8, st.u + piece * 512, 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(gsrc + i * 64 + lane, &st.g[wave][i * 64], 4, 0, 0);
+}
+
+// Results of one chunk that the output stage needs.
+struct StateOut {
+    f16x8 hb[4];   // incoming chunk state, B fragments over d_k
+    f16x8 up[2];   // U', B fragments over positions
+};
+
+__device__ __forceinline__ void state_store(const StateOut& o, const ChunkWorkspace& ws, size_t wsidx,
+                                            int ct, int lane) {
+    f16* hdst = ws.hc + wsidx * kHcElems;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+        *reinterpret_cast<f16x8*>(hdst + ((ct * 4 + qq) * 64 + lane) * 8) = o.hb[qq];
+    f16* udst = ws.up + wsidx * kUpElems;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+        *reinterpret_cast<f16x8*>(udst + ((ct * 2 + qq) * 64 + lane) * 8) = o.up[qq];
+}
+
+// One chunk of the recurrence for this wave's 16 columns.
+__device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st, StateOut& o,
+                                            int wave, int lane, int gq) {
+    // U accumulator fragments of this wave's column tile
+    f32x4 acc[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const f16x4 uf = *reinterpret_cast<const f16x4*>(&st.u[((wave * 4 + p) * 64 + lane) * 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[p][e] = static_cast<float>(uf[e]);
+    }
+    // incoming chunk state as B fragments (d_k slots), kept for the output stage
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) o.hb[qq] = cat_to_f16(H[2 * qq], H[2 * qq + 1]);
+    // U' = U + (-W) H
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const f16x8 wa = *reinterpret_cast<const f16x8*>(&st.w[((p * 4 + qq) * 64 + lane) * 8]);
+            acc[p] = mfma_f16(wa, o.hb[qq], acc[p]);
+        }
+    // U' as B fragments (position slots), kept for the output stage
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) o.up[qq] = cat_to_f16(acc[2 * qq], acc[2 * qq + 1]);
+    // X = diag(e^{G_C - G}) U';   H <- e^{G_C} H + K^T X
+    const float* dec = st.g[wave];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc[p][e] *= dec[16 * p + 4 * gq + e];
+    f16x8 xb[2];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) xb[qq] = cat_to_f16(acc[2 * qq], acc[2 * qq + 1]);
+    const float gam = dec[kChunk + kChunk - 1];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) H[i] *= gam;
+    // eight independent accumulator chains, interleaved
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f16x8 ka = *reinterpret_cast<const f16x8*>(&st.k[((i * 2 + qq) * 64 + lane) * 8]);
+            H[i] = mfma_f16(ka, xb[qq], H[i]);
+        }
+}
+
 __global__ __launch_bounds__(256) void gdn_chunk_state(
-    const uint16_t* __restrict__ k, const int32_t* __restrict__ cu, int n_seqs,
-    int h_qk, int h_v, const float* __restrict__ s0, float* __restrict__ s_final,
-    ChunkWorkspace ws)
+    const int32_t* __restrict__ cu, int n_seqs, int h_qk, int h_v,
+    const float* __restrict__ s0, float* __restrict__ s_final, ChunkWorkspace ws)
 {
     const int nh = blockIdx.x;
     const int seq = nh / h_v;
@@ -237,134 +431,60 @@ __global__ __launch_bounds__(256) void gdn_chunk_state(
     const int ct = cb * 4 + wave;        // column tile 0..7
     const int col = 16 * ct + ln;
 
-    __shared__ __attribute__((aligned(16))) f16 Wf[2][kWElems];      // -W fragments
-    __shared__ __attribute__((aligned(16))) f16 KsT[2][kDim * kTS];  // K^T [dim][pos]
-    __shared__ float Gs[2][kChunk];
+    __shared__ __attribute__((aligned(16))) StateStage stage[kStages];
 
     const int start = cu[seq];
     const int end = cu[seq + 1];
     const int nchunks = (end - start + kChunk - 1) / kChunk;
     const int slot0 = slot_base(cu, seq);
+    const int last = nchunks - 1;
+    auto widx = [&](int c) { return (size_t)(slot0 + min(c, last)) * h_v + h; };
+    auto kidx = [&](int c) { return (size_t)(slot0 + min(c, last)) * h_qk + j; };
 
     // ---- incoming state
     f32x4 H[8];
     const size_t sbase = ((size_t)seq * h_v + h) * kDim * kDim;
+    if (s0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            H[i][e] = s0 ? s0[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col] : 0.f;
-
-    // ---- chunk loads: 1024 16-byte pieces of -W, 1024 of K (64 rows x 16), 64 G
-    uint4 wreg[4];
-    u16x8 kreg[4];
-    float greg = 0.f;
-    auto fetch = [&](int c) {
-        const size_t wsidx = (size_t)(slot0 + c) * h_v + h;
-        const uint4* wsrc = reinterpret_cast<const uint4*>(ws.w + wsidx * kWElems);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wreg[i] = wsrc[tid + 256 * i];
-        const int t0 = start + c * kChunk;
-        const int len = min(kChunk, end - t0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i;
-            const int r = idx >> 4;
-            const int c8 = (idx & 15) * 8;
-            kreg[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (r < len)
-                kreg[i] = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + r) * h_qk + j) * kDim + c8);
-        }
-        if (tid < kChunk) greg = ws.gcum[wsidx * kGElems + tid];
-    };
-    auto commit = [&](int buf) {
-        uint4* wdst = reinterpret_cast<uint4*>(Wf[buf]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wdst[tid + 256 * i] = wreg[i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i;
-            const int r = idx >> 4;
-            const int c8 = (idx & 15) * 8;
-            const f16x8 kf = bf16x8_to_f16x8(kreg[i]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) KsT[buf][(c8 + e) * kTS + r] = kf[e];
-        }
-        if (tid < kChunk) Gs[buf][tid] = greg;
-    };
-
-    if (nchunks > 0) {
-        fetch(0);
-        commit(0);
-    }
-    __syncthreads();
-
-    for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        const size_t wsidx = (size_t)(slot0 + c) * h_v + h;
-        if (c + 1 < nchunks) fetch(c + 1);
-
-        // U accumulator fragments of this wave's column tile
-        f32x4 acc[4];
-        const f16* usrc = ws.u + wsidx * kUElems;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const f16x4 uf = *reinterpret_cast<const f16x4*>(usrc + ((ct * 4 + p) * 64 + lane) * 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[p][e] = static_cast<float>(uf[e]);
-        }
-
-        // chunk state as B fragments (d_k slots); stored for the output stage
-        f16x8 hb[4];
-        f16* hdst = ws.hc + wsidx * kHcElems;
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            hb[qq] = cat_to_f16(H[2 * qq], H[2 * qq + 1]);
-            *reinterpret_cast<f16x8*>(hdst + ((ct * 4 + qq) * 64 + lane) * 8) = hb[qq];
-        }
-
-        // U' = U + (-W) H
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const f16x8 wa = *reinterpret_cast<const f16x8*>(&Wf[buf][((p * 4 + qq) * 64 + lane) * 8]);
-                acc[p] = mfma_f16(wa, hb[qq], acc[p]);
-            }
-
-        // U' as B fragments (position slots); stored for the output stage
-        f16* udst = ws.up + wsidx * kUpElems;
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq)
-            *reinterpret_cast<f16x8*>(udst + ((ct * 2 + qq) * 64 + lane) * 8) =
-                cat_to_f16(acc[2 * qq], acc[2 * qq + 1]);
-
-        // X = diag(e^{G_C - G}) U';   H <- e^{G_C} H + K^T X
-        const float gc = Gs[buf][kChunk - 1];
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                acc[p][e] *= exp_f(gc - Gs[buf][16 * p + 4 * gq + e]);
-        f16x8 xb[2];
+                H[i][e] = s0[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col];
+    } else {
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) xb[qq] = cat_to_f16(acc[2 * qq], acc[2 * qq + 1]);
-        const float gam = exp_f(gc);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            H[i] *= gam;
-            const f16* krow = &KsT[buf][(16 * i + ln) * kTS];
-#pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-                const f16x4 lo = *reinterpret_cast<const f16x4*>(krow + 32 * qq + 4 * gq);
-                const f16x4 hi = *reinterpret_cast<const f16x4*>(krow + 32 * qq + 16 + 4 * gq);
-                const f16x8 ka = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                H[i] = mfma_f16(ka, xb[qq], H[i]);
-            }
-        }
+        for (int i = 0; i < 8; ++i) H[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // settle the initial-state loads before the copies start counting
+    __builtin_amdgcn_s_waitcnt(0);
 
-        if (c + 1 < nchunks) commit(buf ^ 1);
-        __syncthreads();
+    if (nchunks > 0) {
+        // copies are issued for chunks past the last one too (clamped to the
+        // last chunk, never used) so the count in flight is always the same
+        state_copy(stage[0], ws, widx(0), kidx(0), cb, wave, lane);
+        state_copy(stage[1], ws, widx(1), kidx(1), cb, wave, lane);
+        StateOut pa, pb;
+        int c = 0;
+        for (;;) {
+            // chunk c (even) -> pa
+            wait_vmcnt<kCopiesPerChunk>();      // this wave's copies of chunk c have landed
+            wg_barrier();                       // ... and every other wave's
+            if (c > 0) state_store(pb, ws, widx(c - 1), ct, lane);
+            state_copy(stage[(c + 2) % kStages], ws, widx(c + 2), kidx(c + 2), cb, wave, lane);
+            state_chunk(H, stage[c % kStages], pa, wave, lane, gq);
+            if (++c >= nchunks) break;
+            // chunk c (odd) -> pb
+            wait_vmcnt<kCopiesPerChunk>();
+            wg_barrier();
+            state_store(pa, ws, widx(c - 1), ct, lane);
+            state_copy(stage[(c + 2) % kStages], ws, widx(c + 2), kidx(c + 2), cb, wave, lane);
+            state_chunk(H, stage[c % kStages], pb, wave, lane, gq);
+            if (++c >= nchunks) break;
+        }
+        if (nchunks & 1) state_store(pa, ws, widx(last), ct, lane);
+        else state_store(pb, ws, widx(last), ct, lane);
+        // drain the copies of the two chunks past the end before the workgroup
+        // exits (the LDS they target must stay allocated until they land)
+        __builtin_amdgcn_s_waitcnt(0);
     }
 
     if (s_final) {
@@ -394,7 +514,8 @@ __global__ __launch_bounds__(256) void gdn_chunk_out(
     __shared__ __attribute__((aligned(16))) f16 Qs[kChunk * kQS];   // Q [pos][dim]
     __shared__ __attribute__((aligned(16))) f16 Ks[kChunk * kQS];   // K [pos][dim]
     __shared__ __attribute__((aligned(16))) f16 Ps[kChunk * kTS];   // P [pos][pos]
-    __shared__ float Gs[kChunk];
+    __shared__ float Gs[kChunk];   // G_r
+    __shared__ float Es[kChunk];   // e^{G_r}
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -415,7 +536,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_out(
         *reinterpret_cast<f16x8*>(Qs + r * kQS + c8) = bf16x8_to_f16x8(qb);
         *reinterpret_cast<f16x8*>(Ks + r * kQS + c8) = bf16x8_to_f16x8(kb);
     }
-    if (tid < kChunk) Gs[tid] = ws.gcum[wsidx * kGElems + tid];
+    if (tid < kChunk) {
+        Gs[tid] = ws.gcum[wsidx * kGElems + 128 + tid];
+        Es[tid] = ws.gcum[wsidx * kGElems + 64 + tid];
+    }
     __syncthreads();
 
     // ---- P = M o (Q K^T); wave w owns row tile w, zero above the diagonal
@@ -472,7 +596,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_out(
     for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float f = exp_f(Gs[16 * p + 4 * gq + e]);
+            const float f = Es[16 * p + 4 * gq + e];
             o[p][0][e] *= f;
             o[p][1][e] *= f;
         }
@@ -524,7 +648,7 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
     }
     if ((stage_mask & 2) && n_seqs > 0) {
         hipLaunchKernelGGL(gdn_chunk_state, dim3(n_seqs * h_v, kDim / 64), dim3(256), 0, stream,
-                           k, cu, n_seqs, h_qk, h_v, s0, s_final, ws);
+                           cu, n_seqs, h_qk, h_v, s0, s_final, ws);
     }
     if ((stage_mask & 4) && total_tokens > 0) {
         hipLaunchKernelGGL(gdn_chunk_out, dim3(n_slots, h_v), dim3(256), 0, stream,

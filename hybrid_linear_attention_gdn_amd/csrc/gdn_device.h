@@ -32,19 +32,24 @@ typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Per (chunk slot, value head) element counts of the workspace regions.
 constexpr size_t kWElems = 16 * 64 * 8;    // -W, A-operand fragments [p][qq][lane][8]
 constexpr size_t kUElems = 8 * 4 * 64 * 4;  // U, accumulator fragments [ct][p][lane][4]
 constexpr size_t kUpElems = 8 * 2 * 64 * 8; // U', B-operand fragments [ct][qq][lane][8]
 constexpr size_t kHcElems = 8 * 4 * 64 * 8; // chunk state, B-operand fragments [ct][qq][lane][8]
-constexpr size_t kGElems = 64;              // decay cumsum
+// Decay vectors: [0, 64) e^{G_C - G_r} (state update), [64, 128) e^{G_r}, [128, 192) G_r
+constexpr size_t kGElems = 192;
+// Per (chunk slot, q/k head): K^T as A-operand fragments of K^T X [d_k tile][pos step][lane][8]
+constexpr size_t kKtElems = 8 * 2 * 64 * 8;
 
 struct ChunkWorkspace {
     f16* w;
     f16* u;
     f16* up;
     f16* hc;
+    f16* kt;
     float* gcum;
 };
 
@@ -61,6 +66,24 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16x8(u16x8 b) {
 
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x16 product of fp32 operands in fragment form (A: lane l holds row l%16,
+// k = 4 (l/16) + e; B: k = 4 (l/16) + e, column l%16) on fp16 matrix cores,
+// each operand split as hi + lo: hi*hi + hi*lo + lo*hi, error ~2^-22 relative.
+__device__ __forceinline__ f32x4 mfma_split16(f32x4 a, f32x4 b, f32x4 c) {
+    f16x4 ah, al, bh, bl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        ah[e] = static_cast<f16>(a[e]);
+        al[e] = static_cast<f16>(a[e] - static_cast<float>(ah[e]));
+        bh[e] = static_cast<f16>(b[e]);
+        bl[e] = static_cast<f16>(b[e] - static_cast<float>(bh[e]));
+    }
+    c = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bl, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16f16(al, bh, c, 0, 0, 0);
+    return c;
 }
 
 // exp(x) through the hardware base-2 exponential; used for decay factors
