@@ -69,14 +69,13 @@ struct Layout {
 
 Layout workspace_layout(const gdn_dims* d) {
     const size_t units = (size_t)n_chunk_slots(d) * (size_t)d->n_heads_v;
-    const size_t qk_units = (size_t)n_chunk_slots(d) * (size_t)d->n_heads_qk;
     Layout L;
     size_t off = 0;
     L.w = off;  off += round_up(units * gdn::kWElems * sizeof(gdn::f16));
     L.u = off;  off += round_up(units * gdn::kUElems * sizeof(gdn::f16));
     L.up = off; off += round_up(units * gdn::kUpElems * sizeof(gdn::f16));
     L.hc = off; off += round_up(units * gdn::kHcElems * sizeof(gdn::f16));
-    L.kt = off; off += round_up(qk_units * gdn::kKtElems * sizeof(gdn::f16));
+    L.kt = off; off += round_up(units * gdn::kKtElems * sizeof(gdn::f16));
     L.g = off;  off += round_up(units * gdn::kGElems * sizeof(float));
     L.total = off;
     return L;
@@ -175,6 +174,7 @@ gdn_status gdn_chunk_fwd_stages(const void* q, const void* k, const void* v,
     ws.hc = reinterpret_cast<gdn::f16*>(base + L.hc);
     ws.kt = reinterpret_cast<gdn::f16*>(base + L.kt);
     ws.gcum = reinterpret_cast<float*>(base + L.g);
+    ws.n_slots = (int)slots;
 
     const hipError_t e = gdn::launch_chunk_fwd(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),

@@ -32,6 +32,14 @@ namespace {
 constexpr int kTS = 72;   // LDS row stride (halves or floats) of 64-wide tiles
 constexpr int kQS = 136;  // LDS row stride (halves) of 128-wide tiles
 
+// Transposed [dim][pos] fp16 tiles (row stride kTS) are written one position
+// per lane, four dims 8 apart at a time.  Flipping position bits 4-5 by the
+// dim's 8-block spreads those four rows over different banks, and keeps every
+// 8-aligned run of positions contiguous for 16-byte fragment reads.
+__device__ __forceinline__ int tsw(int d, int t) {
+    return d * kTS + (t ^ (((d >> 3) & 3) << 4));
+}
+
 // ---------------------------------------------------------------------------
 // Stage 1: intra-chunk preparation.  One workgroup per (chunk slot, value head).
 // ---------------------------------------------------------------------------
@@ -53,6 +61,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     __shared__ float Gs[kChunk];
     __shared__ float Bs[kChunk];
     __shared__ float Bw[kChunk];                                     // beta e^G
+    __shared__ float Ds[kChunk];                                     // e^{G_C - G}
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -60,22 +69,39 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     const int gq = lane >> 4;
     const int ln = lane & 15;
 
-    // ---- load K, V (bf16 -> fp16), transposed into LDS; pad rows are zero
-    for (int i = tid; i < kChunk * 16; i += 256) {
-        const int r = i >> 4;
-        const int c8 = (i & 15) * 8;
-        u16x8 kb = {0, 0, 0, 0, 0, 0, 0, 0};
-        u16x8 vb = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (r < len) {
-            kb = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + r) * h_qk + j) * kDim + c8);
-            vb = *reinterpret_cast<const u16x8*>(v + ((size_t)(t0 + r) * h_v + h) * kDim + c8);
-        }
-        const f16x8 kf = bf16x8_to_f16x8(kb);
-        const f16x8 vf = bf16x8_to_f16x8(vb);
+    // ---- K as fragments (row 16 jt + ln, dims 32 kk + 8 gq .. +7) for all four
+    //      row tiles (the Gram needs them), V for this wave's row tile; pad
+    //      rows are zero.  Each wave writes its own row tile transposed into
+    //      KsT / VsT (swizzled, see tsw).
+    f16x8 kf[4][4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            KsT[(c8 + e) * kTS + r] = kf[e];
-            VsT[(c8 + e) * kTS + r] = vf[e];
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int r = 16 * jt + ln;
+            u16x8 b = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (r < len)
+                b = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + r) * h_qk + j) * kDim + 32 * kk + 8 * gq);
+            kf[jt][kk] = bf16x8_to_f16x8(b);
+        }
+    {
+        const int r = 16 * wave + ln;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            u16x8 kb = {0, 0, 0, 0, 0, 0, 0, 0};
+            u16x8 vb = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (r < len) {
+                kb = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + r) * h_qk + j) * kDim + 32 * kk + 8 * gq);
+                vb = *reinterpret_cast<const u16x8*>(v + ((size_t)(t0 + r) * h_v + h) * kDim + 32 * kk + 8 * gq);
+            }
+            const f16x8 kt8 = bf16x8_to_f16x8(kb);
+            const f16x8 vt8 = bf16x8_to_f16x8(vb);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int d = 32 * kk + 8 * gq + e;
+                KsT[tsw(d, r)] = kt8[e];
+                VsT[tsw(d, r)] = vt8[e];
+            }
         }
     }
     if (tid < kChunk) {
@@ -85,23 +111,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     }
     __syncthreads();
 
-    // ---- K^T as A-operand fragments of the state update K^T X, written once
-    //      per (slot, q/k head) by the first value head of the group:
-    //      fragment (i, qq), lane (gq, ln) = K^T[16 i + ln][p(gq, s)] for K-step qq
-    const size_t wsidx = (size_t)slot * h_v + h;
-    if (h % (h_v / h_qk) == 0) {
-        f16* kdst = ws.kt + ((size_t)slot * h_qk + j) * kKtElems;
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int f = wave + 4 * it;          // fragment index i * 2 + qq
-            const int i = f >> 1, qq = f & 1;
-            const f16* krow = KsT + (16 * i + ln) * kTS + 32 * qq + 4 * gq;
-            const f16x4 lo = *reinterpret_cast<const f16x4*>(krow);
-            const f16x4 hi = *reinterpret_cast<const f16x4*>(krow + 16);
-            const f16x8 fr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            *reinterpret_cast<f16x8*>(kdst + ((size_t)f * 64 + lane) * 8) = fr;
-        }
-    }
+    const size_t wsidx = ws.vunit(slot, h);
 
     // ---- decay cumsum within the chunk (wave 0, one lane per position)
     if (wave == 0) {
@@ -115,35 +125,50 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
         const float eg = exp_f(x);
         Gs[lane] = x;
         Bw[lane] = Bs[lane] * eg;
+        const float dc = exp_f(gc - x);
+        Ds[lane] = dc;
         float* gdst = ws.gcum + wsidx * kGElems;
-        gdst[lane] = exp_f(gc - x);
+        gdst[lane] = dc;
         gdst[64 + lane] = eg;
         gdst[128 + lane] = x;
     }
     __syncthreads();
 
+    // ---- K^T diag(e^{G_C - G}) as A-operand fragments of the state update:
+    //      fragment (i, qq), lane (gq, ln) = K[p][16 i + ln] e^{G_C - G_p} at the
+    //      position slots p(gq, s) of K-step qq.
+    {
+        f16* kdst = ws.kt + wsidx * kKtElems;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int f = wave + 4 * it;          // fragment index i * 2 + qq
+            const int i = f >> 1, qq = f & 1;
+            const int d = 16 * i + ln;
+            const f16x4 lo = *reinterpret_cast<const f16x4*>(KsT + tsw(d, 32 * qq + 4 * gq));
+            const f16x4 hi = *reinterpret_cast<const f16x4*>(KsT + tsw(d, 32 * qq + 16 + 4 * gq));
+            f16x8 fr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                fr[e] = static_cast<f16>(static_cast<float>(lo[e]) * Ds[32 * qq + 4 * gq + e]);
+                fr[e + 4] = static_cast<f16>(static_cast<float>(hi[e]) * Ds[32 * qq + 16 + 4 * gq + e]);
+            }
+            *reinterpret_cast<f16x8*>(kdst + ((size_t)f * 64 + lane) * 8) = fr;
+        }
+    }
+
     // ---- A = strictly lower (beta_r e^{G_r-G_s} K K^T); wave w owns row tile w.
-    //      Operands straight from global memory: K rows, 8 dims per lane.
     {
         const int p = wave;
-        f16x8 afr[4];
-        const int ra = 16 * p + ln;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            u16x8 b = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (ra < len)
-                b = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + ra) * h_qk + j) * kDim + 32 * kk + 8 * gq);
-            afr[kk] = bf16x8_to_f16x8(b);
-        }
-        for (int jt = 0; jt <= p; ++jt) {
+        for (int jt = 0; jt < 4; ++jt) {
+            if (jt > p) continue;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int rb = 16 * jt + ln;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                u16x8 b = {0, 0, 0, 0, 0, 0, 0, 0};
-                if (rb < len)
-                    b = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + rb) * h_qk + j) * kDim + 32 * kk + 8 * gq);
-                acc = mfma_f16(afr[kk], bf16x8_to_f16x8(b), acc);
+                f16x8 a = kf[0][kk];
+#pragma unroll
+                for (int q2 = 1; q2 < 4; ++q2) if (q2 == p) a = kf[q2][kk];
+                acc = mfma_f16(a, kf[jt][kk], acc);
             }
             const int s = 16 * jt + ln;
 #pragma unroll
@@ -241,8 +266,8 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
                 const int d = 16 * (2 * wave + a) + ln;
-                kfr[a] = *reinterpret_cast<const f16x8*>(KsT + d * kTS + 32 * kt + 8 * gq);
-                vfr[a] = *reinterpret_cast<const f16x8*>(VsT + d * kTS + 32 * kt + 8 * gq);
+                kfr[a] = *reinterpret_cast<const f16x8*>(KsT + tsw(d, 32 * kt + 8 * gq));
+                vfr[a] = *reinterpret_cast<const f16x8*>(VsT + tsw(d, 32 * kt + 8 * gq));
             }
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
@@ -280,16 +305,19 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2: inter-chunk state recurrence.  One workgroup per (sequence, value
-// head, 64-column block); wave w owns 16 state columns for the whole sequence
-// and keeps them in accumulator registers (8 tiles of 16 d_k rows).
-//
-// Per chunk the workgroup reads 42 KB: -W fragments (16 KB), K^T fragments
-// (16 KB), the U fragments of its 4 column tiles (8 KB) and the decay
-// vectors.  They arrive by direct global-to-LDS copies (no registers) into a
-// ring of three LDS stages, two chunks ahead of the chunk being computed.
-// Every wave issues the same fixed number of copies per chunk, so one
-// explicit memory-counter wait plus a barrier makes a stage complete.
+// Stage 2: inter-chunk state recurrence.  A workgroup of NW waves owns
+// 16 * TPW * NW state columns of one (sequence, value head); each wave owns
+// TPW column tiles of 16 and keeps their 128 x 16 slices of the state in
+// accumulator registers (8 tiles of 16 d_k rows each) for the whole
+// sequence.  A wave's tiles share every -W and K^T fragment it reads from
+// LDS, and their two dependency chains interleave.  Per chunk the workgroup
+// reads -W fragments (16 KB) and K^T fragments (16 KB), shared by its waves,
+// plus each wave's U fragments and decay vectors, by direct global-to-LDS
+// copies into a ring of three stages, two chunks ahead.  Every wave issues
+// the same fixed number of copies per chunk, so a memory-counter wait on its
+// own copies (plus a barrier when NW > 1) makes a stage ready.  The
+// workgroups of one head are placed on one XCD so that its L2 serves the
+// shared fragments.
 //
 // Each chunk's results for the output stage (its incoming state and U') are
 // stored at the top of the next chunk from one of two register sets that
@@ -298,15 +326,20 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 // store's data registers cannot be reused before it has.
 // ---------------------------------------------------------------------------
 constexpr int kStages = 3;
-constexpr int kStageU = 4 * 4 * 64 * 4;          // halves: U fragments of 4 column tiles
-constexpr int kCopiesPerChunk = 4 + 4 + 2 + 2;    // per wave: -W, K^T, U, decay vectors
+constexpr int kUTile = 4 * 64 * 4;     // halves of U fragments per column tile
 
+template <int NW, int TPW>
 struct StateStage {
     f16 w[kWElems];
     f16 k[kKtElems];
-    f16 u[kStageU];
-    float g[4][2 * kChunk];   // per-wave copy of e^{G_C - G_r} and e^{G_r}
+    f16 u[NW][TPW * kUTile];  // each wave's U accumulator fragments
+    float g[NW][2 * kChunk];  // each wave's copy of e^{G_C - G_r}, e^{G_r}
 };
+
+template <int NW, int TPW>
+constexpr int copies_per_chunk() { return 2 * (16 / NW) + 2 * TPW + 2; }
+template <int TPW>
+constexpr int stores_per_chunk() { return 6 * TPW; }
 
 // s_waitcnt with vmcnt = N and the other counters left alone (gfx9 encoding).
 template <int N>
@@ -323,136 +356,159 @@ __device__ __forceinline__ void wg_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// One chunk's copies for this wave: 1 KB pieces (16 B per lane) of -W, K^T
-// and U, and the two 256 B decay vectors (4 B per lane) into the wave's copy.
-__device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace& ws, size_t wsidx,
-                                           size_t ktidx, int cb, int wave, int lane) {
-    const f16* wsrc = ws.w + wsidx * kWElems;
-    const f16* ksrc = ws.kt + ktidx * kKtElems;
-    const f16* usrc = ws.u + wsidx * kUElems + (size_t)cb * kStageU;
-    const float* gsrc = ws.gcum + wsidx * kGElems;
+// One chunk's copies by wave `wave`: its share of the 1 KB pieces (16 B per
+// lane) of -W and K^T, its own tiles' U and its own copy of the decay vectors.
+template <int NW, int TPW>
+__device__ __forceinline__ void state_copy(StateStage<NW, TPW>& st, const ChunkWorkspace& ws, size_t vu,
+                                           size_t ku, int ct0, int wave, int lane) {
+    const f16* wsrc = ws.w + vu * kWElems;
+    const f16* ksrc = ws.kt + ku * kKtElems;
+    const f16* usrc = ws.u + vu * kUElems + (size_t)ct0 * kUTile;   // tiles ct0 .. ct0 + TPW - 1
+    const float* gsrc = ws.gcum + vu * kGElems;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int piece = wave * 4 + i;
+    for (int i = 0; i < 16 / NW; ++i) {
+        const int piece = wave * (16 / NW) + i;
         __builtin_amdgcn_global_load_lds(wsrc + (piece * 64 + lane) * 8, st.w + piece * 512, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(ksrc + (piece * 64 + lane) * 8, st.k + piece * 512, 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int piece = wave * 2 + i;
-        __builtin_amdgcn_global_load_lds(usrc + (piece * 64 + lane) * 8, st.u + piece * 512, 16, 0, 0);
-    }
+    for (int piece = 0; piece < 2 * TPW; ++piece)
+        __builtin_amdgcn_global_load_lds(usrc + (piece * 64 + lane) * 8, st.u[wave] + piece * 512, 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds(gsrc + i * 64 + lane, &st.g[wave][i * 64], 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(gsrc + i * 64 + lane, st.g[wave] + i * 64, 4, 0, 0);
 }
 
-// Results of one chunk that the output stage needs.
+// Results of one chunk that the output stage needs, per column tile.
 struct StateOut {
     f16x8 hb[4];   // incoming chunk state, B fragments over d_k
     f16x8 up[2];   // U', B fragments over positions
 };
 
-__device__ __forceinline__ void state_store(const StateOut& o, const ChunkWorkspace& ws, size_t wsidx,
-                                            int ct, int lane) {
-    f16* hdst = ws.hc + wsidx * kHcElems;
+template <int TPW>
+__device__ __forceinline__ void state_store(const StateOut (&o)[TPW], const ChunkWorkspace& ws, size_t vu,
+                                            int ct0, int lane) {
+    f16* hdst = ws.hc + vu * kHcElems;
+    f16* udst = ws.up + vu * kUpElems;
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq)
-        *reinterpret_cast<f16x8*>(hdst + ((ct * 4 + qq) * 64 + lane) * 8) = o.hb[qq];
-    f16* udst = ws.up + wsidx * kUpElems;
+    for (int t = 0; t < TPW; ++t) {
+        const int ct = ct0 + t;
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
-        *reinterpret_cast<f16x8*>(udst + ((ct * 2 + qq) * 64 + lane) * 8) = o.up[qq];
+        for (int qq = 0; qq < 4; ++qq)
+            *reinterpret_cast<f16x8*>(hdst + ((ct * 4 + qq) * 64 + lane) * 8) = o[t].hb[qq];
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+            *reinterpret_cast<f16x8*>(udst + ((ct * 2 + qq) * 64 + lane) * 8) = o[t].up[qq];
+    }
 }
 
-// One chunk of the recurrence for this wave's 16 columns.
-__device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st, StateOut& o,
-                                            int wave, int lane, int gq) {
-    // U accumulator fragments of this wave's column tile
-    f32x4 acc[4];
+// One chunk of the recurrence for one wave's TPW column tiles.
+template <int NW, int TPW>
+__device__ __forceinline__ void state_chunk(f32x4 (&H)[TPW][8], const StateStage<NW, TPW>& st,
+                                            StateOut (&o)[TPW], int wave, int lane, int gq) {
+    // U accumulator fragments of the column tiles
+    f32x4 acc[TPW][4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const f16x4 uf = *reinterpret_cast<const f16x4*>(&st.u[((wave * 4 + p) * 64 + lane) * 4]);
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[p][e] = static_cast<float>(uf[e]);
-    }
+        for (int p = 0; p < 4; ++p) {
+            const f16x4 uf = *reinterpret_cast<const f16x4*>(&st.u[wave][t * kUTile + (p * 64 + lane) * 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[t][p][e] = static_cast<float>(uf[e]);
+        }
     // incoming chunk state as B fragments (d_k slots), kept for the output stage
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) o.hb[qq] = cat_to_f16(H[2 * qq], H[2 * qq + 1]);
-    // U' = U + (-W) H
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) o[t].hb[qq] = cat_to_f16(H[t][2 * qq], H[t][2 * qq + 1]);
+    // U' = U + (-W) H, one -W fragment per pair (p, qq) serving all tiles;
+    // all sixteen fragments are read before the matrix-core burst
+    f16x8 wa[4][4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const f16x8 wa = *reinterpret_cast<const f16x8*>(&st.w[((p * 4 + qq) * 64 + lane) * 8]);
-            acc[p] = mfma_f16(wa, o.hb[qq], acc[p]);
-        }
-    // U' as B fragments (position slots), kept for the output stage
+        for (int p = 0; p < 4; ++p)
+            wa[qq][p] = *reinterpret_cast<const f16x8*>(&st.w[((p * 4 + qq) * 64 + lane) * 8]);
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) o.up[qq] = cat_to_f16(acc[2 * qq], acc[2 * qq + 1]);
-    // X = diag(e^{G_C - G}) U';   H <- e^{G_C} H + K^T X
-    const float* dec = st.g[wave];
+    for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+        for (int p = 0; p < 4; ++p)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            acc[p][e] *= dec[16 * p + 4 * gq + e];
-    f16x8 xb[2];
+            for (int t = 0; t < TPW; ++t) acc[t][p] = mfma_f16(wa[qq][p], o[t].hb[qq], acc[t][p]);
+    // U' as B fragments (position slots): kept for the output stage, and the
+    // B operand of the update, whose A operand K^T diag(e^{G_C - G}) carries
+    // the decay:  H <- e^{G_C} H + (K^T diag(e^{G_C - G})) U'
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) xb[qq] = cat_to_f16(acc[2 * qq], acc[2 * qq + 1]);
-    const float gam = dec[kChunk + kChunk - 1];
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) H[i] *= gam;
-    // eight independent accumulator chains, interleaved
+        for (int qq = 0; qq < 2; ++qq) o[t].up[qq] = cat_to_f16(acc[t][2 * qq], acc[t][2 * qq + 1]);
+    const float gam = st.g[wave][kChunk + kChunk - 1];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) H[t][i] *= gam;
+    // independent accumulator chains, interleaved; one K^T fragment per (i, qq)
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const f16x8 ka = *reinterpret_cast<const f16x8*>(&st.k[((i * 2 + qq) * 64 + lane) * 8]);
-            H[i] = mfma_f16(ka, xb[qq], H[i]);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) H[t][i] = mfma_f16(ka, o[t].up[qq], H[t][i]);
         }
 }
 
-__global__ __launch_bounds__(256) void gdn_chunk_state(
+// Grid: 8 * ceil(U / 8) * P workgroups of 64 NW threads, U = n_seqs * h_v,
+// P = 8 / (NW * TPW) workgroups per unit.  Workgroup b runs on XCD b % 8
+// (round-robin dispatch); it takes unit 8 * (m / P) + b % 8 and column group
+// m % P, m = b / 8, so all workgroups of a unit share an XCD.
+template <int NW, int TPW>
+__global__ __launch_bounds__(64 * NW) void gdn_chunk_state(
     const int32_t* __restrict__ cu, int n_seqs, int h_qk, int h_v,
     const float* __restrict__ s0, float* __restrict__ s_final, ChunkWorkspace ws)
 {
-    const int nh = blockIdx.x;
-    const int seq = nh / h_v;
-    const int h = nh % h_v;
-    const int cb = blockIdx.y;
+    constexpr int P = 8 / (NW * TPW);
+    constexpr int kWait = copies_per_chunk<NW, TPW>() + stores_per_chunk<TPW>();
+    const int b = blockIdx.x;
+    const int m = b >> 3;
+    const int unit = (m / P) * 8 + (b & 7);
+    if (unit >= n_seqs * h_v) return;
+    const int seq = unit / h_v;
+    const int h = unit % h_v;
     const int j = h / (h_v / h_qk);
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = NW == 1 ? 0 : (int)(threadIdx.x >> 6);
     const int gq = lane >> 4;
     const int ln = lane & 15;
-    const int ct = cb * 4 + wave;        // column tile 0..7
-    const int col = 16 * ct + ln;
+    const int ct0 = ((m % P) * NW + wave) * TPW;   // first column tile of this wave
 
-    __shared__ __attribute__((aligned(16))) StateStage stage[kStages];
+    __shared__ __attribute__((aligned(16))) StateStage<NW, TPW> stage[kStages];
 
     const int start = cu[seq];
     const int end = cu[seq + 1];
     const int nchunks = (end - start + kChunk - 1) / kChunk;
     const int slot0 = slot_base(cu, seq);
     const int last = nchunks - 1;
-    auto widx = [&](int c) { return (size_t)(slot0 + min(c, last)) * h_v + h; };
-    auto kidx = [&](int c) { return (size_t)(slot0 + min(c, last)) * h_qk + j; };
+    auto vidx = [&](int c) { return ws.vunit(slot0 + min(c, last), h); };
+    auto kidx = [&](int c) { return ws.vunit(slot0 + min(c, last), h); };
 
     // ---- incoming state
-    f32x4 H[8];
+    f32x4 H[TPW][8];
     const size_t sbase = ((size_t)seq * h_v + h) * kDim * kDim;
-    if (s0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+    for (int t = 0; t < TPW; ++t) {
+        const int col = 16 * (ct0 + t) + ln;
+        if (s0) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                H[i][e] = s0[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col];
-    } else {
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) H[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int e = 0; e < 4; ++e)
+                    H[t][i][e] = s0[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) H[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     // settle the initial-state loads before the copies start counting
     __builtin_amdgcn_s_waitcnt(0);
@@ -460,41 +516,56 @@ __global__ __launch_bounds__(256) void gdn_chunk_state(
     if (nchunks > 0) {
         // copies are issued for chunks past the last one too (clamped to the
         // last chunk, never used) so the count in flight is always the same
-        state_copy(stage[0], ws, widx(0), kidx(0), cb, wave, lane);
-        state_copy(stage[1], ws, widx(1), kidx(1), cb, wave, lane);
-        StateOut pa, pb;
+        state_copy<NW, TPW>(stage[0], ws, vidx(0), kidx(0), ct0, wave, lane);
+        state_copy<NW, TPW>(stage[1], ws, vidx(1), kidx(1), ct0, wave, lane);
+        StateOut pa[TPW], pb[TPW];
         int c = 0;
+        // At the wait for chunk c, the operations issued after its copies are
+        // the stores of chunk c - 2 and the copies of chunk c + 1.
         for (;;) {
             // chunk c (even) -> pa
-            wait_vmcnt<kCopiesPerChunk>();      // this wave's copies of chunk c have landed
-            wg_barrier();                       // ... and every other wave's
-            if (c > 0) state_store(pb, ws, widx(c - 1), ct, lane);
-            state_copy(stage[(c + 2) % kStages], ws, widx(c + 2), kidx(c + 2), cb, wave, lane);
-            state_chunk(H, stage[c % kStages], pa, wave, lane, gq);
+            wait_vmcnt<kWait>();
+            if (NW > 1) wg_barrier();
+            if (c > 0) state_store<TPW>(pb, ws, vidx(c - 1), ct0, lane);
+            state_copy<NW, TPW>(stage[(c + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), ct0, wave, lane);
+            state_chunk<NW, TPW>(H, stage[c % kStages], pa, wave, lane, gq);
             if (++c >= nchunks) break;
             // chunk c (odd) -> pb
-            wait_vmcnt<kCopiesPerChunk>();
-            wg_barrier();
-            state_store(pa, ws, widx(c - 1), ct, lane);
-            state_copy(stage[(c + 2) % kStages], ws, widx(c + 2), kidx(c + 2), cb, wave, lane);
-            state_chunk(H, stage[c % kStages], pb, wave, lane, gq);
+            wait_vmcnt<kWait>();
+            if (NW > 1) wg_barrier();
+            state_store<TPW>(pa, ws, vidx(c - 1), ct0, lane);
+            state_copy<NW, TPW>(stage[(c + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), ct0, wave, lane);
+            state_chunk<NW, TPW>(H, stage[c % kStages], pb, wave, lane, gq);
             if (++c >= nchunks) break;
         }
-        if (nchunks & 1) state_store(pa, ws, widx(last), ct, lane);
-        else state_store(pb, ws, widx(last), ct, lane);
-        // drain the copies of the two chunks past the end before the workgroup
+        if (nchunks & 1) state_store<TPW>(pa, ws, vidx(last), ct0, lane);
+        else state_store<TPW>(pb, ws, vidx(last), ct0, lane);
+        // drain the copies of the chunks past the end before the workgroup
         // exits (the LDS they target must stay allocated until they land)
         __builtin_amdgcn_s_waitcnt(0);
     }
 
     if (s_final) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int t = 0; t < TPW; ++t) {
+            const int col = 16 * (ct0 + t) + ln;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                s_final[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col] = H[i][e];
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s_final[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col] = H[t][i][e];
+        }
     }
 }
+
+#ifndef GDN_STATE_WAVES
+#define GDN_STATE_WAVES 1
+#endif
+#ifndef GDN_STATE_TILES
+#define GDN_STATE_TILES 1
+#endif
+constexpr int kStateWaves = GDN_STATE_WAVES;
+constexpr int kStateTiles = GDN_STATE_TILES;
 
 // ---------------------------------------------------------------------------
 // Stage 3: output.  One workgroup per (chunk slot, value head).
@@ -511,8 +582,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_out(
     if (!resolve_slot(cu, n_seqs, slot, seq, t0, len)) return;
     const int j = h / (h_v / h_qk);
 
-    __shared__ __attribute__((aligned(16))) f16 Qs[kChunk * kQS];   // Q [pos][dim]
-    __shared__ __attribute__((aligned(16))) f16 Ks[kChunk * kQS];   // K [pos][dim]
+    // Q and K row tiles, reused at the end as the fp32 output staging tile
+    __shared__ __attribute__((aligned(16))) f16 QKs[2 * kChunk * kQS];
+    f16* const Qs = QKs;                 // Q [pos][dim]
+    f16* const Ks = QKs + kChunk * kQS;  // K [pos][dim]
     __shared__ __attribute__((aligned(16))) f16 Ps[kChunk * kTS];   // P [pos][pos]
     __shared__ float Gs[kChunk];   // G_r
     __shared__ float Es[kChunk];   // e^{G_r}
@@ -522,7 +595,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_out(
     const int wave = tid >> 6;
     const int gq = lane >> 4;
     const int ln = lane & 15;
-    const size_t wsidx = (size_t)slot * h_v + h;
+    const size_t wsidx = ws.vunit(slot, h);
 
     for (int i = tid; i < kChunk * 16; i += 256) {
         const int r = i >> 4;
@@ -619,17 +692,27 @@ __global__ __launch_bounds__(256) void gdn_chunk_out(
         }
     }
 
+    // ---- stage the 64 x 128 fp32 tile in LDS (over Q and K, now dead) and
+    //      write whole 512-byte token rows with 16-byte stores
+    __syncthreads();
+    constexpr int kOS = 132;   // fp32 row stride
+    float* Os = reinterpret_cast<float*>(Qs);
 #pragma unroll
     for (int p = 0; p < 4; ++p)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * p + 4 * gq + e;
-            if (r < len) {
-                float* orow = out + ((size_t)(t0 + r) * h_v + h) * kDim;
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-                for (int a = 0; a < 2; ++a) orow[16 * (2 * wave + a) + ln] = o[p][a][e];
-            }
-        }
+            for (int a = 0; a < 2; ++a)
+                Os[(16 * p + 4 * gq + e) * kOS + 16 * (2 * wave + a) + ln] = o[p][a][e];
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int idx = tid + 256 * it;
+        const int r = idx >> 5, c4 = (idx & 31) * 4;
+        if (r < len)
+            *reinterpret_cast<f32x4*>(out + ((size_t)(t0 + r) * h_v + h) * kDim + c4) =
+                *reinterpret_cast<const f32x4*>(Os + r * kOS + c4);
+    }
 }
 
 }  // namespace
@@ -647,8 +730,10 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
                            k, v, g, beta, cu, n_seqs, h_qk, h_v, ws);
     }
     if ((stage_mask & 2) && n_seqs > 0) {
-        hipLaunchKernelGGL(gdn_chunk_state, dim3(n_seqs * h_v, kDim / 64), dim3(256), 0, stream,
-                           cu, n_seqs, h_qk, h_v, s0, s_final, ws);
+        const int units = n_seqs * h_v;
+        hipLaunchKernelGGL((gdn_chunk_state<kStateWaves, kStateTiles>),
+                           dim3(8 * ((units + 7) / 8) * (8 / (kStateWaves * kStateTiles))),
+                           dim3(64 * kStateWaves), 0, stream, cu, n_seqs, h_qk, h_v, s0, s_final, ws);
     }
     if ((stage_mask & 4) && total_tokens > 0) {
         hipLaunchKernelGGL(gdn_chunk_out, dim3(n_slots, h_v), dim3(256), 0, stream,

@@ -41,9 +41,12 @@ constexpr size_t kUpElems = 8 * 2 * 64 * 8; // U', B-operand fragments [ct][qq][
 constexpr size_t kHcElems = 8 * 4 * 64 * 8; // chunk state, B-operand fragments [ct][qq][lane][8]
 // Decay vectors: [0, 64) e^{G_C - G_r} (state update), [64, 128) e^{G_r}, [128, 192) G_r
 constexpr size_t kGElems = 192;
-// Per (chunk slot, q/k head): K^T as A-operand fragments of K^T X [d_k tile][pos step][lane][8]
+// K^T diag(e^{G_C - G}) as A-operand fragments of the state update [d_k tile][pos step][lane][8]
 constexpr size_t kKtElems = 8 * 2 * 64 * 8;
 
+// Workspace regions are head-major: unit (slot, head) sits at head * n_slots
+// + slot, so one head's consecutive chunks are contiguous in memory and the
+// state recurrence streams through them in address order.
 struct ChunkWorkspace {
     f16* w;
     f16* u;
@@ -51,6 +54,9 @@ struct ChunkWorkspace {
     f16* hc;
     f16* kt;
     float* gcum;
+    int n_slots;
+
+    __device__ __forceinline__ size_t vunit(int slot, int h) const { return (size_t)h * n_slots + slot; }
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

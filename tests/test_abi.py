@@ -71,9 +71,8 @@ def test_workspace_size_formula(lib):
     st, b = ws_size(lib, dims(n=1, T=4000, hqk=16, hv=32))
     assert st == 0
     slots = 1 + 4000 // 64 + 1
-    per_v = (8192 + 8192 + 8192 + 16384) * 2 + 192 * 4    # W, U, U', chunk state, decay vectors per value head
-    per_qk = 8192 * 2                                      # K^T fragments per q/k head
-    need = slots * (32 * per_v + 16 * per_qk)
+    per_v = (8192 * 4 + 16384) * 2 + 192 * 4    # W, U, U', decayed K^T, chunk state, decay vectors
+    need = slots * 32 * per_v
     assert need <= b < need + 6 * 256
 
 
