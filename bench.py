@@ -41,26 +41,50 @@ def algorithmic_work():
     """Per-token algorithmic flops and bytes of each prefill stage (config dims).
 
     Flops count each causal (triangular) product at half and the K K^T / Q K^T
-    Grams once per q/k head.  Bytes count each tensor a stage must read or
-    write once (fp16 intermediates, bf16 inputs, fp32 g/beta/output)."""
+    Grams once per q/k head.  Bytes count each tensor of a stage's interface
+    read or written once: bf16 inputs, fp32 g / beta / output, fp16
+    intermediates (W, U, K^T diag(e^{G_C-G}) per value head, U', chunk states)
+    and fp32 decay vectors."""
     prep_f = H_V * (C * (D + D) + C * C / 3) + H_QK * (C * D)
     state_f = H_V * (4 * D * D)
     out_f = H_V * (2 * D * D + C * D) + H_QK * (C * D)
     qk_b = H_QK * D * 2          # one of q or k, bf16
     v_b = H_V * D * 2
     gb_b = H_V * 4               # one of g or beta
-    f16_row = H_V * D * 2        # one of W, U, U' per token
+    f16_row = H_V * D * 2        # one of W, U, K^T-decayed, U' per token
     hc_b = H_V * D * D * 2 / C   # fp16 chunk state, per token
     out_b = H_V * D * 4
-    prep_b = qk_b + v_b + 2 * gb_b + 2 * f16_row + gb_b
-    state_b = 2 * f16_row + qk_b + gb_b + f16_row + hc_b
-    out_b_tot = 2 * qk_b + gb_b + hc_b + f16_row + out_b
+    dec_w = 3 * gb_b             # e^{G_C - G}, e^G, G written by prep
+    dec_r = 2 * gb_b             # two of them read by state / out
+    prep_b = qk_b + v_b + 2 * gb_b + 3 * f16_row + dec_w
+    state_b = 3 * f16_row + dec_r + f16_row + hc_b
+    out_b_tot = 2 * qk_b + dec_r + hc_b + f16_row + out_b
     return {
         "prep": (prep_f, prep_b),
         "state": (state_f, state_b),
         "out": (out_f, out_b_tot),
         "layer": (prep_f + state_f + out_f, 2 * qk_b + v_b + 2 * gb_b + out_b),
     }
+
+
+# HBM bytes per launch of the state kernel at T = 4000, from rocprofv3
+# FETCH_SIZE / WRITE_SIZE runs scaled by a plain 1 GiB copy (fetch x 2.0,
+# write x 1.0); valid only for the kernel source they were taken with.
+MEASURED_TRAFFIC = {
+    "gdn_chunk_state": {"bytes": 201466164, "source_sha256_prefix": "4ca35fe904366b59",
+                        "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
+}
+
+
+def measured_traffic(kernel: str):
+    import hashlib
+    rec = MEASURED_TRAFFIC.get(kernel)
+    if rec is None:
+        return None
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != rec["source_sha256_prefix"]:
+            return None      # kernel changed since the counters were taken
+    return rec["bytes"]
 
 
 def time_launches(fn, n, torch):
@@ -101,7 +125,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the CPU-oracle baseline (0 skips it)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run 5 plain device-to-device copies of BYTES bytes (reference for "
+                         "the HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 5}), flush=True)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer's path runs on a single MI355X "
@@ -164,8 +201,8 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": nbytes / t_dom / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
     roof["kernel"] = f"gdn_chunk_{dom}"
+    roof["traffic"] = measured_traffic(roof["kernel"])
     roof["mean_launch_us"] = t_dom * 1e6
     roof["algorithmic_flops_per_launch"] = flops
     roof["algorithmic_bytes_per_launch"] = nbytes
