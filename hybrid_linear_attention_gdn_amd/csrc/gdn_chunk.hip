@@ -305,41 +305,39 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2: inter-chunk state recurrence.  A workgroup of NW waves owns
-// 16 * TPW * NW state columns of one (sequence, value head); each wave owns
-// TPW column tiles of 16 and keeps their 128 x 16 slices of the state in
-// accumulator registers (8 tiles of 16 d_k rows each) for the whole
-// sequence.  A wave's tiles share every -W and K^T fragment it reads from
-// LDS, and their two dependency chains interleave.  Per chunk the workgroup
-// reads -W fragments (16 KB) and K^T fragments (16 KB), shared by its waves,
-// plus each wave's U fragments and decay vectors, by direct global-to-LDS
-// copies into a ring of three stages, two chunks ahead.  Every wave issues
-// the same fixed number of copies per chunk, so a memory-counter wait on its
-// own copies (plus a barrier when NW > 1) makes a stage ready.  The
-// workgroups of one head are placed on one XCD so that its L2 serves the
-// shared fragments.
-//
-// Each chunk's results for the output stage (its incoming state and U') are
-// stored at the top of the next chunk from one of two register sets that
-// alternate, so a store always has a whole chunk to retire before its data
-// registers are rewritten; vector-memory counters retire in order and a
-// store's data registers cannot be reused before it has.
+// Stage 2: inter-chunk state recurrence.  One workgroup of two waves per
+// (sequence, value head, 16-column tile), specialised:
+//   * the compute wave keeps the tile's 128 x 16 slice of the state in
+//     accumulator registers (8 tiles of 16 d_k rows) for the whole sequence
+//     and per chunk only reads operand fragments from LDS, runs the 32
+//     matrix-core products and hands the chunk's results (its incoming state
+//     and U', for the output stage) to LDS;
+//   * the copy wave moves operands in and results out: per chunk it issues
+//     direct global-to-LDS copies of -W fragments (16 KB), decayed K^T
+//     fragments (16 KB), the tile's U fragments (2 KB) and the decay vectors
+//     into a ring of three stages, two chunks ahead, and stores the previous
+//     chunk's hand-off to global memory.
+// The waves meet at one barrier per chunk.  The copy wave issues a fixed
+// number of memory operations per chunk, so one memory-counter wait on its
+// copies makes a stage ready before that barrier.  The eight tiles of a head
+// run on one XCD so that its L2 serves the shared fragments.
 // ---------------------------------------------------------------------------
 constexpr int kStages = 3;
-constexpr int kUTile = 4 * 64 * 4;     // halves of U fragments per column tile
+constexpr int kUTile = 4 * 64 * 4;                           // halves of U fragments per tile
+constexpr int kCopiesPerChunk = 16 + 16 + 2 + 2;             // -W, K^T, U, decay vectors
+constexpr int kStoresPerChunk = 4 + 2;                        // chunk state, U'
 
-template <int NW, int TPW>
 struct StateStage {
     f16 w[kWElems];
     f16 k[kKtElems];
-    f16 u[NW][TPW * kUTile];  // each wave's U accumulator fragments
-    float g[NW][2 * kChunk];  // each wave's copy of e^{G_C - G_r}, e^{G_r}
+    f16 u[kUTile];
+    float g[2 * kChunk];      // e^{G_C - G_r}, then e^{G_r}
 };
 
-template <int NW, int TPW>
-constexpr int copies_per_chunk() { return 2 * (16 / NW) + 2 * TPW + 2; }
-template <int TPW>
-constexpr int stores_per_chunk() { return 6 * TPW; }
+struct StateHandoff {
+    f16 hb[4][64 * 8];        // incoming chunk state, B fragments over d_k
+    f16 up[2][64 * 8];        // U', B fragments over positions
+};
 
 // s_waitcnt with vmcnt = N and the other counters left alone (gfx9 encoding).
 template <int N>
@@ -350,79 +348,71 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ void wg_barrier() {
+// Wait for this wave's LDS operations, then the workgroup barrier.
+__device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
 
-// One chunk's copies by wave `wave`: its share of the 1 KB pieces (16 B per
-// lane) of -W and K^T, its own tiles' U and its own copy of the decay vectors.
-template <int NW, int TPW>
-__device__ __forceinline__ void state_copy(StateStage<NW, TPW>& st, const ChunkWorkspace& ws, size_t vu,
-                                           size_t ku, int ct0, int wave, int lane) {
+// One chunk's copies: 1 KB pieces (16 B per lane) of -W, K^T and U, and the
+// two 256 B decay vectors (4 B per lane).
+__device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace& ws, size_t vu, int ct, int lane) {
     const f16* wsrc = ws.w + vu * kWElems;
-    const f16* ksrc = ws.kt + ku * kKtElems;
-    const f16* usrc = ws.u + vu * kUElems + (size_t)ct0 * kUTile;   // tiles ct0 .. ct0 + TPW - 1
+    const f16* ksrc = ws.kt + vu * kKtElems;
+    const f16* usrc = ws.u + vu * kUElems + (size_t)ct * kUTile;
     const float* gsrc = ws.gcum + vu * kGElems;
 #pragma unroll
-    for (int i = 0; i < 16 / NW; ++i) {
-        const int piece = wave * (16 / NW) + i;
+    for (int piece = 0; piece < 16; ++piece) {
         __builtin_amdgcn_global_load_lds(wsrc + (piece * 64 + lane) * 8, st.w + piece * 512, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(ksrc + (piece * 64 + lane) * 8, st.k + piece * 512, 16, 0, 0);
     }
 #pragma unroll
-    for (int piece = 0; piece < 2 * TPW; ++piece)
-        __builtin_amdgcn_global_load_lds(usrc + (piece * 64 + lane) * 8, st.u[wave] + piece * 512, 16, 0, 0);
+    for (int piece = 0; piece < 2; ++piece)
+        __builtin_amdgcn_global_load_lds(usrc + (piece * 64 + lane) * 8, st.u + piece * 512, 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds(gsrc + i * 64 + lane, st.g[wave] + i * 64, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(gsrc + i * 64 + lane, st.g + i * 64, 4, 0, 0);
 }
 
-// Results of one chunk that the output stage needs, per column tile.
-struct StateOut {
-    f16x8 hb[4];   // incoming chunk state, B fragments over d_k
-    f16x8 up[2];   // U', B fragments over positions
-};
-
-template <int TPW>
-__device__ __forceinline__ void state_store(const StateOut (&o)[TPW], const ChunkWorkspace& ws, size_t vu,
-                                            int ct0, int lane) {
+// Store one chunk's hand-off (read back from LDS) to the workspace.
+__device__ __forceinline__ void state_store(const StateHandoff& ho, const ChunkWorkspace& ws, size_t vu,
+                                            int ct, int lane) {
     f16* hdst = ws.hc + vu * kHcElems;
     f16* udst = ws.up + vu * kUpElems;
+    f16x8 hb[4], up[2];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int ct = ct0 + t;
+    for (int qq = 0; qq < 4; ++qq) hb[qq] = *reinterpret_cast<const f16x8*>(&ho.hb[qq][lane * 8]);
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-            *reinterpret_cast<f16x8*>(hdst + ((ct * 4 + qq) * 64 + lane) * 8) = o[t].hb[qq];
+    for (int qq = 0; qq < 2; ++qq) up[qq] = *reinterpret_cast<const f16x8*>(&ho.up[qq][lane * 8]);
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq)
-            *reinterpret_cast<f16x8*>(udst + ((ct * 2 + qq) * 64 + lane) * 8) = o[t].up[qq];
-    }
+    for (int qq = 0; qq < 4; ++qq)
+        *reinterpret_cast<f16x8*>(hdst + ((ct * 4 + qq) * 64 + lane) * 8) = hb[qq];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+        *reinterpret_cast<f16x8*>(udst + ((ct * 2 + qq) * 64 + lane) * 8) = up[qq];
 }
 
-// One chunk of the recurrence for one wave's TPW column tiles.
-template <int NW, int TPW>
-__device__ __forceinline__ void state_chunk(f32x4 (&H)[TPW][8], const StateStage<NW, TPW>& st,
-                                            StateOut (&o)[TPW], int wave, int lane, int gq) {
-    // U accumulator fragments of the column tiles
-    f32x4 acc[TPW][4];
+// One chunk of the recurrence for the compute wave's 16 columns.
+__device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st, StateHandoff& ho,
+                                            int lane, int gq) {
+    // U accumulator fragments of this column tile
+    f32x4 acc[4];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+    for (int p = 0; p < 4; ++p) {
+        const f16x4 uf = *reinterpret_cast<const f16x4*>(&st.u[(p * 64 + lane) * 4]);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const f16x4 uf = *reinterpret_cast<const f16x4*>(&st.u[wave][t * kUTile + (p * 64 + lane) * 4]);
+        for (int e = 0; e < 4; ++e) acc[p][e] = static_cast<float>(uf[e]);
+    }
+    // incoming chunk state as B fragments (d_k slots), handed to the output stage
+    f16x8 hb[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[t][p][e] = static_cast<float>(uf[e]);
-        }
-    // incoming chunk state as B fragments (d_k slots), kept for the output stage
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) o[t].hb[qq] = cat_to_f16(H[t][2 * qq], H[t][2 * qq + 1]);
-    // U' = U + (-W) H, one -W fragment per pair (p, qq) serving all tiles;
-    // all sixteen fragments are read before the matrix-core burst
+    for (int qq = 0; qq < 4; ++qq) {
+        hb[qq] = cat_to_f16(H[2 * qq], H[2 * qq + 1]);
+        *reinterpret_cast<f16x8*>(&ho.hb[qq][lane * 8]) = hb[qq];
+    }
+    // U' = U + (-W) H; all sixteen -W fragments are read before the burst
     f16x8 wa[4][4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
@@ -432,58 +422,53 @@ __device__ __forceinline__ void state_chunk(f32x4 (&H)[TPW][8], const StateStage
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) acc[t][p] = mfma_f16(wa[qq][p], o[t].hb[qq], acc[t][p]);
-    // U' as B fragments (position slots): kept for the output stage, and the
+        for (int p = 0; p < 4; ++p) acc[p] = mfma_f16(wa[qq][p], hb[qq], acc[p]);
+    // U' as B fragments (position slots): handed to the output stage, and the
     // B operand of the update, whose A operand K^T diag(e^{G_C - G}) carries
     // the decay:  H <- e^{G_C} H + (K^T diag(e^{G_C - G})) U'
+    f16x8 up[2];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+    for (int qq = 0; qq < 2; ++qq) {
+        up[qq] = cat_to_f16(acc[2 * qq], acc[2 * qq + 1]);
+        *reinterpret_cast<f16x8*>(&ho.up[qq][lane * 8]) = up[qq];
+    }
+    const float gam = st.g[kChunk + kChunk - 1];
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) o[t].up[qq] = cat_to_f16(acc[t][2 * qq], acc[t][2 * qq + 1]);
-    const float gam = st.g[wave][kChunk + kChunk - 1];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) H[t][i] *= gam;
-    // independent accumulator chains, interleaved; one K^T fragment per (i, qq)
+    for (int i = 0; i < 8; ++i) H[i] *= gam;
+    // eight independent accumulator chains, interleaved
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const f16x8 ka = *reinterpret_cast<const f16x8*>(&st.k[((i * 2 + qq) * 64 + lane) * 8]);
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) H[t][i] = mfma_f16(ka, o[t].up[qq], H[t][i]);
+            H[i] = mfma_f16(ka, up[qq], H[i]);
         }
 }
 
-// Grid: 8 * ceil(U / 8) * P workgroups of 64 NW threads, U = n_seqs * h_v,
-// P = 8 / (NW * TPW) workgroups per unit.  Workgroup b runs on XCD b % 8
-// (round-robin dispatch); it takes unit 8 * (m / P) + b % 8 and column group
-// m % P, m = b / 8, so all workgroups of a unit share an XCD.
-template <int NW, int TPW>
-__global__ __launch_bounds__(64 * NW) void gdn_chunk_state(
-    const int32_t* __restrict__ cu, int n_seqs, int h_qk, int h_v,
+// Grid: 8 * ceil(U / 8) * 8 workgroups of 128 threads, U = n_seqs * h_v.
+// Workgroup b runs on XCD b % 8 (round-robin dispatch); it takes unit
+// 8 * (m / 8) + b % 8 and column tile m % 8, m = b / 8, so all tiles of a
+// unit share an XCD.
+__global__ __launch_bounds__(128) void gdn_chunk_state(
+    const int32_t* __restrict__ cu, int n_seqs, int h_v,
     const float* __restrict__ s0, float* __restrict__ s_final, ChunkWorkspace ws)
 {
-    constexpr int P = 8 / (NW * TPW);
-    constexpr int kWait = copies_per_chunk<NW, TPW>() + stores_per_chunk<TPW>();
     const int b = blockIdx.x;
     const int m = b >> 3;
-    const int unit = (m / P) * 8 + (b & 7);
+    const int unit = ((m >> 3) << 3) + (b & 7);
     if (unit >= n_seqs * h_v) return;
+    const int ct = m & 7;
     const int seq = unit / h_v;
     const int h = unit % h_v;
-    const int j = h / (h_v / h_qk);
 
     const int lane = threadIdx.x & 63;
-    const int wave = NW == 1 ? 0 : (int)(threadIdx.x >> 6);
+    const bool compute = threadIdx.x < 64;
     const int gq = lane >> 4;
     const int ln = lane & 15;
-    const int ct0 = ((m % P) * NW + wave) * TPW;   // first column tile of this wave
+    const int col = 16 * ct + ln;
 
-    __shared__ __attribute__((aligned(16))) StateStage<NW, TPW> stage[kStages];
+    __shared__ __attribute__((aligned(16))) StateStage stage[kStages];
+    __shared__ __attribute__((aligned(16))) StateHandoff handoff[2];
 
     const int start = cu[seq];
     const int end = cu[seq + 1];
@@ -491,81 +476,57 @@ __global__ __launch_bounds__(64 * NW) void gdn_chunk_state(
     const int slot0 = slot_base(cu, seq);
     const int last = nchunks - 1;
     auto vidx = [&](int c) { return ws.vunit(slot0 + min(c, last), h); };
-    auto kidx = [&](int c) { return ws.vunit(slot0 + min(c, last), h); };
-
-    // ---- incoming state
-    f32x4 H[TPW][8];
     const size_t sbase = ((size_t)seq * h_v + h) * kDim * kDim;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int col = 16 * (ct0 + t) + ln;
+
+    if (compute) {
+        f32x4 H[8];
         if (s0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    H[t][i][e] = s0[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col];
+                    H[i][e] = s0[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col];
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) H[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < 8; ++i) H[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    }
-    // settle the initial-state loads before the copies start counting
-    __builtin_amdgcn_s_waitcnt(0);
-
-    if (nchunks > 0) {
-        // copies are issued for chunks past the last one too (clamped to the
-        // last chunk, never used) so the count in flight is always the same
-        state_copy<NW, TPW>(stage[0], ws, vidx(0), kidx(0), ct0, wave, lane);
-        state_copy<NW, TPW>(stage[1], ws, vidx(1), kidx(1), ct0, wave, lane);
-        StateOut pa[TPW], pb[TPW];
-        int c = 0;
-        // At the wait for chunk c, the operations issued after its copies are
-        // the stores of chunk c - 2 and the copies of chunk c + 1.
-        for (;;) {
-            // chunk c (even) -> pa
-            wait_vmcnt<kWait>();
-            if (NW > 1) wg_barrier();
-            if (c > 0) state_store<TPW>(pb, ws, vidx(c - 1), ct0, lane);
-            state_copy<NW, TPW>(stage[(c + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), ct0, wave, lane);
-            state_chunk<NW, TPW>(H, stage[c % kStages], pa, wave, lane, gq);
-            if (++c >= nchunks) break;
-            // chunk c (odd) -> pb
-            wait_vmcnt<kWait>();
-            if (NW > 1) wg_barrier();
-            state_store<TPW>(pa, ws, vidx(c - 1), ct0, lane);
-            state_copy<NW, TPW>(stage[(c + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), ct0, wave, lane);
-            state_chunk<NW, TPW>(H, stage[c % kStages], pb, wave, lane, gq);
-            if (++c >= nchunks) break;
-        }
-        if (nchunks & 1) state_store<TPW>(pa, ws, vidx(last), ct0, lane);
-        else state_store<TPW>(pb, ws, vidx(last), ct0, lane);
-        // drain the copies of the chunks past the end before the workgroup
-        // exits (the LDS they target must stay allocated until they land)
         __builtin_amdgcn_s_waitcnt(0);
-    }
-
-    if (s_final) {
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int col = 16 * (ct0 + t) + ln;
+        if (nchunks > 0) {
+            lds_barrier();                                   // B_0: chunk 0 has landed
+            for (int c = 0; c < nchunks; ++c) {
+                state_chunk(H, stage[c % kStages], handoff[c & 1], lane, gq);
+                lds_barrier();                               // B_{c+1}
+            }
+        }
+        if (s_final) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    s_final[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col] = H[t][i][e];
+                    s_final[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col] = H[i][e];
         }
+    } else if (nchunks > 0) {
+        // copies for chunks past the last one are issued too (clamped, never
+        // used) so the number of memory operations per chunk never changes
+        state_copy(stage[0], ws, vidx(0), ct, lane);
+        state_copy(stage[1], ws, vidx(1), ct, lane);
+        wait_vmcnt<kCopiesPerChunk>();                       // chunk 0 has landed
+        lds_barrier();                                       // B_0
+        for (int c = 0; c < nchunks; ++c) {
+            // between B_c and B_{c+1}: the compute wave works on chunk c
+            if (c > 0) state_store(handoff[(c - 1) & 1], ws, vidx(c - 1), ct, lane);
+            state_copy(stage[(c + 2) % kStages], ws, vidx(c + 2), ct, lane);
+            // chunk c + 1 landed: after its copies came this chunk's stores
+            // (none for c = 0) and the copies of chunk c + 2
+            if (c > 0) wait_vmcnt<kStoresPerChunk + kCopiesPerChunk>();
+            else wait_vmcnt<kCopiesPerChunk>();
+            lds_barrier();                                   // B_{c+1}
+        }
+        state_store(handoff[(nchunks - 1) & 1], ws, vidx(nchunks - 1), ct, lane);
+        // drain the copies past the end before the workgroup's LDS goes away
+        __builtin_amdgcn_s_waitcnt(0);
     }
 }
-
-#ifndef GDN_STATE_WAVES
-#define GDN_STATE_WAVES 1
-#endif
-#ifndef GDN_STATE_TILES
-#define GDN_STATE_TILES 1
-#endif
-constexpr int kStateWaves = GDN_STATE_WAVES;
-constexpr int kStateTiles = GDN_STATE_TILES;
 
 // ---------------------------------------------------------------------------
 // Stage 3: output.  One workgroup per (chunk slot, value head).
@@ -731,9 +692,8 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
     }
     if ((stage_mask & 2) && n_seqs > 0) {
         const int units = n_seqs * h_v;
-        hipLaunchKernelGGL((gdn_chunk_state<kStateWaves, kStateTiles>),
-                           dim3(8 * ((units + 7) / 8) * (8 / (kStateWaves * kStateTiles))),
-                           dim3(64 * kStateWaves), 0, stream, cu, n_seqs, h_qk, h_v, s0, s_final, ws);
+        hipLaunchKernelGGL(gdn_chunk_state, dim3(64 * ((units + 7) / 8)), dim3(128), 0, stream,
+                           cu, n_seqs, h_v, s0, s_final, ws);
     }
     if ((stage_mask & 4) && total_tokens > 0) {
         hipLaunchKernelGGL(gdn_chunk_out, dim3(n_slots, h_v), dim3(256), 0, stream,
