@@ -32,16 +32,21 @@ namespace {
 constexpr int kTS = 72;   // LDS row stride (halves or floats) of 64-wide tiles
 constexpr int kQS = 136;  // LDS row stride (halves) of 128-wide tiles
 
-// Transposed [dim][pos] fp16 tiles (row stride kTS) are written one position
-// per lane, four dims 8 apart at a time.  Flipping position bits 4-5 by the
-// dim's 8-block spreads those four rows over different banks, and keeps every
-// 8-aligned run of positions contiguous for 16-byte fragment reads.
+// Transposed [dim][pos] fp16 tiles, 64 positions per row, no padding.  Rows
+// are written one position per lane, four dims 8 apart at a time, and read as
+// 16-byte runs of 8 positions, 16 consecutive dims at a time.  XOR-ing the
+// position's 8-block index (bits 3-5) with (d & 7) ^ 2 ((d >> 3) & 3) keeps
+// every 8-aligned run contiguous, puts the four written rows on different
+// banks and gives eight consecutive read rows eight different 8-blocks.
 __device__ __forceinline__ int tsw(int d, int t) {
-    return d * kTS + (t ^ (((d >> 3) & 3) << 4));
+    return d * kChunk + (t ^ ((((d & 7) ^ (((d >> 3) & 3) << 1)) & 7) << 3));
 }
 
 // ---------------------------------------------------------------------------
-// Stage 1: intra-chunk preparation.  One workgroup per (chunk slot, value head).
+// Stage 1: intra-chunk preparation.  One workgroup per (chunk slot, value
+// head); 51 KB of LDS so that three workgroups share a CU.  The UT transform
+// runs in place in the A buffer: A, then Tm = (I + A)^{-1}, then the fp16
+// rows of Tm diag(beta e^G) and Tm diag(beta).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gdn_chunk_prep(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -54,35 +59,35 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     if (!resolve_slot(cu, n_seqs, slot, seq, t0, len)) return;
     const int j = h / (h_v / h_qk);
 
-    __shared__ __attribute__((aligned(16))) f16 KsT[kDim * kTS];   // K^T [dim][pos]
-    __shared__ __attribute__((aligned(16))) f16 VsT[kDim * kTS];   // V^T [dim][pos]
-    __shared__ __attribute__((aligned(16))) float Ab[kChunk * kTS]; // A fp32, then TW | TU fp16
-    __shared__ __attribute__((aligned(16))) float Tb[kChunk * kTS]; // Tm = (I + A)^{-1} fp32
-    __shared__ float Gs[kChunk];
-    __shared__ float Bs[kChunk];
-    __shared__ float Bw[kChunk];                                     // beta e^G
-    __shared__ float Ds[kChunk];                                     // e^{G_C - G}
+    __shared__ __attribute__((aligned(16))) f16 KsT[kDim * kChunk];  // K^T [dim][pos], swizzled
+    __shared__ __attribute__((aligned(16))) f16 VsT[kDim * kChunk];  // V^T [dim][pos], swizzled
+    __shared__ __attribute__((aligned(16))) float Ab[kChunk * kTS];  // A, then Tm, then TW | TU
+    __shared__ float Bs[kChunk];     // beta
+    __shared__ float Bw[kChunk];     // beta e^G
+    __shared__ float Ds[kChunk];     // e^{G_C - G}
+    __shared__ float Gs[kChunk];     // G
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int gq = lane >> 4;
     const int ln = lane & 15;
+    const size_t wsidx = ws.vunit(slot, h);
 
     // ---- K as fragments (row 16 jt + ln, dims 32 kk + 8 gq .. +7) for all four
-    //      row tiles (the Gram needs them), V for this wave's row tile; pad
-    //      rows are zero.  Each wave writes its own row tile transposed into
-    //      KsT / VsT (swizzled, see tsw).
+    //      row tiles (the Gram needs them); V for this wave's row tile.  Each
+    //      wave writes its own row tile of K and V transposed into LDS.  Pad
+    //      rows are zero.
     f16x8 kf[4][4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int r = 16 * jt + ln;
-            u16x8 b = {0, 0, 0, 0, 0, 0, 0, 0};
+            u16x8 bkv = {0, 0, 0, 0, 0, 0, 0, 0};
             if (r < len)
-                b = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + r) * h_qk + j) * kDim + 32 * kk + 8 * gq);
-            kf[jt][kk] = bf16x8_to_f16x8(b);
+                bkv = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + r) * h_qk + j) * kDim + 32 * kk + 8 * gq);
+            kf[jt][kk] = bf16x8_to_f16x8(bkv);
         }
     {
         const int r = 16 * wave + ln;
@@ -104,18 +109,11 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
             }
         }
     }
-    if (tid < kChunk) {
-        const bool in = tid < len;
-        Gs[tid] = in ? g[(size_t)(t0 + tid) * h_v + h] : 0.f;
-        Bs[tid] = in ? beta[(size_t)(t0 + tid) * h_v + h] : 0.f;
-    }
-    __syncthreads();
-
-    const size_t wsidx = ws.vunit(slot, h);
-
-    // ---- decay cumsum within the chunk (wave 0, one lane per position)
+    // ---- decay cumsum (wave 0, one lane per position) and the decay vectors
     if (wave == 0) {
-        float x = Gs[lane];
+        const bool in = lane < len;
+        float x = in ? g[(size_t)(t0 + lane) * h_v + h] : 0.f;
+        const float bt = in ? beta[(size_t)(t0 + lane) * h_v + h] : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(x, off, 64);
@@ -123,9 +121,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
         }
         const float gc = __shfl(x, kChunk - 1, 64);
         const float eg = exp_f(x);
-        Gs[lane] = x;
-        Bw[lane] = Bs[lane] * eg;
         const float dc = exp_f(gc - x);
+        Gs[lane] = x;
+        Bs[lane] = bt;
+        Bw[lane] = bt * eg;
         Ds[lane] = dc;
         float* gdst = ws.gcum + wsidx * kGElems;
         gdst[lane] = dc;
@@ -156,7 +155,8 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
         }
     }
 
-    // ---- A = strictly lower (beta_r e^{G_r-G_s} K K^T); wave w owns row tile w.
+    // ---- A = strictly lower (beta_r e^{G_r-G_s} K K^T); wave w owns row tile w
+    //      (tiles above the diagonal are never written or read as A)
     {
         const int p = wave;
 #pragma unroll
@@ -180,14 +180,9 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     }
     __syncthreads();
 
-    // ---- Tm = (I + A)^{-1}, blocked by 16 (A strictly lower triangular).
+    // ---- Tm = (I + A)^{-1}, blocked by 16, in place.
     //  (1) Diagonal blocks Tm_ii = (I + A_ii)^{-1}: wave i, lane c % 16 holds
     //      column c; x_r = delta_rc - sum_{t<r} A_rt x_t (x_t = 0 for t < c).
-    //  (2) Below the diagonal, block column j on wave j, rows i = j+1..3:
-    //      Tm_ij = -Tm_ii sum_{k=j}^{i-1} A_ik Tm_kj, with 16x16x16 products on
-    //      the matrix cores (split fp16 operands, ~fp32 accuracy).  A product's
-    //      accumulator is already the B operand of the next one, so the column
-    //      chain never leaves registers.
     {
         const int ib = wave;
         float x[16];
@@ -199,23 +194,45 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
             for (int t = 0; t < r; ++t) acc -= arow[t] * x[t];
             x[r] = acc;
         }
+        // this wave's reads of its block are done before these writes
         if (gq == 0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Tb[(16 * ib + r) * kTS + 16 * ib + ln] = x[r];
+            for (int r = 0; r < 16; ++r) Ab[(16 * ib + r) * kTS + 16 * ib + ln] = x[r];
+        }
+    }
+    __syncthreads();
+    //  (2) Below the diagonal, block column j on wave j, rows i = j+1..3:
+    //      Tm_ij = -Tm_ii sum_{k=j}^{i-1} A_ik Tm_kj, with 16x16x16 products on
+    //      the matrix cores (split fp16 operands, ~fp32 accuracy).  A product's
+    //      accumulator is already the B operand of the next one, so the column
+    //      chain stays in registers.  Every A_ik a wave needs is read before
+    //      any wave overwrites A blocks with Tm blocks.
+    f32x4 tcol[4];     // Tm_{k, jb} in accumulator (= B operand) layout, k >= jb
+    f32x4 aik[4][4];   // A_ik, A-operand layout
+    f32x4 tii[4];      // Tm_ii, A-operand layout
+    const int jb = wave;
+    if (wave < 3) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            tcol[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (kb == jb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tcol[kb][e] = Ab[(16 * kb + 4 * gq + e) * kTS + 16 * kb + ln];
+            }
+        }
+#pragma unroll
+        for (int i2 = 1; i2 < 4; ++i2) {
+            if (i2 <= jb) continue;
+            tii[i2] = *reinterpret_cast<const f32x4*>(Ab + (16 * i2 + ln) * kTS + 16 * i2 + 4 * gq);
+#pragma unroll
+            for (int kb = 0; kb < i2; ++kb) {
+                if (kb < jb) continue;
+                aik[i2][kb] = *reinterpret_cast<const f32x4*>(Ab + (16 * i2 + ln) * kTS + 16 * kb + 4 * gq);
+            }
         }
     }
     __syncthreads();
     if (wave < 3) {
-        const int jb = wave;
-        f32x4 tcol[4];     // Tm_{k, jb} in accumulator (= B operand) layout, k >= jb
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) tcol[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-            if (kb == jb) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tcol[kb][e] = Tb[(16 * kb + 4 * gq + e) * kTS + 16 * kb + ln];
-            }
 #pragma unroll
         for (int i2 = 1; i2 < 4; ++i2) {
             if (i2 <= jb) continue;
@@ -223,29 +240,36 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 #pragma unroll
             for (int kb = 0; kb < i2; ++kb) {
                 if (kb < jb) continue;
-                const f32x4 aik = *reinterpret_cast<const f32x4*>(Ab + (16 * i2 + ln) * kTS + 16 * kb + 4 * gq);
-                xs = mfma_split16(aik, tcol[kb], xs);
+                xs = mfma_split16(aik[i2][kb], tcol[kb], xs);
             }
-            const f32x4 tii = *reinterpret_cast<const f32x4*>(Tb + (16 * i2 + ln) * kTS + 16 * i2 + 4 * gq);
-            const f32x4 y = mfma_split16(tii, xs, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 y = mfma_split16(tii[i2], xs, f32x4{0.f, 0.f, 0.f, 0.f});
             tcol[i2] = -y;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Tb[(16 * i2 + 4 * gq + e) * kTS + 16 * jb + ln] = -y[e];
+            for (int e = 0; e < 4; ++e) Ab[(16 * i2 + 4 * gq + e) * kTS + 16 * jb + ln] = -y[e];
         }
     }
     __syncthreads();
 
-    // ---- TW = Tm diag(beta e^G), TU = Tm diag(beta) in fp16 over the dead A
-    //      buffer; blocks above the diagonal are zero.
+    // ---- TW = Tm diag(beta e^G), TU = Tm diag(beta) as fp16, in place; blocks
+    //      above the diagonal are zero.
     f16* TWs = reinterpret_cast<f16*>(Ab);          // [pos][t]
     f16* TUs = TWs + kChunk * kTS;                  // [pos][t]
+    {
+        float tv[16];
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const int idx = tid + 256 * it;
-        const int r = idx >> 6, t = idx & 63;
-        const float tm = ((t >> 4) > (r >> 4)) ? 0.f : Tb[r * kTS + t];
-        TWs[r * kTS + t] = static_cast<f16>(tm * Bw[t]);
-        TUs[r * kTS + t] = static_cast<f16>(tm * Bs[t]);
+        for (int it = 0; it < 16; ++it) {
+            const int idx = tid + 256 * it;
+            const int r = idx >> 6, t = idx & 63;
+            tv[it] = ((t >> 4) > (r >> 4)) ? 0.f : Ab[r * kTS + t];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int idx = tid + 256 * it;
+            const int r = idx >> 6, t = idx & 63;
+            TWs[r * kTS + t] = static_cast<f16>(tv[it] * Bw[t]);
+            TUs[r * kTS + t] = static_cast<f16>(tv[it] * Bs[t]);
+        }
     }
     __syncthreads();
 
