@@ -74,20 +74,20 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     const int ln = lane & 15;
     const size_t wsidx = ws.vunit(slot, h);
 
-    // ---- K as fragments (row 16 jt + ln, dims 32 kk + 8 gq .. +7) for all four
-    //      row tiles (the Gram needs them); V for this wave's row tile.  Each
-    //      wave writes its own row tile of K and V transposed into LDS.  Pad
-    //      rows are zero.
-    f16x8 kf[4][4];
+    // ---- K as raw bf16 fragments (row 16 jt + ln, dims 32 kk + 8 gq .. +7) for
+    //      row tiles 0 .. w (wave w's Gram rows need them); V for this wave's row
+    //      tile.  Each wave writes its own row tile of K and V transposed into
+    //      LDS as fp16.  Pad rows are zero.
+    bf16x8 kf[4][4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int r = 16 * jt + ln;
             u16x8 bkv = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (r < len)
+            if (jt <= wave && r < len)
                 bkv = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + r) * h_qk + j) * kDim + 32 * kk + 8 * gq);
-            kf[jt][kk] = bf16x8_to_f16x8(bkv);
+            kf[jt][kk] = __builtin_bit_cast(bf16x8, bkv);
         }
     {
         const int r = 16 * wave + ln;
@@ -165,10 +165,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                f16x8 a = kf[0][kk];
+                bf16x8 a = kf[0][kk];
 #pragma unroll
                 for (int q2 = 1; q2 < 4; ++q2) if (q2 == p) a = kf[q2][kk];
-                acc = mfma_f16(a, kf[jt][kk], acc);
+                acc = mfma_bf16(a, kf[jt][kk], acc);   // exact bf16 inputs
             }
             const int s = 16 * jt + ln;
 #pragma unroll

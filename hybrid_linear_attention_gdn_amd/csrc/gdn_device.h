@@ -33,6 +33,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Per (chunk slot, value head) element counts of the workspace regions.
 constexpr size_t kWElems = 16 * 64 * 8;    // -W, A-operand fragments [p][qq][lane][8]
@@ -72,6 +73,11 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16x8(u16x8 b) {
 
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Same tile on raw bfloat16 operands (used where both operands are inputs).
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // 16x16x16 product of fp32 operands in fragment form (A: lane l holds row l%16,
