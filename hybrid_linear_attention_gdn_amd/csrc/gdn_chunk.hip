@@ -62,30 +62,32 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     __shared__ __attribute__((aligned(16))) f16 KsT[kDim * kChunk];  // K^T [dim][pos], swizzled
     __shared__ __attribute__((aligned(16))) f16 VsT[kDim * kChunk];  // V^T [dim][pos], swizzled
     __shared__ __attribute__((aligned(16))) float Ab[kChunk * kTS];  // A, then Tm, then TW | TU
-    __shared__ float Bs[kChunk];     // beta
-    __shared__ float Bw[kChunk];     // beta e^G
+    __shared__ __attribute__((aligned(16))) float Bs[kChunk];  // beta
+    __shared__ __attribute__((aligned(16))) float Bw[kChunk];  // beta e^G
     __shared__ float Ds[kChunk];     // e^{G_C - G}
     __shared__ float Gs[kChunk];     // G
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int gq = lane >> 4;
     const int ln = lane & 15;
     const size_t wsidx = ws.vunit(slot, h);
 
-    // ---- K as raw bf16 fragments (row 16 jt + ln, dims 32 kk + 8 gq .. +7) for
-    //      row tiles 0 .. w (wave w's Gram rows need them); V for this wave's row
-    //      tile.  Each wave writes its own row tile of K and V transposed into
-    //      LDS as fp16.  Pad rows are zero.
-    bf16x8 kf[4][4];
+    // ---- K as raw bf16 fragments (row 16 jt + ln, dims 32 kk + 8 gq .. +7):
+    //      kown = this wave's row tile, kf[jt] = row tiles jt < wave (the Gram
+    //      rows of wave w need tiles 0 .. w).  V for this wave's row tile.  Each
+    //      wave writes its own row tile of K and V transposed into LDS as fp16.
+    //      Pad rows are zero.
+    bf16x8 kf[3][4];
+    bf16x8 kown[4];
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
+    for (int jt = 0; jt < 3; ++jt)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int r = 16 * jt + ln;
             u16x8 bkv = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (jt <= wave && r < len)
+            if (jt < wave && r < len)
                 bkv = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + r) * h_qk + j) * kDim + 32 * kk + 8 * gq);
             kf[jt][kk] = __builtin_bit_cast(bf16x8, bkv);
         }
@@ -99,6 +101,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
                 kb = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + r) * h_qk + j) * kDim + 32 * kk + 8 * gq);
                 vb = *reinterpret_cast<const u16x8*>(v + ((size_t)(t0 + r) * h_v + h) * kDim + 32 * kk + 8 * gq);
             }
+            kown[kk] = __builtin_bit_cast(bf16x8, kb);
             const f16x8 kt8 = bf16x8_to_f16x8(kb);
             const f16x8 vt8 = bf16x8_to_f16x8(vb);
 #pragma unroll
@@ -162,13 +165,13 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             if (jt > p) continue;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};   // exact bf16 inputs
+            if (jt == p) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                bf16x8 a = kf[0][kk];
+                for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(kown[kk], kown[kk], acc);
+            } else {
 #pragma unroll
-                for (int q2 = 1; q2 < 4; ++q2) if (q2 == p) a = kf[q2][kk];
-                acc = mfma_bf16(a, kf[jt][kk], acc);   // exact bf16 inputs
+                for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(kown[kk], kf[jt < 3 ? jt : 0][kk], acc);
             }
             const int s = 16 * jt + ln;
 #pragma unroll
@@ -207,18 +210,18 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     //      accumulator is already the B operand of the next one, so the column
     //      chain stays in registers.  Every A_ik a wave needs is read before
     //      any wave overwrites A blocks with Tm blocks.
-    f32x4 tcol[4];     // Tm_{k, jb} in accumulator (= B operand) layout, k >= jb
+    Split16 tcol[4];   // Tm_{k, jb} in accumulator (= B operand) layout, k >= jb
     f32x4 aik[4][4];   // A_ik, A-operand layout
     f32x4 tii[4];      // Tm_ii, A-operand layout
     const int jb = wave;
     if (wave < 3) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            tcol[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (kb == jb) {
+        for (int kb = 0; kb < 3; ++kb) {
+            if (kb != jb) continue;
+            f32x4 t;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) tcol[kb][e] = Ab[(16 * kb + 4 * gq + e) * kTS + 16 * kb + ln];
-            }
+            for (int e = 0; e < 4; ++e) t[e] = Ab[(16 * kb + 4 * gq + e) * kTS + 16 * kb + ln];
+            tcol[kb] = split16(t);
         }
 #pragma unroll
         for (int i2 = 1; i2 < 4; ++i2) {
@@ -240,10 +243,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 #pragma unroll
             for (int kb = 0; kb < i2; ++kb) {
                 if (kb < jb) continue;
-                xs = mfma_split16(aik[i2][kb], tcol[kb], xs);
+                xs = mfma_split16(split16(aik[i2][kb]), tcol[kb], xs);
             }
-            const f32x4 y = mfma_split16(tii[i2], xs, f32x4{0.f, 0.f, 0.f, 0.f});
-            tcol[i2] = -y;
+            const f32x4 y = mfma_split16(split16(tii[i2]), split16(xs), f32x4{0.f, 0.f, 0.f, 0.f});
+            tcol[i2] = split16(-y);
 #pragma unroll
             for (int e = 0; e < 4; ++e) Ab[(16 * i2 + 4 * gq + e) * kTS + 16 * jb + ln] = -y[e];
         }
@@ -255,20 +258,30 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     f16* TWs = reinterpret_cast<f16*>(Ab);          // [pos][t]
     f16* TUs = TWs + kChunk * kTS;                  // [pos][t]
     {
-        float tv[16];
+        // thread: row r = idx / 16, columns t .. t + 3 (one 16-block)
+        f32x4 tv[4];
 #pragma unroll
-        for (int it = 0; it < 16; ++it) {
+        for (int it = 0; it < 4; ++it) {
             const int idx = tid + 256 * it;
-            const int r = idx >> 6, t = idx & 63;
-            tv[it] = ((t >> 4) > (r >> 4)) ? 0.f : Ab[r * kTS + t];
+            const int r = idx >> 4, t = (idx & 15) * 4;
+            tv[it] = ((t >> 4) > (r >> 4)) ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                            : *reinterpret_cast<const f32x4*>(Ab + r * kTS + t);
         }
         __syncthreads();
 #pragma unroll
-        for (int it = 0; it < 16; ++it) {
+        for (int it = 0; it < 4; ++it) {
             const int idx = tid + 256 * it;
-            const int r = idx >> 6, t = idx & 63;
-            TWs[r * kTS + t] = static_cast<f16>(tv[it] * Bw[t]);
-            TUs[r * kTS + t] = static_cast<f16>(tv[it] * Bs[t]);
+            const int r = idx >> 4, t = (idx & 15) * 4;
+            const f32x4 bw = *reinterpret_cast<const f32x4*>(Bw + t);
+            const f32x4 bs = *reinterpret_cast<const f32x4*>(Bs + t);
+            f16x4 tw, tu;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                tw[e] = static_cast<f16>(tv[it][e] * bw[e]);
+                tu[e] = static_cast<f16>(tv[it][e] * bs[e]);
+            }
+            *reinterpret_cast<f16x4*>(TWs + r * kTS + t) = tw;
+            *reinterpret_cast<f16x4*>(TUs + r * kTS + t) = tu;
         }
     }
     __syncthreads();

@@ -80,21 +80,29 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// 16x16x16 product of fp32 operands in fragment form (A: lane l holds row l%16,
-// k = 4 (l/16) + e; B: k = 4 (l/16) + e, column l%16) on fp16 matrix cores,
-// each operand split as hi + lo: hi*hi + hi*lo + lo*hi, error ~2^-22 relative.
-__device__ __forceinline__ f32x4 mfma_split16(f32x4 a, f32x4 b, f32x4 c) {
-    f16x4 ah, al, bh, bl;
+// fp32 value split as hi + lo in fp16 (hi = fp16(x), lo = fp16(x - hi)):
+// 22 significant bits between them for |x| in the fp16 normal range.
+struct Split16 {
+    f16x4 hi, lo;
+};
+
+__device__ __forceinline__ Split16 split16(f32x4 x) {
+    Split16 s;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        ah[e] = static_cast<f16>(a[e]);
-        al[e] = static_cast<f16>(a[e] - static_cast<float>(ah[e]));
-        bh[e] = static_cast<f16>(b[e]);
-        bl[e] = static_cast<f16>(b[e] - static_cast<float>(bh[e]));
+        s.hi[e] = static_cast<f16>(x[e]);
+        s.lo[e] = static_cast<f16>(x[e] - static_cast<float>(s.hi[e]));
     }
-    c = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bh, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bl, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x16f16(al, bh, c, 0, 0, 0);
+    return s;
+}
+
+// 16x16x16 product of split fp32 operands in fragment form (A: lane l holds
+// row l%16, k = 4 (l/16) + e; B: k = 4 (l/16) + e, column l%16) on fp16
+// matrix cores: hi*hi + hi*lo + lo*hi, error ~2^-22 relative.
+__device__ __forceinline__ f32x4 mfma_split16(Split16 a, Split16 b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x16f16(a.hi, b.hi, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16f16(a.hi, b.lo, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16f16(a.lo, b.hi, c, 0, 0, 0);
     return c;
 }
 
