@@ -15,6 +15,8 @@ Printed as one JSON line:
              mean launch time (HIP events on the launch stream), vs MI355X peak
   verify     the speculative-verify leg (8 requests x 6 tokens, per-token state
              snapshots kept) timed the same way, as a fraction of HBM bandwidth
+  verify_fp16_slots  the same verify over an fp16 state pool addressed through
+             a slot table (gdn_recurrent_step_slots)
   cpu_baseline  the CPU oracle (fp32 token recurrence) on host cores
 """
 
@@ -249,6 +251,29 @@ def main():
         "pct_hbm_peak": 100 * v_bytes / t_verify / PEAK_HBM,
     }
 
+    # ---------------- the same verify over an fp16 slot pool (state slots picked by
+    #                  a device-side table, as a serving loop with rollback runs it)
+    pool16 = torch.from_numpy(gi.state_pool(y, R * n_tok, f16=True)).to(dev)
+    table = torch.from_numpy(gi.slot_table_contiguous(R, n_tok, R)).to(dev)
+    cu_tok = torch.from_numpy(y.cu_seqlens).to(dev)
+
+    def sstep():
+        gdn.gdn_recurrent_step_slots(vq, vk, vv, vg, vb, cu_tok, R, n_tok, pool16, table, None, vout)
+
+    for _ in range(args.warmup):
+        sstep()
+    t_slots = time_launches(sstep, args.steps, torch)
+    state_h = H_V * D * D * 2
+    s_bytes = R * state_h + R * n_tok * state_h + R * n_tok * (2 * H_QK * D * 2 + H_V * D * 2 + 2 * H_V * 4 + H_V * D * 4)
+    verify_f16 = {
+        "workload": y.name + "_fp16_slot_pool",
+        "us_per_step": t_slots * 1e6,
+        "tokens_per_s": R * n_tok / t_slots,
+        "algorithmic_bytes": s_bytes,
+        "achieved_GBps": s_bytes / t_slots / 1e9,
+        "pct_hbm_peak": 100 * s_bytes / t_slots / PEAK_HBM,
+    }
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(x, args.cpu_seconds)
@@ -275,6 +300,7 @@ def main():
         "prefill": prefill,
         "roofline": roof,
         "verify": verify,
+        "verify_fp16_slots": verify_f16,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -201,6 +201,34 @@ def no_decay_small_beta(T: int = 4000, seed: int = 0) -> GDNInputs:
     return x
 
 
+def slot_table_contiguous(n_requests: int, max_tokens: int, first_write_slot: int,
+                          read_slots=None) -> np.ndarray:
+    """Slot table [R, max_tokens + 1] (int32): request r reads slot read_slots[r]
+    (default r) and stores the state after token t in slot
+    first_write_slot + r * max_tokens + t."""
+    table = np.empty((n_requests, max_tokens + 1), np.int32)
+    table[:, 0] = np.arange(n_requests) if read_slots is None else read_slots
+    for r in range(n_requests):
+        table[r, 1:] = first_write_slot + r * max_tokens + np.arange(max_tokens)
+    return table
+
+
+def state_pool(x: GDNInputs, extra_slots: int, *, f16: bool = False, seed: int = 0) -> np.ndarray:
+    """Pool [N + extra_slots, H_v, d_k, d_v]: slots 0..N-1 hold x.initial_state,
+    the rest distinct N(0, 0.02^2) fill (so a wrong read shows).  float16 pools
+    hold the fp16 rounding of those values."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 7]))
+    fill = rng.normal(0.0, 0.02, size=(extra_slots,) + x.initial_state.shape[1:]).astype(np.float32)
+    pool = np.concatenate([x.initial_state, fill], axis=0)
+    return pool.astype(np.float16) if f16 else pool
+
+
+def verify_variable(lengths, seed: int = 0) -> GDNInputs:
+    """Verify tokens with a variable count per request (accepted length varies)."""
+    return make_inputs(list(lengths), 16, 32, 128, 128, seed=seed, state_std=0.02,
+                       name="verify_var_" + "_".join(str(int(n)) for n in lengths))
+
+
 WORKLOADS = {
     "tiny": tiny,
     "prefill_4000": prefill_4000,

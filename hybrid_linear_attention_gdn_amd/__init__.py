@@ -9,6 +9,8 @@ current stream.  The names mirror the C entry points:
 * ``gdn_chunk_fwd_stages(..., stage_mask)`` (prep = 1, state = 2, out = 4)
 * ``gdn_recurrent_step(q, k, v, g, beta, n_requests, tokens_per_request, state_in,
   state_out, out, intermediate_states, save_intermediate_states)``
+* ``gdn_recurrent_step_slots(q, k, v, g, beta, cu_tokens, n_requests, max_tokens,
+  state_pool, slot_table, num_accepted, out)`` (pool dtype float32 or float16)
 
 There is no fallback: if ``libgdn.so`` is missing or a call fails, a
 ``GDNError`` is raised.  Build the library with
@@ -31,11 +33,15 @@ GDN_ERR_MISALIGNED = 3
 GDN_ERR_WORKSPACE = 4
 GDN_ERR_LAUNCH = 5
 
+GDN_STATE_F32 = 0
+GDN_STATE_F16 = 1
+
 EXPORTED_SYMBOLS = (
     "gdn_chunk_fwd_workspace_size",
     "gdn_chunk_fwd",
     "gdn_chunk_fwd_stages",
     "gdn_recurrent_step",
+    "gdn_recurrent_step_slots",
     "gdn_status_string",
     "gdn_get_last_error",
 )
@@ -77,6 +83,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_chunk_fwd_stages.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [vp, vp, vp, vp, vp, c32, c32, vp, vp, vp, vp, ctypes.c_int, dims_p, vp]
     lib.gdn_recurrent_step.restype = ctypes.c_int
+    lib.gdn_recurrent_step_slots.argtypes = [vp, vp, vp, vp, vp, vp, c32, c32, vp, c32, c64, vp, vp, vp,
+                                             dims_p, vp]
+    lib.gdn_recurrent_step_slots.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_get_last_error.argtypes = []
@@ -171,3 +180,35 @@ def gdn_recurrent_step(q, k, v, g, beta, n_requests: int, tokens_per_request: in
                                 1 if save_intermediate_states else 0, ctypes.byref(dims),
                                 _stream(stream, q, state_in, out))
     _check(lib, st, "gdn_recurrent_step")
+
+
+def _state_dtype(pool) -> int:
+    import torch
+    if pool.dtype == torch.float32:
+        return GDN_STATE_F32
+    if pool.dtype == torch.float16:
+        return GDN_STATE_F16
+    raise GDNError(GDN_ERR_INVALID_VALUE, f"state pool dtype {pool.dtype} is neither float32 nor float16")
+
+
+def gdn_recurrent_step_slots(q, k, v, g, beta, cu_tokens, n_requests: int, max_tokens: int,
+                             state_pool, slot_table, num_accepted, out, *,
+                             state_dtype: Optional[int] = None, pool_slots: Optional[int] = None,
+                             dims: Optional[gdn_dims] = None, stream=None) -> None:
+    """Per-token update over a pool of state slots (see include/gdn.h).
+
+    ``state_pool`` is a float32 or float16 tensor [pool_slots, H_v, d_k, d_v];
+    ``slot_table`` int32 [R, max_tokens + 1]; ``num_accepted`` int32 [R] or None.
+    """
+    lib = load_library()
+    if dims is None:
+        dims = make_dims(n_requests, q.shape[0], q.shape[1], v.shape[1], q.shape[2], v.shape[2])
+    if state_dtype is None:
+        state_dtype = _state_dtype(state_pool)
+    if pool_slots is None:
+        pool_slots = state_pool.shape[0]
+    st = lib.gdn_recurrent_step_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_tokens),
+                                      int(n_requests), int(max_tokens), _ptr(state_pool), int(state_dtype),
+                                      int(pool_slots), _ptr(slot_table), _ptr(num_accepted), _ptr(out),
+                                      ctypes.byref(dims), _stream(stream, q, state_pool, out))
+    _check(lib, st, "gdn_recurrent_step_slots")

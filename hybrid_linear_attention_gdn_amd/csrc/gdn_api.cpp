@@ -232,4 +232,48 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v,
     return ok();
 }
 
+gdn_status gdn_recurrent_step_slots(const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta,
+                                    const int32_t* cu_tokens,
+                                    int32_t n_requests, int32_t max_tokens,
+                                    void* state_pool, int32_t state_dtype, int64_t pool_slots,
+                                    const int32_t* slot_table,
+                                    const int32_t* num_accepted,
+                                    float* out,
+                                    const gdn_dims* dims,
+                                    void* stream) {
+    gdn_status s = check_dims(dims);
+    if (s != GDN_SUCCESS) return s;
+    if (n_requests < 0 || max_tokens < 0)
+        return fail(GDN_ERR_INVALID_VALUE, "negative n_requests (%d) or max_tokens (%d)", n_requests, max_tokens);
+    if (dims->n_seqs != n_requests)
+        return fail(GDN_ERR_INVALID_VALUE, "dims->n_seqs = %d differs from n_requests = %d",
+                    dims->n_seqs, n_requests);
+    if (state_dtype != GDN_STATE_F32 && state_dtype != GDN_STATE_F16)
+        return fail(GDN_ERR_INVALID_VALUE, "state_dtype = %d is not a gdn_state_dtype", state_dtype);
+    if (pool_slots <= 0) return fail(GDN_ERR_INVALID_VALUE, "pool_slots = %lld must be positive", (long long)pool_slots);
+    if (n_requests == 0) return ok();
+    GDN_REQUIRE_PTR(state_pool);
+    if (!cu_tokens) return fail(GDN_ERR_INVALID_VALUE, "cu_tokens is NULL");
+    if (!slot_table) return fail(GDN_ERR_INVALID_VALUE, "slot_table is NULL");
+    if ((reinterpret_cast<uintptr_t>(cu_tokens) & 3u) || (reinterpret_cast<uintptr_t>(slot_table) & 3u) ||
+        (reinterpret_cast<uintptr_t>(num_accepted) & 3u))
+        return fail(GDN_ERR_MISALIGNED, "int32 index arrays must be 4-byte aligned");
+    if (dims->total_tokens > 0) {
+        GDN_REQUIRE_PTR(q);
+        GDN_REQUIRE_PTR(k);
+        GDN_REQUIRE_PTR(v);
+        GDN_REQUIRE_PTR(g);
+        GDN_REQUIRE_PTR(beta);
+        GDN_REQUIRE_PTR(out);
+    }
+    const hipError_t e = gdn::launch_recurrent_step_slots(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+        g, beta, cu_tokens, n_requests, max_tokens, dims->total_tokens, dims->n_heads_qk, dims->n_heads_v,
+        state_pool, state_dtype == GDN_STATE_F16 ? 1 : 0, pool_slots, slot_table, num_accepted, out,
+        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "gdn_recurrent_step_slots launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

@@ -22,4 +22,12 @@ hipError_t launch_recurrent_step(const uint16_t* q, const uint16_t* k, const uin
                                  int h_qk, int h_v, const float* s_in, float* s_out,
                                  float* out, float* inter, int save, hipStream_t stream);
 
+// Enqueues the per-token update over a pool of state slots (fp32 or fp16).
+hipError_t launch_recurrent_step_slots(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                       const float* g, const float* beta, const int32_t* cu_tokens,
+                                       int n_req, int max_tok, int64_t total_tokens, int h_qk, int h_v,
+                                       void* pool, int state_f16, int64_t pool_slots,
+                                       const int32_t* table, const int32_t* accepted,
+                                       float* out, hipStream_t stream);
+
 }  // namespace gdn

@@ -158,6 +158,61 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v,
                               const gdn_dims* dims,
                               void* stream);
 
+/* Storage type of the recurrent states in a slot pool. */
+typedef enum {
+    GDN_STATE_F32 = 0,
+    GDN_STATE_F16 = 1
+} gdn_state_dtype;
+
+/*
+ * Per-token recurrent update over a pool of state slots: speculative verify
+ * with a variable number of tokens per request, rollback and commit by slot
+ * index, and fp32 or fp16 state storage.
+ *
+ * The "Qwen3.8-27B on one RTX 3090" page keeps a fixed-size state per request
+ * in fp16 (section "Exploiter l'architecture hybride") and eight speculative
+ * state slots per request (section on the 131,072-token limit); the "2080 Ti
+ * runs Qwen3.8-27B: a vLLM plugin" page verifies 1 + K query tokens per
+ * request (section "vLLM on old cards").  The arithmetic is the update of
+ * gdn_recurrent_step, in fp32 registers, whatever the storage type.
+ *
+ *  cu_tokens     int32 [R + 1], device: request r owns token rows
+ *                cu_tokens[r] .. cu_tokens[r+1] - 1 of q, k, v, g, beta and
+ *                out; between 0 and max_tokens rows each.
+ *  state_pool    [pool_slots, H_v, d_k, d_v], float32 or float16
+ *                (state_dtype), d_v contiguous; read and written in place.
+ *  slot_table    int32 [R, max_tokens + 1], device.  Column c > 0 of row r
+ *                names the slot that receives the state right after token
+ *                c - 1 of request r (negative: not stored).  The incoming
+ *                state is read from column num_accepted[r] (column 0 when
+ *                num_accepted is NULL).  So a serving loop that keeps one row
+ *                per request passes the previous call's accepted-token count
+ *                to roll back to the last accepted state with no copy; column
+ *                0 holds the committed state of a fresh request.
+ *  num_accepted  int32 [R], device, or NULL.
+ *  out           float32 [T, H_v, d_v], T = dims->total_tokens.
+ *  dims          n_seqs = R; total_tokens = T rows of the token arrays.
+ *
+ * A request may name its own incoming slot among its write slots (the update
+ * holds the whole state before it stores any snapshot); slots named by two
+ * different requests race.  Device-content checks, done before any access
+ * they guard: a request whose token range is not inside [0, T) or holds more
+ * than max_tokens rows is skipped (nothing written); a request whose incoming
+ * column or slot, or any write slot, is outside the table or pool gets NaN
+ * outputs and no state read or written.  Host-side errors as for
+ * gdn_recurrent_step; state_dtype outside the enum is GDN_ERR_INVALID_VALUE.
+ */
+gdn_status gdn_recurrent_step_slots(const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta,
+                                    const int32_t* cu_tokens,
+                                    int32_t n_requests, int32_t max_tokens,
+                                    void* state_pool, int32_t state_dtype, int64_t pool_slots,
+                                    const int32_t* slot_table,
+                                    const int32_t* num_accepted,
+                                    float* out,
+                                    const gdn_dims* dims,
+                                    void* stream);
+
 /* Static text for a status code. */
 const char* gdn_status_string(gdn_status s);
 

@@ -211,3 +211,43 @@ def test_stages_rejects_bad_mask(lib):
     for mask in (0, 8, -1):
         assert lib.gdn_chunk_fwd_stages(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
                                         ctypes.byref(d), FAKE, need, mask, None) == gdn.GDN_ERR_INVALID_VALUE
+
+
+def slots_call(lib, d, R=2, M=6, dtype=gdn.GDN_STATE_F16, pool_slots=14, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, pool=FAKE, table=FAKE,
+                acc=None, out=FAKE)
+    args.update(over)
+    return lib.gdn_recurrent_step_slots(args["q"], args["k"], args["v"], args["g"], args["beta"],
+                                        args["cu"], R, M, args["pool"], dtype, pool_slots,
+                                        args["table"], args["acc"], args["out"], ctypes.byref(d), None)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "cu", "pool", "table", "out"])
+def test_slots_step_rejects_null(lib, name):
+    assert slots_call(lib, dims(n=2, T=9), **{name: None}) == gdn.GDN_ERR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "pool", "out"])
+def test_slots_step_rejects_misaligned(lib, name):
+    assert slots_call(lib, dims(n=2, T=9), **{name: MIS}) == gdn.GDN_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("name", ["cu", "table", "acc"])
+def test_slots_step_rejects_misaligned_index_arrays(lib, name):
+    assert slots_call(lib, dims(n=2, T=9), **{name: FAKE + 2}) == gdn.GDN_ERR_MISALIGNED
+
+
+def test_slots_step_argument_checks(lib):
+    d = dims(n=2, T=9)
+    assert slots_call(lib, d, dtype=2) == gdn.GDN_ERR_INVALID_VALUE
+    assert slots_call(lib, d, dtype=-1) == gdn.GDN_ERR_INVALID_VALUE
+    assert slots_call(lib, d, pool_slots=0) == gdn.GDN_ERR_INVALID_VALUE
+    assert slots_call(lib, d, R=3) == gdn.GDN_ERR_INVALID_VALUE          # dims->n_seqs differs
+    assert slots_call(lib, d, M=-1) == gdn.GDN_ERR_INVALID_VALUE
+    assert slots_call(lib, dims(n=2, T=9, dk=64, dv=64)) == gdn.GDN_ERR_NOT_SUPPORTED
+    assert b"state_dtype" in (slots_call(lib, d, dtype=5), lib.gdn_get_last_error())[1]
+
+
+def test_slots_step_zero_requests_is_a_noop(lib):
+    assert slots_call(lib, dims(n=0, T=0), R=0, q=None, k=None, v=None, g=None, beta=None, cu=None,
+                      pool=None, table=None, out=None) == gdn.GDN_SUCCESS
