@@ -40,32 +40,29 @@ H_V, H_QK, D, C = 32, 16, 128, 64
 
 
 def algorithmic_work():
-    """Per-token algorithmic flops and bytes of each prefill stage (config dims).
+    """Per-token algorithmic flops and bytes of each prefill kernel (config dims).
 
     Flops count each causal (triangular) product at half and the K K^T / Q K^T
-    Grams once per q/k head.  Bytes count each tensor of a stage's interface
-    read or written once: bf16 inputs, fp32 g / beta / output, fp16
-    intermediates (W, U, K^T diag(e^{G_C-G}) per value head, U', chunk states)
-    and fp32 decay vectors."""
-    prep_f = H_V * (C * (D + D) + C * C / 3) + H_QK * (C * D)
-    state_f = H_V * (4 * D * D)
-    out_f = H_V * (2 * D * D + C * D) + H_QK * (C * D)
+    Grams once per q/k head; they are the layer's terms, each assigned to the
+    kernel that evaluates it: prep takes the decay, Grams, UT transform, W, U
+    and the intra-chunk output term (as P U); the state kernel the recurrence
+    (W H, K^T U') and Q S.  The extra P W product of the Q' = diag(e^G) Q - P W
+    rewrite is not counted.  Bytes count each tensor of a kernel's interface
+    read or written once: bf16 inputs, fp32 g / beta / decay vector / output,
+    fp16 intermediates (-W, U, K^T diag(e^{G_C-G}), Q', Y per value head)."""
+    prep_f = H_V * (C * (D + D) + C * C / 3) + H_QK * (C * D) + H_QK * (C * D) + H_V * (C * D)
+    state_f = H_V * (4 * D * D) + H_V * (2 * D * D)
     qk_b = H_QK * D * 2          # one of q or k, bf16
     v_b = H_V * D * 2
-    gb_b = H_V * 4               # one of g or beta
-    f16_row = H_V * D * 2        # one of W, U, K^T-decayed, U' per token
-    hc_b = H_V * D * D * 2 / C   # fp16 chunk state, per token
+    gb_b = H_V * 4               # one of g, beta or the e^G vector
+    f16_row = H_V * D * 2        # one of -W, U, K^T-decayed, Q', Y per token
     out_b = H_V * D * 4
-    dec_w = 3 * gb_b             # e^{G_C - G}, e^G, G written by prep
-    dec_r = 2 * gb_b             # two of them read by state / out
-    prep_b = qk_b + v_b + 2 * gb_b + 3 * f16_row + dec_w
-    state_b = 3 * f16_row + dec_r + f16_row + hc_b
-    out_b_tot = 2 * qk_b + dec_r + hc_b + f16_row + out_b
+    prep_b = 2 * qk_b + v_b + 2 * gb_b + 5 * f16_row + gb_b
+    state_b = 5 * f16_row + gb_b + out_b
     return {
         "prep": (prep_f, prep_b),
         "state": (state_f, state_b),
-        "out": (out_f, out_b_tot),
-        "layer": (prep_f + state_f + out_f, 2 * qk_b + v_b + 2 * gb_b + out_b),
+        "layer": (prep_f + state_f, 2 * qk_b + v_b + 2 * gb_b + out_b),
     }
 
 
@@ -183,7 +180,7 @@ def main():
     t_step = time_launches(step, args.steps, torch)
 
     stage_t = {}
-    for name, mask in (("prep", 1), ("state", 2), ("out", 4)):
+    for name, mask in (("prep", 1), ("state", 2)):
         stage_t[name] = time_launches(
             lambda m=mask: gdn.gdn_chunk_fwd_stages(q, k, v, g, beta, cu, None, out, fin, ws, m),
             args.steps, torch)
@@ -192,7 +189,7 @@ def main():
 
     work = algorithmic_work()
     state_bytes = H_V * D * D * 4          # one fp32 state per sequence (final state written)
-    per_seq = {"prep": 0, "state": state_bytes, "out": 0, "layer": state_bytes}
+    per_seq = {"prep": 0, "state": state_bytes, "layer": state_bytes}
     dom = max(stage_t, key=stage_t.get)
     f_tok, b_tok = work[dom]
     flops, nbytes = f_tok * T, b_tok * T + per_seq[dom]

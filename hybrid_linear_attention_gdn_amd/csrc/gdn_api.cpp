@@ -64,7 +64,7 @@ int64_t n_chunk_slots(const gdn_dims* d) {
 }
 
 struct Layout {
-    size_t w, u, up, hc, kt, g, total;
+    size_t w, u, kt, qt, y, eg, junk, total;
 };
 
 Layout workspace_layout(const gdn_dims* d) {
@@ -73,10 +73,11 @@ Layout workspace_layout(const gdn_dims* d) {
     size_t off = 0;
     L.w = off;  off += round_up(units * gdn::kWElems * sizeof(gdn::f16));
     L.u = off;  off += round_up(units * gdn::kUElems * sizeof(gdn::f16));
-    L.up = off; off += round_up(units * gdn::kUpElems * sizeof(gdn::f16));
-    L.hc = off; off += round_up(units * gdn::kHcElems * sizeof(gdn::f16));
     L.kt = off; off += round_up(units * gdn::kKtElems * sizeof(gdn::f16));
-    L.g = off;  off += round_up(units * gdn::kGElems * sizeof(float));
+    L.qt = off; off += round_up(units * gdn::kQtElems * sizeof(gdn::f16));
+    L.y = off;  off += round_up(units * gdn::kUElems * sizeof(gdn::f16));
+    L.eg = off; off += round_up(units * gdn::kGElems * sizeof(float));
+    L.junk = off; off += round_up(gdn::kJunkBytes);
     L.total = off;
     return L;
 }
@@ -118,37 +119,30 @@ gdn_status gdn_chunk_fwd_workspace_size(const gdn_dims* dims, size_t* bytes) {
     return ok();
 }
 
-gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
-                         const float* g, const float* beta,
-                         const int32_t* cu_seqlens,
-                         const float* initial_state,
-                         float* out,
-                         float* final_state,
-                         const gdn_dims* dims,
-                         void* workspace, size_t workspace_bytes,
-                         void* stream) {
-    return gdn_chunk_fwd_stages(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
-                                dims, workspace, workspace_bytes, 7, stream);
+gdn_status gdn_chunk_state_slots(const gdn_dims* dims, int64_t* n_slots) {
+    if (!n_slots) return fail(GDN_ERR_INVALID_VALUE, "n_slots is NULL");
+    const gdn_status s = check_dims(dims);
+    if (s != GDN_SUCCESS) return s;
+    *n_slots = n_chunk_slots(dims);
+    return ok();
 }
 
-gdn_status gdn_chunk_fwd_stages(const void* q, const void* k, const void* v,
-                                const float* g, const float* beta,
-                                const int32_t* cu_seqlens,
-                                const float* initial_state,
-                                float* out,
-                                float* final_state,
-                                const gdn_dims* dims,
-                                void* workspace, size_t workspace_bytes,
-                                int stage_mask,
-                                void* stream) {
-    if (stage_mask < 1 || stage_mask > 7)
-        return fail(GDN_ERR_INVALID_VALUE, "stage_mask = %d is outside 1..7", stage_mask);
+namespace {
+
+gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const int32_t* cu_seqlens, const float* initial_state, float* out,
+                          float* final_state, float* chunk_states, const gdn_dims* dims,
+                          void* workspace, size_t workspace_bytes, int stage_mask, void* stream,
+                          const char* what) {
+    if (stage_mask < 1 || stage_mask > 3)
+        return fail(GDN_ERR_INVALID_VALUE, "stage_mask = %d is outside 1..3", stage_mask);
     gdn_status s = check_dims(dims);
     if (s != GDN_SUCCESS) return s;
     if (dims->n_seqs == 0) return ok();   // nothing to do, nothing to write
     GDN_REQUIRE_PTR(cu_seqlens);
     GDN_OPTIONAL_PTR(initial_state);
     GDN_OPTIONAL_PTR(final_state);
+    GDN_OPTIONAL_PTR(chunk_states);
     if (dims->total_tokens > 0) {
         GDN_REQUIRE_PTR(q);
         GDN_REQUIRE_PTR(k);
@@ -170,18 +164,65 @@ gdn_status gdn_chunk_fwd_stages(const void* q, const void* k, const void* v,
     gdn::ChunkWorkspace ws;
     ws.w = reinterpret_cast<gdn::f16*>(base + L.w);
     ws.u = reinterpret_cast<gdn::f16*>(base + L.u);
-    ws.up = reinterpret_cast<gdn::f16*>(base + L.up);
-    ws.hc = reinterpret_cast<gdn::f16*>(base + L.hc);
     ws.kt = reinterpret_cast<gdn::f16*>(base + L.kt);
-    ws.gcum = reinterpret_cast<float*>(base + L.g);
+    ws.qt = reinterpret_cast<gdn::f16*>(base + L.qt);
+    ws.y = reinterpret_cast<gdn::f16*>(base + L.y);
+    ws.eg = reinterpret_cast<float*>(base + L.eg);
+    ws.junk = reinterpret_cast<float*>(base + L.junk);
     ws.n_slots = (int)slots;
 
     const hipError_t e = gdn::launch_chunk_fwd(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
         g, beta, cu_seqlens, dims->n_seqs, dims->total_tokens, dims->n_heads_qk, dims->n_heads_v,
-        initial_state, out, final_state, ws, (int)slots, stage_mask, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "gdn_chunk_fwd launch: %s", hipGetErrorString(e));
+        initial_state, out, final_state, chunk_states, ws, (int)slots, stage_mask,
+        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "%s launch: %s", what, hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
+                         const float* g, const float* beta,
+                         const int32_t* cu_seqlens,
+                         const float* initial_state,
+                         float* out,
+                         float* final_state,
+                         const gdn_dims* dims,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    return chunk_fwd_impl(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, nullptr,
+                          dims, workspace, workspace_bytes, 3, stream, "gdn_chunk_fwd");
+}
+
+gdn_status gdn_chunk_fwd_snapshots(const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta,
+                                   const int32_t* cu_seqlens,
+                                   const float* initial_state,
+                                   float* out,
+                                   float* final_state,
+                                   float* chunk_states,
+                                   const gdn_dims* dims,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    if (dims && dims->n_seqs > 0 && !chunk_states)
+        return fail(GDN_ERR_INVALID_VALUE, "chunk_states is NULL");
+    return chunk_fwd_impl(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, chunk_states,
+                          dims, workspace, workspace_bytes, 3, stream, "gdn_chunk_fwd_snapshots");
+}
+
+gdn_status gdn_chunk_fwd_stages(const void* q, const void* k, const void* v,
+                                const float* g, const float* beta,
+                                const int32_t* cu_seqlens,
+                                const float* initial_state,
+                                float* out,
+                                float* final_state,
+                                const gdn_dims* dims,
+                                void* workspace, size_t workspace_bytes,
+                                int stage_mask,
+                                void* stream) {
+    return chunk_fwd_impl(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, nullptr,
+                          dims, workspace, workspace_bytes, stage_mask, stream, "gdn_chunk_fwd_stages");
 }
 
 gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v,

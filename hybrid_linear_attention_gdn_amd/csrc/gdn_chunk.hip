@@ -49,7 +49,7 @@ __device__ __forceinline__ int tsw(int d, int t) {
 // rows of Tm diag(beta e^G) and Tm diag(beta).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gdn_chunk_prep(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, int n_seqs, int h_qk, int h_v, ChunkWorkspace ws)
 {
@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     __shared__ __attribute__((aligned(16))) float Bw[kChunk];  // beta e^G
     __shared__ float Ds[kChunk];     // e^{G_C - G}
     __shared__ float Gs[kChunk];     // G
+    __shared__ float Es[kChunk];     // e^G
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -129,10 +130,8 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
         Bs[lane] = bt;
         Bw[lane] = bt * eg;
         Ds[lane] = dc;
-        float* gdst = ws.gcum + wsidx * kGElems;
-        gdst[lane] = dc;
-        gdst[64 + lane] = eg;
-        gdst[128 + lane] = x;
+        Es[lane] = eg;
+        ws.eg[wsidx * kGElems + lane] = eg;
     }
     __syncthreads();
 
@@ -182,6 +181,44 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
         }
     }
     __syncthreads();
+
+    // ---- P = M o (Q K^T) for row tile p = wave, M_rs = e^{G_r - G_s} (s <= r),
+    //      computed as (K Q^T)[s][r] so that the accumulators of two position
+    //      tiles stack into the A fragment of P over position slots.  Kept in
+    //      registers until the output-side products at the end.
+    f16x8 pf[2];
+    {
+        const int p = wave;
+        const int r = 16 * p + ln;
+        bf16x8 qf[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            u16x8 b = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (r < len) b = *reinterpret_cast<const u16x8*>(q + ((size_t)(t0 + r) * h_qk + j) * kDim + 32 * kk + 8 * gq);
+            qf[kk] = __builtin_bit_cast(bf16x8, b);
+        }
+        f32x4 dt[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            dt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (jt > p) continue;
+            if (jt == p) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) dt[jt] = mfma_bf16(kown[kk], qf[kk], dt[jt]);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) dt[jt] = mfma_bf16(kf[jt < 3 ? jt : 0][kk], qf[kk], dt[jt]);
+            }
+            const float gr = Gs[r];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int sp = 16 * jt + 4 * gq + e;
+                dt[jt][e] = (sp <= r) ? exp_f(gr - Gs[sp]) * dt[jt][e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) pf[qq] = cat_to_f16(dt[2 * qq], dt[2 * qq + 1]);
+    }
 
     // ---- Tm = (I + A)^{-1}, blocked by 16, in place.
     //  (1) Diagonal blocks Tm_ii = (I + A_ii)^{-1}: wave i, lane c % 16 holds
@@ -286,10 +323,25 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     }
     __syncthreads();
 
-    // ---- W^T = K^T TW^T and U = TU V.  Wave w owns dim/col tiles 2w, 2w+1.
+    // ---- W = TW K (twice: dims on lanes and positions on lanes) and U = TU V.
+    //      Wave w owns d_k tiles 2w, 2w+1 and d_v tiles 2w, 2w+1.
+    // Q~^T = diag(e^G) Q, transposed, for this wave's d_k tiles: accumulator
+    // layout (d_k rows 4 gq + e, query row 16 p + ln).  Loaded now, used last.
+    u16x4 qraw[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int r = 16 * p + ln;
+            qraw[a][p] = u16x4{0, 0, 0, 0};
+            if (r < len)
+                qraw[a][p] = *reinterpret_cast<const u16x4*>(q + ((size_t)(t0 + r) * h_qk + j) * kDim +
+                                                            16 * (2 * wave + a) + 4 * gq);
+        }
+    f32x4 w2acc[4][2];   // W[pos tile p][d_k tile 2w + a]: d_k on lanes
+    f32x4 uacc[4][2];    // U[pos tile p][d_v tile 2w + a]: d_v on lanes
     {
-        f32x4 wacc[2][4];
-        f32x4 uacc[4][2];
+        f32x4 wacc[2][4];   // W^T[d_k tile 2w + a][pos tile p]: positions on lanes
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -313,67 +365,143 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
                 const f16x8 tu = *reinterpret_cast<const f16x8*>(TUs + row * kTS + 32 * kt + 8 * gq);
 #pragma unroll
                 for (int a = 0; a < 2; ++a) {
-                    wacc[a][p] = mfma_f16(kfr[a], tw, wacc[a][p]);   // W^T[dim][pos]
-                    uacc[p][a] = mfma_f16(tu, vfr[a], uacc[p][a]);   // U[pos][col]
+                    wacc[a][p] = mfma_f16(kfr[a], tw, wacc[a][p]);
+                    uacc[p][a] = mfma_f16(tu, vfr[a], uacc[p][a]);
                 }
             }
         }
-        // -W fragments (p, qq = wave): stacked dim tiles 2w, 2w+1 of W^T
+        // -W fragments (p, qq = wave): stacked d_k tiles 2w, 2w+1 of W^T
         f16* wdst = ws.w + wsidx * kWElems;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const f16x8 fr = cat_to_f16(-wacc[0][p], -wacc[1][p]);
             *reinterpret_cast<f16x8*>(wdst + ((p * 4 + wave) * 64 + lane) * 8) = fr;
         }
-        // U accumulator fragments (ct, p)
-        f16* udst = ws.u + wsidx * kUElems;
+    }
+    // the same W with d_k on lanes, for P W below (a second pass keeps the
+    // register peak down)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) w2acc[p][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        f16x8 kfr[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+            kfr[a] = *reinterpret_cast<const f16x8*>(KsT + tsw(16 * (2 * wave + a) + ln, 32 * kt + 8 * gq));
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const f16x8 tw = *reinterpret_cast<const f16x8*>(TWs + (16 * p + ln) * kTS + 32 * kt + 8 * gq);
+#pragma unroll
+            for (int a = 0; a < 2; ++a) w2acc[p][a] = mfma_f16(tw, kfr[a], w2acc[p][a]);
+        }
+    }
+    // U accumulator fragments (ct, p)
+    f16* udst = ws.u + wsidx * kUElems;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int ct = 2 * wave + a;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            f16x4 fr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) fr[e] = static_cast<f16>(uacc[p][a][e]);
+            *reinterpret_cast<f16x4*>(udst + ((ct * 4 + p) * 64 + lane) * 4) = fr;
+        }
+    }
+
+    // ---- exchange P: every wave needs all four row tiles
+    __syncthreads();                                  // K, V, TW, TU are consumed
+    f16* Pl = KsT;                                    // [p][qq][lane][8]
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+        *reinterpret_cast<f16x8*>(Pl + ((wave * 2 + qq) * 64 + lane) * 8) = pf[qq];
+    __syncthreads();
+    f16x8 pa[4][2];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) pa[p][qq] = *reinterpret_cast<const f16x8*>(Pl + ((p * 2 + qq) * 64 + lane) * 8);
+
+    // ---- Q' = diag(e^G) Q - P W as A fragments over the chunk state's d_k
+    //      slots: (Q')^T = Q~^T + (-W)^T P^T, d_k tiles 2w, 2w+1 = K-step w.
+    {
+        f16x8 wn[2][2];   // -W with d_k on lanes, positions on slots [a][pos step]
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) wn[a][qq] = cat_to_f16(-w2acc[2 * qq][a], -w2acc[2 * qq + 1][a]);
+        f16* qdst = ws.qt + wsidx * kQtElems;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const float er = Es[16 * p + ln];
+            f32x4 acc[2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[a][e] = bf16_to_f32(qraw[a][p][e]) * er;
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq) acc[a] = mfma_f16(wn[a][qq], pa[p][qq], acc[a]);
+            }
+            *reinterpret_cast<f16x8*>(qdst + ((p * 4 + wave) * 64 + lane) * 8) = cat_to_f16(acc[0], acc[1]);
+        }
+    }
+    // ---- Y = P U in the output tile's accumulator layout (ct, p)
+    {
+        f16x8 ub[2][2];   // U with d_v on lanes, positions on slots [a][pos step]
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) ub[a][qq] = cat_to_f16(uacc[2 * qq][a], uacc[2 * qq + 1][a]);
+        f16* ydst = ws.y + wsidx * kUElems;
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
             const int ct = 2 * wave + a;
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq) acc = mfma_f16(pa[p][qq], ub[a][qq], acc);
                 f16x4 fr;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) fr[e] = static_cast<f16>(uacc[p][a][e]);
-                *reinterpret_cast<f16x4*>(udst + ((ct * 4 + p) * 64 + lane) * 4) = fr;
+                for (int e = 0; e < 4; ++e) fr[e] = static_cast<f16>(acc[e]);
+                *reinterpret_cast<f16x4*>(ydst + ((ct * 4 + p) * 64 + lane) * 4) = fr;
             }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2: inter-chunk state recurrence.  One workgroup of two waves per
-// (sequence, value head, 16-column tile), specialised:
+// Stage 2: inter-chunk state recurrence with the output.  One workgroup of
+// two waves per (sequence, value head, 16-column tile), specialised:
 //   * the compute wave keeps the tile's 128 x 16 slice of the state in
-//     accumulator registers (8 tiles of 16 d_k rows) for the whole sequence
-//     and per chunk only reads operand fragments from LDS, runs the 32
-//     matrix-core products and hands the chunk's results (its incoming state
-//     and U', for the output stage) to LDS;
-//   * the copy wave moves operands in and results out: per chunk it issues
-//     direct global-to-LDS copies of -W fragments (16 KB), decayed K^T
-//     fragments (16 KB), the tile's U fragments (2 KB) and the decay vectors
-//     into a ring of three stages, two chunks ahead, and stores the previous
-//     chunk's hand-off to global memory.
+//     accumulator registers (8 tiles of 16 d_k rows) for the whole sequence.
+//     Per chunk it reads operand fragments from LDS and runs 48 matrix-core
+//     products: U' = U - W H0 and H_C = e^{G_C} H0 + K^T D U' (the chain
+//     from chunk to chunk), and the tile's output O = Y + Q' H0, which needs
+//     only the incoming state (Q' = diag(e^G) Q - P W and Y = P U come from
+//     the prep stage).  It stores O (and, when asked for, the state after the
+//     chunk) straight to global memory and never waits on memory itself;
+//   * the copy wave issues direct global-to-LDS copies of -W, K^T, Q', the
+//     tile's U and Y and the decay vector into a ring of three stages, two
+//     chunks ahead.
 // The waves meet at one barrier per chunk.  The copy wave issues a fixed
-// number of memory operations per chunk, so one memory-counter wait on its
-// copies makes a stage ready before that barrier.  The eight tiles of a head
-// run on one XCD so that its L2 serves the shared fragments.
+// number of copies per chunk, so one memory-counter wait makes a stage ready
+// before that barrier.  The eight tiles of a head run on one XCD so that its
+// L2 serves the shared fragments.
 // ---------------------------------------------------------------------------
 constexpr int kStages = 3;
-constexpr int kUTile = 4 * 64 * 4;                           // halves of U fragments per tile
-constexpr int kCopiesPerChunk = 16 + 16 + 2 + 2;             // -W, K^T, U, decay vectors
-constexpr int kStoresPerChunk = 4 + 2;                        // chunk state, U'
+constexpr int kUTile = 4 * 64 * 4;                           // halves of U (or Y) fragments per tile
+constexpr int kCopiesPerChunk = 16 + 16 + 16 + 2 + 2 + 1;    // -W, K^T, Q', U, Y, e^G
 
 struct StateStage {
     f16 w[kWElems];
     f16 k[kKtElems];
+    f16 q[kQtElems];
     f16 u[kUTile];
-    float g[2 * kChunk];      // e^{G_C - G_r}, then e^{G_r}
-};
-
-struct StateHandoff {
-    f16 hb[4][64 * 8];        // incoming chunk state, B fragments over d_k
-    f16 up[2][64 * 8];        // U', B fragments over positions
+    f16 y[kUTile];
+    float eg[kChunk];         // e^{G_r}; the last entry is e^{G_C}
 };
 
 // s_waitcnt with vmcnt = N and the other counters left alone (gfx9 encoding).
@@ -393,102 +521,116 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// One chunk's copies: 1 KB pieces (16 B per lane) of -W, K^T and U, and the
-// two 256 B decay vectors (4 B per lane).
+// One chunk's copies: 1 KB pieces (16 B per lane) of -W, K^T, Q', U and Y,
+// and the 256 B decay vector (4 B per lane).
 __device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace& ws, size_t vu, int ct, int lane) {
     const f16* wsrc = ws.w + vu * kWElems;
     const f16* ksrc = ws.kt + vu * kKtElems;
+    const f16* qsrc = ws.qt + vu * kQtElems;
     const f16* usrc = ws.u + vu * kUElems + (size_t)ct * kUTile;
-    const float* gsrc = ws.gcum + vu * kGElems;
+    const f16* ysrc = ws.y + vu * kUElems + (size_t)ct * kUTile;
+    const float* gsrc = ws.eg + vu * kGElems;
 #pragma unroll
     for (int piece = 0; piece < 16; ++piece) {
         __builtin_amdgcn_global_load_lds(wsrc + (piece * 64 + lane) * 8, st.w + piece * 512, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(ksrc + (piece * 64 + lane) * 8, st.k + piece * 512, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(qsrc + (piece * 64 + lane) * 8, st.q + piece * 512, 16, 0, 0);
     }
 #pragma unroll
-    for (int piece = 0; piece < 2; ++piece)
+    for (int piece = 0; piece < 2; ++piece) {
         __builtin_amdgcn_global_load_lds(usrc + (piece * 64 + lane) * 8, st.u + piece * 512, 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds(gsrc + i * 64 + lane, st.g + i * 64, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(ysrc + (piece * 64 + lane) * 8, st.y + piece * 512, 16, 0, 0);
+    }
+    // (the casts keep this 4-byte copy from tripping a code-generation fault
+    //  of the ROCm 7.2 compiler in this kernel)
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gsrc + lane), reinterpret_cast<void*>(st.eg),
+                                     4, 0, 0);
 }
 
-// Store one chunk's hand-off (read back from LDS) to the workspace.
-__device__ __forceinline__ void state_store(const StateHandoff& ho, const ChunkWorkspace& ws, size_t vu,
-                                            int ct, int lane) {
-    f16* hdst = ws.hc + vu * kHcElems;
-    f16* udst = ws.up + vu * kUpElems;
-    f16x8 hb[4], up[2];
+// One chunk for the compute wave's 16 columns: the recurrence step and the
+// output rows t0 .. t0 + len - 1 of the tile.  out_tile and snap point at
+// column 0 of the tile (row 0 of the chunk).  Rows past len go to the sink so
+// that the number of stores never changes.
+template <bool kSnap>
+__device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st, float* out_tile,
+                                            size_t row_stride, int len, float* snap, float* junk,
+                                            int lane, int gq, int ln) {
+    // incoming chunk state as B fragments (d_k slots)
+    f16x8 hb[4];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) hb[qq] = *reinterpret_cast<const f16x8*>(&ho.hb[qq][lane * 8]);
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) up[qq] = *reinterpret_cast<const f16x8*>(&ho.up[qq][lane * 8]);
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq)
-        *reinterpret_cast<f16x8*>(hdst + ((ct * 4 + qq) * 64 + lane) * 8) = hb[qq];
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
-        *reinterpret_cast<f16x8*>(udst + ((ct * 2 + qq) * 64 + lane) * 8) = up[qq];
-}
-
-// One chunk of the recurrence for the compute wave's 16 columns.
-__device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st, StateHandoff& ho,
-                                            int lane, int gq) {
-    // U accumulator fragments of this column tile
-    f32x4 acc[4];
+    for (int qq = 0; qq < 4; ++qq) hb[qq] = cat_to_f16(H[2 * qq], H[2 * qq + 1]);
+    // U' = U + (-W) H0 and O = Y + Q' H0: all 32 fragments are read before
+    // the burst, whose 8 accumulator chains interleave
+    f32x4 acc[4], oacc[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const f16x4 uf = *reinterpret_cast<const f16x4*>(&st.u[(p * 64 + lane) * 4]);
+        const f16x4 yf = *reinterpret_cast<const f16x4*>(&st.y[(p * 64 + lane) * 4]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[p][e] = static_cast<float>(uf[e]);
+        for (int e = 0; e < 4; ++e) {
+            acc[p][e] = static_cast<float>(uf[e]);
+            oacc[p][e] = static_cast<float>(yf[e]);
+        }
     }
-    // incoming chunk state as B fragments (d_k slots), handed to the output stage
-    f16x8 hb[4];
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-        hb[qq] = cat_to_f16(H[2 * qq], H[2 * qq + 1]);
-        *reinterpret_cast<f16x8*>(&ho.hb[qq][lane * 8]) = hb[qq];
-    }
-    // U' = U + (-W) H; all sixteen -W fragments are read before the burst
-    f16x8 wa[4][4];
+    f16x8 wa[4][4], qa[4][4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
+        for (int p = 0; p < 4; ++p) {
             wa[qq][p] = *reinterpret_cast<const f16x8*>(&st.w[((p * 4 + qq) * 64 + lane) * 8]);
+            qa[qq][p] = *reinterpret_cast<const f16x8*>(&st.q[((p * 4 + qq) * 64 + lane) * 8]);
+        }
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) acc[p] = mfma_f16(wa[qq][p], hb[qq], acc[p]);
-    // U' as B fragments (position slots): handed to the output stage, and the
-    // B operand of the update, whose A operand K^T diag(e^{G_C - G}) carries
-    // the decay:  H <- e^{G_C} H + (K^T diag(e^{G_C - G})) U'
+        for (int p = 0; p < 4; ++p) {
+            acc[p] = mfma_f16(wa[qq][p], hb[qq], acc[p]);
+            oacc[p] = mfma_f16(qa[qq][p], hb[qq], oacc[p]);
+        }
+    // U' as B fragments (position slots), the B operand of the update, whose A
+    // operand K^T diag(e^{G_C - G}) carries the decay:
+    //     H <- e^{G_C} H + (K^T diag(e^{G_C - G})) U'
     f16x8 up[2];
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-        up[qq] = cat_to_f16(acc[2 * qq], acc[2 * qq + 1]);
-        *reinterpret_cast<f16x8*>(&ho.up[qq][lane * 8]) = up[qq];
-    }
-    const float gam = st.g[kChunk + kChunk - 1];
+    for (int qq = 0; qq < 2; ++qq) up[qq] = cat_to_f16(acc[2 * qq], acc[2 * qq + 1]);
+    f16x8 ka[2][8];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ka[qq][i] = *reinterpret_cast<const f16x8*>(&st.k[((i * 2 + qq) * 64 + lane) * 8]);
+    const float gam = st.eg[kChunk - 1];
 #pragma unroll
     for (int i = 0; i < 8; ++i) H[i] *= gam;
     // eight independent accumulator chains, interleaved
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const f16x8 ka = *reinterpret_cast<const f16x8*>(&st.k[((i * 2 + qq) * 64 + lane) * 8]);
-            H[i] = mfma_f16(ka, up[qq], H[i]);
+        for (int i = 0; i < 8; ++i) H[i] = mfma_f16(ka[qq][i], up[qq], H[i]);
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * p + 4 * gq + e;
+            float* d = row < len ? out_tile + (size_t)row * row_stride + ln : junk + lane;
+            *d = oacc[p][e];
         }
+    if constexpr (kSnap) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) snap[(size_t)(16 * i + 4 * gq + e) * kDim + ln] = H[i][e];
+    }
 }
 
 // Grid: 8 * ceil(U / 8) * 8 workgroups of 128 threads, U = n_seqs * h_v.
 // Workgroup b runs on XCD b % 8 (round-robin dispatch); it takes unit
 // 8 * (m / 8) + b % 8 and column tile m % 8, m = b / 8, so all tiles of a
 // unit share an XCD.
+template <bool kSnap>
 __global__ __launch_bounds__(128) void gdn_chunk_state(
     const int32_t* __restrict__ cu, int n_seqs, int h_v,
-    const float* __restrict__ s0, float* __restrict__ s_final, ChunkWorkspace ws)
+    const float* s0, float* s_final, float* __restrict__ out, float* __restrict__ chunk_states,
+    ChunkWorkspace ws)
 {
     const int b = blockIdx.x;
     const int m = b >> 3;
@@ -505,7 +647,6 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
     const int col = 16 * ct + ln;
 
     __shared__ __attribute__((aligned(16))) StateStage stage[kStages];
-    __shared__ __attribute__((aligned(16))) StateHandoff handoff[2];
 
     const int start = cu[seq];
     const int end = cu[seq + 1];
@@ -531,7 +672,12 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
         if (nchunks > 0) {
             lds_barrier();                                   // B_0: chunk 0 has landed
             for (int c = 0; c < nchunks; ++c) {
-                state_chunk(H, stage[c % kStages], handoff[c & 1], lane, gq);
+                const int t0 = start + kChunk * c;
+                // tile bases (column 16 ct); each lane adds its column ln
+                float* snap = kSnap ? chunk_states + ((size_t)(slot0 + c) * h_v + h) * kDim * kDim + 16 * ct
+                                    : nullptr;
+                state_chunk<kSnap>(H, stage[c % kStages], out + ((size_t)t0 * h_v + h) * kDim + 16 * ct,
+                                   (size_t)h_v * kDim, min(kChunk, end - t0), snap, ws.junk, lane, gq, ln);
                 lds_barrier();                               // B_{c+1}
             }
         }
@@ -544,172 +690,19 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
         }
     } else if (nchunks > 0) {
         // copies for chunks past the last one are issued too (clamped, never
-        // used) so the number of memory operations per chunk never changes
+        // used) so the number of copies per chunk never changes
         state_copy(stage[0], ws, vidx(0), ct, lane);
         state_copy(stage[1], ws, vidx(1), ct, lane);
         wait_vmcnt<kCopiesPerChunk>();                       // chunk 0 has landed
         lds_barrier();                                       // B_0
         for (int c = 0; c < nchunks; ++c) {
             // between B_c and B_{c+1}: the compute wave works on chunk c
-            if (c > 0) state_store(handoff[(c - 1) & 1], ws, vidx(c - 1), ct, lane);
             state_copy(stage[(c + 2) % kStages], ws, vidx(c + 2), ct, lane);
-            // chunk c + 1 landed: after its copies came this chunk's stores
-            // (none for c = 0) and the copies of chunk c + 2
-            if (c > 0) wait_vmcnt<kStoresPerChunk + kCopiesPerChunk>();
-            else wait_vmcnt<kCopiesPerChunk>();
+            wait_vmcnt<kCopiesPerChunk>();                   // chunk c + 1 has landed
             lds_barrier();                                   // B_{c+1}
         }
-        state_store(handoff[(nchunks - 1) & 1], ws, vidx(nchunks - 1), ct, lane);
         // drain the copies past the end before the workgroup's LDS goes away
         __builtin_amdgcn_s_waitcnt(0);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Stage 3: output.  One workgroup per (chunk slot, value head).
-//   O = diag(e^G) Q H0 + P U',   P = M o (Q K^T)
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gdn_chunk_out(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const int32_t* __restrict__ cu, int n_seqs, int h_qk, int h_v,
-    float* __restrict__ out, ChunkWorkspace ws)
-{
-    const int slot = blockIdx.x;
-    const int h = blockIdx.y;
-    int seq, t0, len;
-    if (!resolve_slot(cu, n_seqs, slot, seq, t0, len)) return;
-    const int j = h / (h_v / h_qk);
-
-    // Q and K row tiles, reused at the end as the fp32 output staging tile
-    __shared__ __attribute__((aligned(16))) f16 QKs[2 * kChunk * kQS];
-    f16* const Qs = QKs;                 // Q [pos][dim]
-    f16* const Ks = QKs + kChunk * kQS;  // K [pos][dim]
-    __shared__ __attribute__((aligned(16))) f16 Ps[kChunk * kTS];   // P [pos][pos]
-    __shared__ float Gs[kChunk];   // G_r
-    __shared__ float Es[kChunk];   // e^{G_r}
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int gq = lane >> 4;
-    const int ln = lane & 15;
-    const size_t wsidx = ws.vunit(slot, h);
-
-    for (int i = tid; i < kChunk * 16; i += 256) {
-        const int r = i >> 4;
-        const int c8 = (i & 15) * 8;
-        u16x8 qb = {0, 0, 0, 0, 0, 0, 0, 0};
-        u16x8 kb = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (r < len) {
-            qb = *reinterpret_cast<const u16x8*>(q + ((size_t)(t0 + r) * h_qk + j) * kDim + c8);
-            kb = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + r) * h_qk + j) * kDim + c8);
-        }
-        *reinterpret_cast<f16x8*>(Qs + r * kQS + c8) = bf16x8_to_f16x8(qb);
-        *reinterpret_cast<f16x8*>(Ks + r * kQS + c8) = bf16x8_to_f16x8(kb);
-    }
-    if (tid < kChunk) {
-        Gs[tid] = ws.gcum[wsidx * kGElems + 128 + tid];
-        Es[tid] = ws.gcum[wsidx * kGElems + 64 + tid];
-    }
-    __syncthreads();
-
-    // ---- P = M o (Q K^T); wave w owns row tile w, zero above the diagonal
-    {
-        const int p = wave;
-        f16x8 qa[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            qa[kk] = *reinterpret_cast<const f16x8*>(Qs + (16 * p + ln) * kQS + 32 * kk + 8 * gq);
-        for (int jt = 0; jt < 4; ++jt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (jt <= p) {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const f16x8 kb = *reinterpret_cast<const f16x8*>(Ks + (16 * jt + ln) * kQS + 32 * kk + 8 * gq);
-                    acc = mfma_f16(qa[kk], kb, acc);
-                }
-            }
-            const int s = 16 * jt + ln;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * p + 4 * gq + e;
-                Ps[r * kTS + s] = static_cast<f16>((s <= r) ? acc[e] * exp_f(Gs[r] - Gs[s]) : 0.f);
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- O tiles: wave w owns column tiles 2w, 2w+1, all four row tiles
-    f32x4 o[4][2];
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int a = 0; a < 2; ++a) o[p][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const f16* hsrc = ws.hc + wsidx * kHcElems;
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-        f16x8 hb[2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-            hb[a] = *reinterpret_cast<const f16x8*>(hsrc + (((2 * wave + a) * 4 + qq) * 64 + lane) * 8);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const f16* qrow = Qs + (16 * p + ln) * kQS;
-            const f16x4 lo = *reinterpret_cast<const f16x4*>(qrow + 32 * qq + 4 * gq);
-            const f16x4 hi = *reinterpret_cast<const f16x4*>(qrow + 32 * qq + 16 + 4 * gq);
-            const f16x8 qa = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-            for (int a = 0; a < 2; ++a) o[p][a] = mfma_f16(qa, hb[a], o[p][a]);
-        }
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float f = Es[16 * p + 4 * gq + e];
-            o[p][0][e] *= f;
-            o[p][1][e] *= f;
-        }
-
-    const f16* usrc = ws.up + wsidx * kUpElems;
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-        f16x8 ub[2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-            ub[a] = *reinterpret_cast<const f16x8*>(usrc + (((2 * wave + a) * 2 + qq) * 64 + lane) * 8);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const f16* prow = Ps + (16 * p + ln) * kTS;
-            const f16x4 lo = *reinterpret_cast<const f16x4*>(prow + 32 * qq + 4 * gq);
-            const f16x4 hi = *reinterpret_cast<const f16x4*>(prow + 32 * qq + 16 + 4 * gq);
-            const f16x8 pa = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-            for (int a = 0; a < 2; ++a) o[p][a] = mfma_f16(pa, ub[a], o[p][a]);
-        }
-    }
-
-    // ---- stage the 64 x 128 fp32 tile in LDS (over Q and K, now dead) and
-    //      write whole 512-byte token rows with 16-byte stores
-    __syncthreads();
-    constexpr int kOS = 132;   // fp32 row stride
-    float* Os = reinterpret_cast<float*>(Qs);
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-                Os[(16 * p + 4 * gq + e) * kOS + 16 * (2 * wave + a) + ln] = o[p][a][e];
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int idx = tid + 256 * it;
-        const int r = idx >> 5, c4 = (idx & 31) * 4;
-        if (r < len)
-            *reinterpret_cast<f32x4*>(out + ((size_t)(t0 + r) * h_v + h) * kDim + c4) =
-                *reinterpret_cast<const f32x4*>(Os + r * kOS + c4);
     }
 }
 
@@ -719,22 +712,23 @@ __global__ __launch_bounds__(256) void gdn_chunk_out(
 hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* g, const float* beta, const int32_t* cu,
                             int n_seqs, int64_t total_tokens, int h_qk, int h_v,
-                            const float* s0, float* out, float* s_final,
+                            const float* s0, float* out, float* s_final, float* chunk_states,
                             const ChunkWorkspace& ws, int n_slots, int stage_mask,
                             hipStream_t stream)
 {
     if ((stage_mask & 1) && total_tokens > 0) {
         hipLaunchKernelGGL(gdn_chunk_prep, dim3(n_slots, h_v), dim3(256), 0, stream,
-                           k, v, g, beta, cu, n_seqs, h_qk, h_v, ws);
+                           q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws);
     }
     if ((stage_mask & 2) && n_seqs > 0) {
         const int units = n_seqs * h_v;
-        hipLaunchKernelGGL(gdn_chunk_state, dim3(64 * ((units + 7) / 8)), dim3(128), 0, stream,
-                           cu, n_seqs, h_v, s0, s_final, ws);
-    }
-    if ((stage_mask & 4) && total_tokens > 0) {
-        hipLaunchKernelGGL(gdn_chunk_out, dim3(n_slots, h_v), dim3(256), 0, stream,
-                           q, k, cu, n_seqs, h_qk, h_v, out, ws);
+        const dim3 grid(64 * ((units + 7) / 8));
+        if (chunk_states)
+            hipLaunchKernelGGL(gdn_chunk_state<true>, grid, dim3(128), 0, stream,
+                               cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws);
+        else
+            hipLaunchKernelGGL(gdn_chunk_state<false>, grid, dim3(128), 0, stream,
+                               cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws);
     }
     return hipGetLastError();
 }

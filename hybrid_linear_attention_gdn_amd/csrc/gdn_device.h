@@ -35,15 +35,17 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// Per (chunk slot, value head) element counts of the workspace regions.
-constexpr size_t kWElems = 16 * 64 * 8;    // -W, A-operand fragments [p][qq][lane][8]
+// Per (chunk slot, value head) element counts of the workspace regions, all
+// in matrix-core fragment order.
+constexpr size_t kWElems = 16 * 64 * 8;    // -W, A fragments [p][qq][lane][8]
 constexpr size_t kUElems = 8 * 4 * 64 * 4;  // U, accumulator fragments [ct][p][lane][4]
-constexpr size_t kUpElems = 8 * 2 * 64 * 8; // U', B-operand fragments [ct][qq][lane][8]
-constexpr size_t kHcElems = 8 * 4 * 64 * 8; // chunk state, B-operand fragments [ct][qq][lane][8]
-// Decay vectors: [0, 64) e^{G_C - G_r} (state update), [64, 128) e^{G_r}, [128, 192) G_r
-constexpr size_t kGElems = 192;
-// K^T diag(e^{G_C - G}) as A-operand fragments of the state update [d_k tile][pos step][lane][8]
+// K^T diag(e^{G_C - G}) as A fragments of the state update [d_k tile][pos step][lane][8]
 constexpr size_t kKtElems = 8 * 2 * 64 * 8;
+// Q' = diag(e^G) Q - (M o Q K^T) W, A fragments over d_k [p][qq][lane][8]
+constexpr size_t kQtElems = 4 * 4 * 64 * 8;
+// Y = (M o Q K^T) U shares U's accumulator-fragment layout and size (kUElems)
+constexpr size_t kGElems = 64;              // e^{G_r}
+constexpr size_t kJunkBytes = 1024;         // sink for the lanes of masked-off stores
 
 // Workspace regions are head-major: unit (slot, head) sits at head * n_slots
 // + slot, so one head's consecutive chunks are contiguous in memory and the
@@ -51,10 +53,11 @@ constexpr size_t kKtElems = 8 * 2 * 64 * 8;
 struct ChunkWorkspace {
     f16* w;
     f16* u;
-    f16* up;
-    f16* hc;
     f16* kt;
-    float* gcum;
+    f16* qt;
+    f16* y;
+    float* eg;
+    float* junk;
     int n_slots;
 
     __device__ __forceinline__ size_t vunit(int slot, int h) const { return (size_t)h * n_slots + slot; }

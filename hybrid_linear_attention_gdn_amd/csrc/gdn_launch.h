@@ -8,11 +8,12 @@
 
 namespace gdn {
 
-// Enqueues prep, state and output kernels of the chunked prefill on `stream`.
+// Enqueues the chunked prefill on `stream`: prep (stage bit 0) and the state
+// recurrence with the output (stage bit 1); chunk_states may be null.
 hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* g, const float* beta, const int32_t* cu,
                             int n_seqs, int64_t total_tokens, int h_qk, int h_v,
-                            const float* s0, float* out, float* s_final,
+                            const float* s0, float* out, float* s_final, float* chunk_states,
                             const ChunkWorkspace& ws, int n_slots, int stage_mask,
                             hipStream_t stream);
 

@@ -10,7 +10,7 @@
  * The pages this library follows use it as the linear-attention layer of a
  * hybrid model: the "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page, section
  * 2 ("GDN prefill"), runs the prefill chunkwise with chunk length 64 in three
- * stages (intra-chunk preparation, inter-chunk state recurrence, output), the
+ * steps (intra-chunk preparation, inter-chunk state recurrence, output), the
  * entry point gdn_chunk_fwd below; its section 1 describes the speculative
  * verify step of 1 + K query tokens per request, and the "Qwen3.8-27B on one
  * RTX 3090" page keeps a fixed-size recurrent state per request plus one
@@ -84,12 +84,15 @@ gdn_status gdn_chunk_fwd_workspace_size(const gdn_dims* dims, size_t* bytes);
 
 /*
  * Chunked prefill (chunk length 64) over a packed batch of N sequences
- * (tokens cu_seqlens[n] .. cu_seqlens[n+1]-1).  Follows the three-stage split
- * of the "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page, section 2:
- *   gdn_chunk_prep  -- decay cumsum, masked K K^T, (I + A)^{-1}, W and U;
- *   gdn_chunk_state -- inter-chunk recurrence, state held in matrix-core
- *                      accumulators, next chunk prefetched;
- *   gdn_chunk_out   -- intra-chunk causal term plus Q S.
+ * (tokens cu_seqlens[n] .. cu_seqlens[n+1]-1).  Follows the three steps
+ * of the "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page, section 2, in two
+ * kernels:
+ *   gdn_chunk_prep  -- decay cumsum, masked K K^T, (I + A)^{-1}, W and U, and
+ *                      the state-independent parts of the output
+ *                      (Q' = diag(e^G) Q - P W, Y = P U, P = M o Q K^T);
+ *   gdn_chunk_state -- inter-chunk recurrence with the state held in
+ *                      matrix-core accumulators and the next chunks
+ *                      prefetched, and the output O = Y + Q' S_chunk.
  *  q, k, v       bf16 device tensors, layouts above.
  *  g, beta       float32 [T, H_v].
  *  cu_seqlens    int32 [N + 1], device.
@@ -111,14 +114,47 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
                          void* stream);
 
 /*
+ * Number of chunk-state slots of a batch: n_seqs + floor(total_tokens / 64)
+ * + 1, the first dimension of gdn_chunk_fwd_snapshots' chunk_states.  Host
+ * only.
+ */
+gdn_status gdn_chunk_state_slots(const gdn_dims* dims, int64_t* n_slots);
+
+/*
+ * gdn_chunk_fwd that also exports the state at every chunk boundary, for a
+ * prefix cache that keeps the recurrent state (the "Qwen3.8-27B on one RTX
+ * 3090" page, section "Pourquoi cela convient aux agents harness": the prefix
+ * cache of the hybrid model stores the DeltaNet state as well as the
+ * attention KV).
+ *  chunk_states  float32 [n_slots, H_v, d_k, d_v], n_slots from
+ *                gdn_chunk_state_slots.  The state after chunk c of sequence
+ *                n, i.e. after its first min(64 (c + 1), len_n) tokens, goes
+ *                to slot n + floor(cu_seqlens[n] / 64) + c for c = 0 ..
+ *                ceil(len_n / 64) - 1 (the last one equals the final state).
+ *                Slots of different sequences never overlap; slots no chunk
+ *                maps to are not written.  Required (non-NULL) when N > 0.
+ * Other arguments, results and errors as gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_fwd_snapshots(const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta,
+                                   const int32_t* cu_seqlens,
+                                   const float* initial_state,
+                                   float* out,
+                                   float* final_state,
+                                   float* chunk_states,
+                                   const gdn_dims* dims,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * Runs only the selected stages of gdn_chunk_fwd, for callers that time or
  * schedule the stages one by one.  stage_mask bits: 1 = gdn_chunk_prep,
- * 2 = gdn_chunk_state, 4 = gdn_chunk_out (7 = gdn_chunk_fwd).  A stage reads
- * what earlier stages left in the same workspace; run them in order, on the
+ * 2 = gdn_chunk_state with the output (3 = gdn_chunk_fwd).  The second stage
+ * reads what the first left in the same workspace; run them in order, on the
  * same inputs and workspace, or the results are undefined (memory accesses
  * stay in bounds regardless, since every index comes from cu_seqlens and the
  * launch grid, never from workspace contents).  Arguments as gdn_chunk_fwd;
- * a mask outside 1..7 returns GDN_ERR_INVALID_VALUE.
+ * a mask outside 1..3 returns GDN_ERR_INVALID_VALUE.
  */
 gdn_status gdn_chunk_fwd_stages(const void* q, const void* k, const void* v,
                                 const float* g, const float* beta,

@@ -71,9 +71,9 @@ def test_workspace_size_formula(lib):
     st, b = ws_size(lib, dims(n=1, T=4000, hqk=16, hv=32))
     assert st == 0
     slots = 1 + 4000 // 64 + 1
-    per_v = (8192 * 4 + 16384) * 2 + 192 * 4    # W, U, U', decayed K^T, chunk state, decay vectors
-    need = slots * 32 * per_v
-    assert need <= b < need + 6 * 256
+    per_v = 8192 * 5 * 2 + 64 * 4    # -W, U, decayed K^T, Q', Y (fp16), e^G (fp32)
+    need = slots * 32 * per_v + 1024  # + the sink of masked-off stores
+    assert need <= b < need + 7 * 256
 
 
 @pytest.mark.parametrize("d,code", [
@@ -208,7 +208,7 @@ def test_last_error_is_thread_local(lib):
 def test_stages_rejects_bad_mask(lib):
     d = dims()
     need = ws_size(lib, d)[1]
-    for mask in (0, 8, -1):
+    for mask in (0, 4, 7, 8, -1):
         assert lib.gdn_chunk_fwd_stages(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
                                         ctypes.byref(d), FAKE, need, mask, None) == gdn.GDN_ERR_INVALID_VALUE
 
@@ -251,3 +251,34 @@ def test_slots_step_argument_checks(lib):
 def test_slots_step_zero_requests_is_a_noop(lib):
     assert slots_call(lib, dims(n=0, T=0), R=0, q=None, k=None, v=None, g=None, beta=None, cu=None,
                       pool=None, table=None, out=None) == gdn.GDN_SUCCESS
+
+
+def test_chunk_state_slots(lib):
+    n = ctypes.c_int64(-1)
+    assert lib.gdn_chunk_state_slots(ctypes.byref(dims(n=3, T=200)), ctypes.byref(n)) == gdn.GDN_SUCCESS
+    assert n.value == 3 + 200 // 64 + 1
+    assert lib.gdn_chunk_state_slots(ctypes.byref(dims(n=3, T=200)), None) == gdn.GDN_ERR_INVALID_VALUE
+    assert lib.gdn_chunk_state_slots(ctypes.byref(dims(dk=64, dv=64)), ctypes.byref(n)) == gdn.GDN_ERR_NOT_SUPPORTED
+    assert gdn.gdn_chunk_state_slots(1, 4000, 16, 32) == 64
+
+
+def snap_call(lib, d, **over):
+    need = ws_size(lib, d)[1]
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, s0=None, out=FAKE, fin=None,
+                cs=FAKE, ws=FAKE, wsb=need)
+    args.update(over)
+    return lib.gdn_chunk_fwd_snapshots(args["q"], args["k"], args["v"], args["g"], args["beta"], args["cu"],
+                                       args["s0"], args["out"], args["fin"], args["cs"], ctypes.byref(d),
+                                       args["ws"], args["wsb"], None)
+
+
+def test_snapshots_rejects_bad_arguments(lib):
+    d = dims(n=2, T=130)
+    assert snap_call(lib, d, cs=None) == gdn.GDN_ERR_INVALID_VALUE
+    assert snap_call(lib, d, cs=MIS) == gdn.GDN_ERR_MISALIGNED
+    assert snap_call(lib, d, q=None) == gdn.GDN_ERR_INVALID_VALUE
+    assert snap_call(lib, d, ws=None) == gdn.GDN_ERR_WORKSPACE
+    assert snap_call(lib, d, wsb=ws_size(lib, d)[1] - 1) == gdn.GDN_ERR_WORKSPACE
+    assert snap_call(lib, dims(n=2, T=130, dk=64, dv=64)) == gdn.GDN_ERR_NOT_SUPPORTED
+    assert snap_call(lib, dims(n=0, T=0), cs=None, q=None, k=None, v=None, g=None, beta=None, cu=None,
+                     out=None, ws=None, wsb=0) == gdn.GDN_SUCCESS

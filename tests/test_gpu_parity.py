@@ -234,3 +234,70 @@ def test_long_context_131072_sampled():
     P = 2048
     po, _, _ = oracle.forward(x.q[:P], x.k[:P], x.v[:P], x.g[:P], x.beta[:P], [0, P], None)
     assert rel_l2(out[:P].cpu().numpy(), po) <= OUT_TOL
+
+
+# ------------------------------------------------------------ state snapshots at chunk boundaries
+
+def _snapshots(x, d, poison=True):
+    import hybrid_linear_attention_gdn_amd as gdn
+    from gpu_util import workspace_for
+    n_slots = gdn.gdn_chunk_state_slots(x.n_seqs, x.total_tokens, x.h_qk, x.h_v)
+    cs = torch.full((n_slots, x.h_v, 128, 128), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.empty((x.total_tokens, x.h_v, x.d_v), dtype=torch.float32, device="cuda")
+    fin = torch.empty((x.n_seqs, x.h_v, 128, 128), dtype=torch.float32, device="cuda")
+    ws = workspace_for(x)
+    if poison:
+        ws.fill_(0xFF)
+    gdn.gdn_chunk_fwd_snapshots(d.q, d.k, d.v, d.g, d.beta, d.cu, d.s0, out, fin, cs, ws)
+    torch.cuda.synchronize()
+    return out, fin, cs
+
+
+def test_chunk_snapshots_varlen():
+    """State after every chunk of every sequence, in slot n + cu[n] // 64 + c;
+    slots no chunk maps to stay untouched; outputs and final states are those
+    of gdn_chunk_fwd, bit for bit."""
+    lengths = [200, 64, 1, 130, 0, 65]
+    x = gi.make_inputs(lengths, 2, 4, 128, 128, seed=77, state_std=0.02)
+    _print_case("snapshots_varlen", x)
+    d = DevInputs(x)
+    out, fin, cs = _snapshots(x, d)
+    _, _, rs = oracle.forward_inputs(x, precision="f64", record_states=True)
+    cs_np, fin_np = cs.cpu().numpy(), fin.cpu().numpy()
+    written = set()
+    for n, L in enumerate(lengths):
+        start = int(x.cu_seqlens[n])
+        nch = (L + 63) // 64
+        for c in range(nch):
+            slot = n + start // 64 + c
+            t_end = start + min(64 * (c + 1), L) - 1
+            e = rel_l2(cs_np[slot], rs[t_end])
+            assert e <= STATE_TOL, (n, c, e)
+            assert slot not in written
+            written.add(slot)
+        if nch:
+            np.testing.assert_array_equal(cs_np[n + start // 64 + nch - 1], fin_np[n])
+    for slot in range(cs_np.shape[0]):
+        if slot not in written:
+            assert np.isnan(cs_np[slot]).all(), slot
+    out2, fin2 = chunk_fwd(d)
+    np.testing.assert_array_equal(out.cpu().numpy(), out2.cpu().numpy())
+    np.testing.assert_array_equal(fin_np, fin2.cpu().numpy())
+
+
+def test_chunk_snapshots_prefill_4000_sampled():
+    """Full-size prefill with snapshots: sampled chunk boundaries against the
+    oracle's state after the same prefix."""
+    x = gi.prefill_4000()
+    _print_case("snapshots_prefill_4000", x)
+    d = DevInputs(x)
+    out, fin, cs = _snapshots(x, d, poison=False)
+    cs_np = cs.cpu().numpy()
+    assert cs_np.shape[0] == 64 and np.isnan(cs_np[63]).all()
+    for c in (0, 1, 30, 62):
+        t = min(64 * (c + 1), 4000)
+        _, rf, _ = oracle.forward(x.q[:t], x.k[:t], x.v[:t], x.g[:t], x.beta[:t], np.array([0, t], np.int32))
+        e = rel_l2(cs_np[c], rf[0])
+        print(f"[result] snapshot chunk {c}: state rel-L2 {e:.3e}", flush=True)
+        assert e <= STATE_TOL
+    np.testing.assert_array_equal(cs_np[62], fin.cpu().numpy()[0])
