@@ -42,6 +42,14 @@ __device__ __forceinline__ int tsw(int d, int t) {
     return d * kChunk + (t ^ ((((d & 7) ^ (((d >> 3) & 3) << 1)) & 7) << 3));
 }
 
+// Row-major [pos][dim] bf16 tiles, 128 dims per row, no padding: 16-byte
+// chunk c (dims 8 c .. 8 c + 7) of row r sits at chunk c ^ (r % 16), so the
+// 16 rows read at the same dims by a fragment load hit 16 different banks.
+// Returns the element offset of chunk c of row r.
+__device__ __forceinline__ int rsw(int r, int c) {
+    return r * kDim + ((c ^ (r & 15)) << 3);
+}
+
 // ---------------------------------------------------------------------------
 // Stage 1: intra-chunk preparation.  One workgroup per (chunk slot, value
 // head); 51 KB of LDS so that three workgroups share a CU.  The UT transform
@@ -75,34 +83,30 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     const int ln = lane & 15;
     const size_t wsidx = ws.vunit(slot, h);
 
-    // ---- K as raw bf16 fragments (row 16 jt + ln, dims 32 kk + 8 gq .. +7):
-    //      kown = this wave's row tile, kf[jt] = row tiles jt < wave (the Gram
-    //      rows of wave w need tiles 0 .. w).  V for this wave's row tile.  Each
-    //      wave writes its own row tile of K and V transposed into LDS as fp16.
-    //      Pad rows are zero.
-    bf16x8 kf[3][4];
-    bf16x8 kown[4];
-#pragma unroll
-    for (int jt = 0; jt < 3; ++jt)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int r = 16 * jt + ln;
-            u16x8 bkv = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (jt < wave && r < len)
-                bkv = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + r) * h_qk + j) * kDim + 32 * kk + 8 * gq);
-            kf[jt][kk] = __builtin_bit_cast(bf16x8, bkv);
-        }
+    // ---- This wave's row tile of K, Q and V (rows 16 w + ln, dims 32 kk +
+    //      8 gq .. +7), the only global reads of the inputs: K and V go to LDS
+    //      transposed (fp16) for the products over positions; K also goes to
+    //      LDS row-major (bf16, in the A buffer, which is still free) so that
+    //      every wave can read the row tiles its Gram rows need.  Q stays in
+    //      registers.  Pad rows are zero.
+    uint16_t* Kr = reinterpret_cast<uint16_t*>(Ab);   // [pos][dim] bf16, chunk-swizzled
+    bf16x8 kown[4], qf[4];
     {
         const int r = 16 * wave + ln;
+        const size_t krow = ((size_t)(t0 + r) * h_qk + j) * kDim;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             u16x8 kb = {0, 0, 0, 0, 0, 0, 0, 0};
+            u16x8 qb = {0, 0, 0, 0, 0, 0, 0, 0};
             u16x8 vb = {0, 0, 0, 0, 0, 0, 0, 0};
             if (r < len) {
-                kb = *reinterpret_cast<const u16x8*>(k + ((size_t)(t0 + r) * h_qk + j) * kDim + 32 * kk + 8 * gq);
+                kb = *reinterpret_cast<const u16x8*>(k + krow + 32 * kk + 8 * gq);
+                qb = *reinterpret_cast<const u16x8*>(q + krow + 32 * kk + 8 * gq);
                 vb = *reinterpret_cast<const u16x8*>(v + ((size_t)(t0 + r) * h_v + h) * kDim + 32 * kk + 8 * gq);
             }
             kown[kk] = __builtin_bit_cast(bf16x8, kb);
+            qf[kk] = __builtin_bit_cast(bf16x8, qb);
+            *reinterpret_cast<u16x8*>(Kr + rsw(r, 4 * kk + gq)) = kb;
             const f16x8 kt8 = bf16x8_to_f16x8(kb);
             const f16x8 vt8 = bf16x8_to_f16x8(vb);
 #pragma unroll
@@ -135,6 +139,17 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     }
     __syncthreads();
 
+    // K row tiles jt < w for this wave's Gram rows
+    bf16x8 kf[3][4];
+#pragma unroll
+    for (int jt = 0; jt < 3; ++jt)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            kf[jt][kk] = bf16x8{};
+            if (jt < wave)
+                kf[jt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(Kr + rsw(16 * jt + ln, 4 * kk + gq)));
+        }
+
     // ---- K^T diag(e^{G_C - G}) as A-operand fragments of the state update:
     //      fragment (i, qq), lane (gq, ln) = K[p][16 i + ln] e^{G_C - G_p} at the
     //      position slots p(gq, s) of K-step qq.
@@ -157,30 +172,26 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
         }
     }
 
-    // ---- A = strictly lower (beta_r e^{G_r-G_s} K K^T); wave w owns row tile w
-    //      (tiles above the diagonal are never written or read as A)
+    // ---- Gram rows of A = strictly lower (beta_r e^{G_r-G_s} K K^T); wave w
+    //      owns row tile w (tiles above the diagonal are never written or read
+    //      as A).  The accumulators wait in registers until every wave has read
+    //      its K tiles from the A buffer.
+    f32x4 gacc[4];
     {
         const int p = wave;
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
+            gacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};   // exact bf16 inputs
             if (jt > p) continue;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};   // exact bf16 inputs
             if (jt == p) {
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(kown[kk], kown[kk], acc);
+                for (int kk = 0; kk < 4; ++kk) gacc[jt] = mfma_bf16(kown[kk], kown[kk], gacc[jt]);
             } else {
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(kown[kk], kf[jt < 3 ? jt : 0][kk], acc);
-            }
-            const int s = 16 * jt + ln;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * p + 4 * gq + e;
-                Ab[r * kTS + s] = (s < r) ? Bs[r] * exp_f(Gs[r] - Gs[s]) * acc[e] : 0.f;
+                for (int kk = 0; kk < 4; ++kk) gacc[jt] = mfma_bf16(kown[kk], kf[jt < 3 ? jt : 0][kk], gacc[jt]);
             }
         }
     }
-    __syncthreads();
 
     // ---- P = M o (Q K^T) for row tile p = wave, M_rs = e^{G_r - G_s} (s <= r),
     //      computed as (K Q^T)[s][r] so that the accumulators of two position
@@ -190,13 +201,6 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     {
         const int p = wave;
         const int r = 16 * p + ln;
-        bf16x8 qf[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            u16x8 b = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (r < len) b = *reinterpret_cast<const u16x8*>(q + ((size_t)(t0 + r) * h_qk + j) * kDim + 32 * kk + 8 * gq);
-            qf[kk] = __builtin_bit_cast(bf16x8, b);
-        }
         f32x4 dt[4];
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
@@ -219,6 +223,22 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) pf[qq] = cat_to_f16(dt[2 * qq], dt[2 * qq + 1]);
     }
+
+    __syncthreads();                                  // K rows in the A buffer are consumed
+    {
+        const int p = wave;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            if (jt > p) continue;
+            const int s = 16 * jt + ln;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * p + 4 * gq + e;
+                Ab[r * kTS + s] = (s < r) ? Bs[r] * exp_f(Gs[r] - Gs[s]) * gacc[jt][e] : 0.f;
+            }
+        }
+    }
+    __syncthreads();
 
     // ---- Tm = (I + A)^{-1}, blocked by 16, in place.
     //  (1) Diagonal blocks Tm_ii = (I + A_ii)^{-1}: wave i, lane c % 16 holds
@@ -325,19 +345,6 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 
     // ---- W = TW K (twice: dims on lanes and positions on lanes) and U = TU V.
     //      Wave w owns d_k tiles 2w, 2w+1 and d_v tiles 2w, 2w+1.
-    // Q~^T = diag(e^G) Q, transposed, for this wave's d_k tiles: accumulator
-    // layout (d_k rows 4 gq + e, query row 16 p + ln).  Loaded now, used last.
-    u16x4 qraw[2][4];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int r = 16 * p + ln;
-            qraw[a][p] = u16x4{0, 0, 0, 0};
-            if (r < len)
-                qraw[a][p] = *reinterpret_cast<const u16x4*>(q + ((size_t)(t0 + r) * h_qk + j) * kDim +
-                                                            16 * (2 * wave + a) + 4 * gq);
-        }
     f32x4 w2acc[4][2];   // W[pos tile p][d_k tile 2w + a]: d_k on lanes
     f32x4 uacc[4][2];    // U[pos tile p][d_v tile 2w + a]: d_v on lanes
     {
@@ -417,7 +424,21 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
         *reinterpret_cast<f16x8*>(Pl + ((wave * 2 + qq) * 64 + lane) * 8) = pf[qq];
+    uint16_t* Qr = reinterpret_cast<uint16_t*>(VsT);  // Q rows [pos][dim] bf16, chunk-swizzled
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        *reinterpret_cast<u16x8*>(Qr + rsw(16 * wave + ln, 4 * kk + gq)) = __builtin_bit_cast(u16x8, qf[kk]);
     __syncthreads();
+    // Q~^T = diag(e^G) Q, transposed, for this wave's d_k tiles in accumulator
+    // layout: d_k rows 16 (2w + a) + 4 gq + e, query row 16 p + ln
+    u16x4 qraw[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int dd = 16 * (2 * wave + a) + 4 * gq;
+            qraw[a][p] = *reinterpret_cast<const u16x4*>(Qr + rsw(16 * p + ln, dd >> 3) + (dd & 7));
+        }
     f16x8 pa[4][2];
 #pragma unroll
     for (int p = 0; p < 4; ++p)
