@@ -177,13 +177,33 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    # Timed region: K steps back to back on the current stream.
     t_step = time_launches(step, args.steps, torch)
 
-    stage_t = {}
-    for name, mask in (("prep", 1), ("state", 2)):
-        stage_t[name] = time_launches(
-            lambda m=mask: gdn.gdn_chunk_fwd_stages(q, k, v, g, beta, cu, None, out, fin, ws, m),
-            args.steps, torch)
+    # The same K steps again with HIP events between the two kernels of each
+    # step (launched stage by stage), for each kernel's mean duration.  The
+    # events add a few microseconds of gap per kernel, so these durations are
+    # upper bounds of the kernel times.
+    s = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e_start.record(s)
+    for i in range(args.steps):
+        ev[i][0].record(s)
+        gdn.gdn_chunk_fwd_stages(q, k, v, g, beta, cu, None, out, fin, ws, 1)
+        ev[i][1].record(s)
+        gdn.gdn_chunk_fwd_stages(q, k, v, g, beta, cu, None, out, fin, ws, 2)
+        ev[i][2].record(s)
+    e_end.record(s)
+    torch.cuda.synchronize()
+    t_step_evented = e_start.elapsed_time(e_end) / 1e3 / args.steps
+    stage_t = {
+        "prep": sum(e[0].elapsed_time(e[1]) for e in ev) / 1e3 / args.steps,
+        "state": sum(e[1].elapsed_time(e[2]) for e in ev) / 1e3 / args.steps,
+    }
     step()
     torch.cuda.synchronize()
 
@@ -209,6 +229,7 @@ def main():
     f_layer, b_layer = work["layer"]
     prefill = {
         "ms_per_layer": t_step * 1e3,
+        "ms_per_layer_with_events": t_step_evented * 1e3,
         "pct_mfma_peak": 100 * f_layer * T / t_step / PEAK_MFMA_F16,
         "pct_hbm_peak": 100 * (b_layer * T + per_seq["layer"]) / t_step / PEAK_HBM,
         "algorithmic_flops": f_layer * T,

@@ -64,7 +64,7 @@ int64_t n_chunk_slots(const gdn_dims* d) {
 }
 
 struct Layout {
-    size_t w, u, kt, qt, y, eg, junk, total;
+    size_t w, u, kt, qt, y, dg, junk, total;
 };
 
 Layout workspace_layout(const gdn_dims* d) {
@@ -73,10 +73,10 @@ Layout workspace_layout(const gdn_dims* d) {
     size_t off = 0;
     L.w = off;  off += round_up(units * gdn::kWElems * sizeof(gdn::f16));
     L.u = off;  off += round_up(units * gdn::kUElems * sizeof(gdn::f16));
-    L.kt = off; off += round_up(units * gdn::kKtElems * sizeof(gdn::f16));
+    L.kt = off; off += round_up((size_t)n_chunk_slots(d) * (size_t)d->n_heads_qk * gdn::kKtElems * sizeof(gdn::f16));
     L.qt = off; off += round_up(units * gdn::kQtElems * sizeof(gdn::f16));
     L.y = off;  off += round_up(units * gdn::kUElems * sizeof(gdn::f16));
-    L.eg = off; off += round_up(units * gdn::kGElems * sizeof(float));
+    L.dg = off; off += round_up(units * gdn::kGElems * sizeof(float));
     L.junk = off; off += round_up(gdn::kJunkBytes);
     L.total = off;
     return L;
@@ -167,9 +167,10 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
     ws.kt = reinterpret_cast<gdn::f16*>(base + L.kt);
     ws.qt = reinterpret_cast<gdn::f16*>(base + L.qt);
     ws.y = reinterpret_cast<gdn::f16*>(base + L.y);
-    ws.eg = reinterpret_cast<float*>(base + L.eg);
+    ws.dg = reinterpret_cast<float*>(base + L.dg);
     ws.junk = reinterpret_cast<float*>(base + L.junk);
     ws.n_slots = (int)slots;
+    ws.group = dims->n_heads_v / dims->n_heads_qk;
 
     const hipError_t e = gdn::launch_chunk_fwd(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),

@@ -72,7 +72,6 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     __shared__ __attribute__((aligned(16))) float Ab[kChunk * kTS];  // A, then Tm, then TW | TU
     __shared__ __attribute__((aligned(16))) float Bs[kChunk];  // beta
     __shared__ __attribute__((aligned(16))) float Bw[kChunk];  // beta e^G
-    __shared__ float Ds[kChunk];     // e^{G_C - G}
     __shared__ float Gs[kChunk];     // G
     __shared__ float Es[kChunk];     // e^G
 
@@ -133,9 +132,8 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
         Gs[lane] = x;
         Bs[lane] = bt;
         Bw[lane] = bt * eg;
-        Ds[lane] = dc;
         Es[lane] = eg;
-        ws.eg[wsidx * kGElems + lane] = eg;
+        ws.dg[wsidx * kGElems + lane] = lane == kChunk - 1 ? eg : dc;
     }
     __syncthreads();
 
@@ -150,11 +148,12 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
                 kf[jt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(Kr + rsw(16 * jt + ln, 4 * kk + gq)));
         }
 
-    // ---- K^T diag(e^{G_C - G}) as A-operand fragments of the state update:
-    //      fragment (i, qq), lane (gq, ln) = K[p][16 i + ln] e^{G_C - G_p} at the
-    //      position slots p(gq, s) of K-step qq.
-    {
-        f16* kdst = ws.kt + wsidx * kKtElems;
+    // ---- K^T as A-operand fragments of the state update (which applies the
+    //      decay e^{G_C - G} to U' instead): fragment (i, qq), lane (gq, ln) =
+    //      K[p][16 i + ln] at the position slots p(gq, s) of K-step qq.  The
+    //      value heads of a q/k head share it; the first one writes it.
+    if (h % ws.group == 0) {
+        f16* kdst = ws.kt + ws.kunit(slot, j) * kKtElems;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int f = wave + 4 * it;          // fragment index i * 2 + qq
@@ -162,12 +161,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
             const int d = 16 * i + ln;
             const f16x4 lo = *reinterpret_cast<const f16x4*>(KsT + tsw(d, 32 * qq + 4 * gq));
             const f16x4 hi = *reinterpret_cast<const f16x4*>(KsT + tsw(d, 32 * qq + 16 + 4 * gq));
-            f16x8 fr;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                fr[e] = static_cast<f16>(static_cast<float>(lo[e]) * Ds[32 * qq + 4 * gq + e]);
-                fr[e + 4] = static_cast<f16>(static_cast<float>(hi[e]) * Ds[32 * qq + 16 + 4 * gq + e]);
-            }
+            const f16x8 fr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             *reinterpret_cast<f16x8*>(kdst + ((size_t)f * 64 + lane) * 8) = fr;
         }
     }
@@ -514,7 +508,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 // ---------------------------------------------------------------------------
 constexpr int kStages = 3;
 constexpr int kUTile = 4 * 64 * 4;                           // halves of U (or Y) fragments per tile
-constexpr int kCopiesPerChunk = 16 + 16 + 16 + 2 + 2 + 1;    // -W, K^T, Q', U, Y, e^G
+constexpr int kCopiesPerChunk = 16 + 16 + 16 + 2 + 2 + 1;    // -W, K^T, Q', U, Y, decay vector
 
 struct StateStage {
     f16 w[kWElems];
@@ -522,7 +516,7 @@ struct StateStage {
     f16 q[kQtElems];
     f16 u[kUTile];
     f16 y[kUTile];
-    float eg[kChunk];         // e^{G_r}; the last entry is e^{G_C}
+    float dg[kChunk];         // e^{G_C - G_r} (r < 63), e^{G_C} in entry 63
 };
 
 // s_waitcnt with vmcnt = N and the other counters left alone (gfx9 encoding).
@@ -544,13 +538,14 @@ __device__ __forceinline__ void lds_barrier() {
 
 // One chunk's copies: 1 KB pieces (16 B per lane) of -W, K^T, Q', U and Y,
 // and the 256 B decay vector (4 B per lane).
-__device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace& ws, size_t vu, int ct, int lane) {
+__device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace& ws, size_t vu, size_t ku,
+                                           int ct, int lane) {
     const f16* wsrc = ws.w + vu * kWElems;
-    const f16* ksrc = ws.kt + vu * kKtElems;
+    const f16* ksrc = ws.kt + ku * kKtElems;
     const f16* qsrc = ws.qt + vu * kQtElems;
     const f16* usrc = ws.u + vu * kUElems + (size_t)ct * kUTile;
     const f16* ysrc = ws.y + vu * kUElems + (size_t)ct * kUTile;
-    const float* gsrc = ws.eg + vu * kGElems;
+    const float* gsrc = ws.dg + vu * kGElems;
 #pragma unroll
     for (int piece = 0; piece < 16; ++piece) {
         __builtin_amdgcn_global_load_lds(wsrc + (piece * 64 + lane) * 8, st.w + piece * 512, 16, 0, 0);
@@ -564,7 +559,7 @@ __device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace&
     }
     // (the casts keep this 4-byte copy from tripping a code-generation fault
     //  of the ROCm 7.2 compiler in this kernel)
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gsrc + lane), reinterpret_cast<void*>(st.eg),
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gsrc + lane), reinterpret_cast<void*>(st.dg),
                                      4, 0, 0);
 }
 
@@ -608,9 +603,14 @@ __device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st,
             acc[p] = mfma_f16(wa[qq][p], hb[qq], acc[p]);
             oacc[p] = mfma_f16(qa[qq][p], hb[qq], oacc[p]);
         }
-    // U' as B fragments (position slots), the B operand of the update, whose A
-    // operand K^T diag(e^{G_C - G}) carries the decay:
-    //     H <- e^{G_C} H + (K^T diag(e^{G_C - G})) U'
+    // diag(e^{G_C - G}) U' as B fragments (position slots), the B operand of
+    // the update  H <- e^{G_C} H + K^T (diag(e^{G_C - G}) U')
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        f32x4 dc = *reinterpret_cast<const f32x4*>(&st.dg[16 * p + 4 * gq]);
+        if (p == 3 && gq == 3) dc[3] = 1.f;      // row 63: G_C - G_63 = 0
+        acc[p] *= dc;
+    }
     f16x8 up[2];
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) up[qq] = cat_to_f16(acc[2 * qq], acc[2 * qq + 1]);
@@ -619,7 +619,7 @@ __device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st,
     for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
         for (int i = 0; i < 8; ++i) ka[qq][i] = *reinterpret_cast<const f16x8*>(&st.k[((i * 2 + qq) * 64 + lane) * 8]);
-    const float gam = st.eg[kChunk - 1];
+    const float gam = st.dg[kChunk - 1];
 #pragma unroll
     for (int i = 0; i < 8; ++i) H[i] *= gam;
     // eight independent accumulator chains, interleaved
@@ -660,6 +660,7 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
     const int ct = m & 7;
     const int seq = unit / h_v;
     const int h = unit % h_v;
+    const int j = h / ws.group;
 
     const int lane = threadIdx.x & 63;
     const bool compute = threadIdx.x < 64;
@@ -675,6 +676,7 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
     const int slot0 = slot_base(cu, seq);
     const int last = nchunks - 1;
     auto vidx = [&](int c) { return ws.vunit(slot0 + min(c, last), h); };
+    auto kidx = [&](int c) { return ws.kunit(slot0 + min(c, last), j); };
     const size_t sbase = ((size_t)seq * h_v + h) * kDim * kDim;
 
     if (compute) {
@@ -712,13 +714,13 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
     } else if (nchunks > 0) {
         // copies for chunks past the last one are issued too (clamped, never
         // used) so the number of copies per chunk never changes
-        state_copy(stage[0], ws, vidx(0), ct, lane);
-        state_copy(stage[1], ws, vidx(1), ct, lane);
+        state_copy(stage[0], ws, vidx(0), kidx(0), ct, lane);
+        state_copy(stage[1], ws, vidx(1), kidx(1), ct, lane);
         wait_vmcnt<kCopiesPerChunk>();                       // chunk 0 has landed
         lds_barrier();                                       // B_0
         for (int c = 0; c < nchunks; ++c) {
             // between B_c and B_{c+1}: the compute wave works on chunk c
-            state_copy(stage[(c + 2) % kStages], ws, vidx(c + 2), ct, lane);
+            state_copy(stage[(c + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), ct, lane);
             wait_vmcnt<kCopiesPerChunk>();                   // chunk c + 1 has landed
             lds_barrier();                                   // B_{c+1}
         }
