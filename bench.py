@@ -49,16 +49,17 @@ def algorithmic_work():
     (W H, K^T U') and Q S.  The extra P W product of the Q' = diag(e^G) Q - P W
     rewrite is not counted.  Bytes count each tensor of a kernel's interface
     read or written once: bf16 inputs, fp32 g / beta / decay vector / output,
-    fp16 intermediates (-W, U, K^T diag(e^{G_C-G}), Q', Y per value head)."""
+    fp16 intermediates (-W, U, Q', Y per value head, K^T per q/k head)."""
     prep_f = H_V * (C * (D + D) + C * C / 3) + H_QK * (C * D) + H_QK * (C * D) + H_V * (C * D)
     state_f = H_V * (4 * D * D) + H_V * (2 * D * D)
     qk_b = H_QK * D * 2          # one of q or k, bf16
     v_b = H_V * D * 2
     gb_b = H_V * 4               # one of g, beta or the e^G vector
-    f16_row = H_V * D * 2        # one of -W, U, K^T-decayed, Q', Y per token
+    f16_row = H_V * D * 2        # one of -W, U, Q', Y per token (per value head)
+    kt_row = H_QK * D * 2        # K^T fragments per token (per q/k head)
     out_b = H_V * D * 4
-    prep_b = 2 * qk_b + v_b + 2 * gb_b + 5 * f16_row + gb_b
-    state_b = 5 * f16_row + gb_b + out_b
+    prep_b = 2 * qk_b + v_b + 2 * gb_b + 4 * f16_row + kt_row + gb_b
+    state_b = 4 * f16_row + kt_row + gb_b + out_b
     return {
         "prep": (prep_f, prep_b),
         "state": (state_f, state_b),
@@ -66,11 +67,13 @@ def algorithmic_work():
     }
 
 
-# HBM bytes per launch of the state kernel at T = 4000, from rocprofv3
+# HBM bytes per launch of the prefill kernels at T = 4000, from rocprofv3
 # FETCH_SIZE / WRITE_SIZE runs scaled by a plain 1 GiB copy (fetch x 2.0,
 # write x 1.0); valid only for the kernel source they were taken with.
 MEASURED_TRAFFIC = {
-    "gdn_chunk_state": {"bytes": 201466164, "source_sha256_prefix": "4ca35fe904366b59",
+    "gdn_chunk_prep": {"bytes": 220183347, "source_sha256_prefix": "3cc8df0b1d21bb64",
+                       "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
+    "gdn_chunk_state": {"bytes": 233469747, "source_sha256_prefix": "3cc8df0b1d21bb64",
                         "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
 }
 
