@@ -8,6 +8,9 @@ current stream.  The names mirror the C entry points:
 * ``gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace)``
 * ``gdn_chunk_fwd_stages(..., stage_mask)`` (prep = 1, state with output = 2)
 * ``gdn_chunk_state_slots(n_seqs, total_tokens, h_qk, h_v)``
+* ``gdn_chunk_fwd_segmented_workspace_size(n_seqs, total_tokens, h_qk, h_v, segment_chunks)``
+* ``gdn_chunk_fwd_segmented(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
+  segment_chunks, workspace)``
 * ``gdn_chunk_fwd_snapshots(q, k, v, g, beta, cu_seqlens, initial_state, out,
   final_state, chunk_states, workspace)``
 * ``gdn_recurrent_step(q, k, v, g, beta, n_requests, tokens_per_request, state_in,
@@ -45,6 +48,8 @@ EXPORTED_SYMBOLS = (
     "gdn_chunk_fwd_stages",
     "gdn_chunk_state_slots",
     "gdn_chunk_fwd_snapshots",
+    "gdn_chunk_fwd_segmented_workspace_size",
+    "gdn_chunk_fwd_segmented",
     "gdn_recurrent_step",
     "gdn_recurrent_step_slots",
     "gdn_status_string",
@@ -90,6 +95,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_chunk_state_slots.restype = ctypes.c_int
     lib.gdn_chunk_fwd_snapshots.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, dims_p, vp, sz, vp]
     lib.gdn_chunk_fwd_snapshots.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_segmented_workspace_size.argtypes = [dims_p, c32, ctypes.POINTER(sz)]
+    lib.gdn_chunk_fwd_segmented_workspace_size.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_segmented.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, c32, dims_p, vp, sz, vp]
+    lib.gdn_chunk_fwd_segmented.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [vp, vp, vp, vp, vp, c32, c32, vp, vp, vp, vp, ctypes.c_int, dims_p, vp]
     lib.gdn_recurrent_step.restype = ctypes.c_int
     lib.gdn_recurrent_step_slots.argtypes = [vp, vp, vp, vp, vp, vp, c32, c32, vp, c32, c64, vp, vp, vp,
@@ -198,6 +207,33 @@ def gdn_chunk_fwd_snapshots(q, k, v, g, beta, cu_seqlens, initial_state, out, fi
                                      ctypes.byref(dims), _ptr(workspace), int(workspace_bytes),
                                      _stream(stream, q, out, cu_seqlens))
     _check(lib, st, "gdn_chunk_fwd_snapshots")
+
+
+def gdn_chunk_fwd_segmented_workspace_size(n_seqs: int, total_tokens: int, h_qk: int, h_v: int,
+                                           segment_chunks: int, d_k: int = 128, d_v: int = 128) -> int:
+    lib = load_library()
+    dims = make_dims(n_seqs, total_tokens, h_qk, h_v, d_k, d_v)
+    out = ctypes.c_size_t(0)
+    _check(lib, lib.gdn_chunk_fwd_segmented_workspace_size(ctypes.byref(dims), int(segment_chunks),
+                                                          ctypes.byref(out)),
+           "gdn_chunk_fwd_segmented_workspace_size")
+    return int(out.value)
+
+
+def gdn_chunk_fwd_segmented(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, segment_chunks: int,
+                            workspace, *, dims: Optional[gdn_dims] = None,
+                            workspace_bytes: Optional[int] = None, stream=None) -> None:
+    """Chunked prefill with the recurrence parallel over segments (see include/gdn.h)."""
+    lib = load_library()
+    if dims is None:
+        dims = make_dims(cu_seqlens.shape[0] - 1, q.shape[0], q.shape[1], v.shape[1], q.shape[2], v.shape[2])
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_chunk_fwd_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                     _ptr(initial_state), _ptr(out), _ptr(final_state), int(segment_chunks),
+                                     ctypes.byref(dims), _ptr(workspace), int(workspace_bytes),
+                                     _stream(stream, q, out, cu_seqlens))
+    _check(lib, st, "gdn_chunk_fwd_segmented")
 
 
 def gdn_recurrent_step(q, k, v, g, beta, n_requests: int, tokens_per_request: int,

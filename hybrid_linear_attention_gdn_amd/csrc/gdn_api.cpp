@@ -64,10 +64,15 @@ int64_t n_chunk_slots(const gdn_dims* d) {
 }
 
 struct Layout {
-    size_t w, u, kt, qt, y, dg, junk, total;
+    size_t w, u, kt, qt, y, dg, junk, maps, hstart, total;
 };
 
-Layout workspace_layout(const gdn_dims* d) {
+// Segment slots of the segment-parallel recurrence (see gdn_chunk.hip).
+int64_t n_seg_slots(const gdn_dims* d, int32_t seg_chunks) {
+    return (int64_t)d->n_seqs + n_chunk_slots(d) / seg_chunks + 1;
+}
+
+Layout workspace_layout(const gdn_dims* d, int32_t seg_chunks = 0) {
     const size_t units = (size_t)n_chunk_slots(d) * (size_t)d->n_heads_v;
     Layout L;
     size_t off = 0;
@@ -78,6 +83,12 @@ Layout workspace_layout(const gdn_dims* d) {
     L.y = off;  off += round_up(units * gdn::kUElems * sizeof(gdn::f16));
     L.dg = off; off += round_up(units * gdn::kGElems * sizeof(float));
     L.junk = off; off += round_up(gdn::kJunkBytes);
+    L.maps = L.hstart = off;
+    if (seg_chunks > 0) {
+        const size_t per = (size_t)n_seg_slots(d, seg_chunks) * (size_t)d->n_heads_v * gdn::kDim * gdn::kDim * sizeof(float);
+        L.maps = off;   off += round_up(2 * per);
+        L.hstart = off; off += round_up(per);
+    }
     L.total = off;
     return L;
 }
@@ -133,7 +144,7 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
                           const int32_t* cu_seqlens, const float* initial_state, float* out,
                           float* final_state, float* chunk_states, const gdn_dims* dims,
                           void* workspace, size_t workspace_bytes, int stage_mask, void* stream,
-                          const char* what) {
+                          const char* what, int32_t seg_chunks = 0) {
     if (stage_mask < 1 || stage_mask > 3)
         return fail(GDN_ERR_INVALID_VALUE, "stage_mask = %d is outside 1..3", stage_mask);
     gdn_status s = check_dims(dims);
@@ -151,7 +162,7 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
         GDN_REQUIRE_PTR(beta);
         GDN_REQUIRE_PTR(out);
     }
-    const Layout L = workspace_layout(dims);
+    const Layout L = workspace_layout(dims, seg_chunks);
     if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes required)", L.total);
     if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
         return fail(GDN_ERR_MISALIGNED, "workspace is not 256-byte aligned");
@@ -172,11 +183,20 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
     ws.n_slots = (int)slots;
     ws.group = dims->n_heads_v / dims->n_heads_qk;
 
+    gdn::SegLaunch seg;
+    if (seg_chunks > 0) {
+        const int64_t segslots = n_seg_slots(dims, seg_chunks);
+        if (segslots * dims->n_heads_v > 0x7fffffffLL / 16) return fail(GDN_ERR_INVALID_VALUE, "too many segments");
+        seg.seg_chunks = seg_chunks;
+        seg.n_segslots = (int)segslots;
+        seg.maps = reinterpret_cast<float*>(base + L.maps);
+        seg.hstart = reinterpret_cast<float*>(base + L.hstart);
+    }
     const hipError_t e = gdn::launch_chunk_fwd(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
         g, beta, cu_seqlens, dims->n_seqs, dims->total_tokens, dims->n_heads_qk, dims->n_heads_v,
         initial_state, out, final_state, chunk_states, ws, (int)slots, stage_mask,
-        static_cast<hipStream_t>(stream));
+        seg_chunks > 0 ? &seg : nullptr, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "%s launch: %s", what, hipGetErrorString(e));
     return ok();
 }
@@ -210,6 +230,30 @@ gdn_status gdn_chunk_fwd_snapshots(const void* q, const void* k, const void* v,
         return fail(GDN_ERR_INVALID_VALUE, "chunk_states is NULL");
     return chunk_fwd_impl(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, chunk_states,
                           dims, workspace, workspace_bytes, 3, stream, "gdn_chunk_fwd_snapshots");
+}
+
+gdn_status gdn_chunk_fwd_segmented_workspace_size(const gdn_dims* dims, int32_t segment_chunks, size_t* bytes) {
+    if (!bytes) return fail(GDN_ERR_INVALID_VALUE, "bytes is NULL");
+    if (segment_chunks < 1) return fail(GDN_ERR_INVALID_VALUE, "segment_chunks = %d must be positive", segment_chunks);
+    const gdn_status s = check_dims(dims);
+    if (s != GDN_SUCCESS) return s;
+    *bytes = workspace_layout(dims, segment_chunks).total;
+    return ok();
+}
+
+gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta,
+                                   const int32_t* cu_seqlens,
+                                   const float* initial_state,
+                                   float* out,
+                                   float* final_state,
+                                   int32_t segment_chunks,
+                                   const gdn_dims* dims,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    if (segment_chunks < 1) return fail(GDN_ERR_INVALID_VALUE, "segment_chunks = %d must be positive", segment_chunks);
+    return chunk_fwd_impl(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, nullptr,
+                          dims, workspace, workspace_bytes, 3, stream, "gdn_chunk_fwd_segmented", segment_chunks);
 }
 
 gdn_status gdn_chunk_fwd_stages(const void* q, const void* k, const void* v,

@@ -509,6 +509,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 constexpr int kStages = 3;
 constexpr int kUTile = 4 * 64 * 4;                           // halves of U (or Y) fragments per tile
 constexpr int kCopiesPerChunk = 16 + 16 + 16 + 2 + 2 + 1;    // -W, K^T, Q', U, Y, decay vector
+constexpr int kCopiesPerChunkMap = 16 + 16 + 2 + 1;          // without the output's Q', Y
 
 struct StateStage {
     f16 w[kWElems];
@@ -538,6 +539,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 // One chunk's copies: 1 KB pieces (16 B per lane) of -W, K^T, Q', U and Y,
 // and the 256 B decay vector (4 B per lane).
+template <bool kOut>
 __device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace& ws, size_t vu, size_t ku,
                                            int ct, int lane) {
     const f16* wsrc = ws.w + vu * kWElems;
@@ -550,12 +552,14 @@ __device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace&
     for (int piece = 0; piece < 16; ++piece) {
         __builtin_amdgcn_global_load_lds(wsrc + (piece * 64 + lane) * 8, st.w + piece * 512, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(ksrc + (piece * 64 + lane) * 8, st.k + piece * 512, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(qsrc + (piece * 64 + lane) * 8, st.q + piece * 512, 16, 0, 0);
+        if constexpr (kOut)
+            __builtin_amdgcn_global_load_lds(qsrc + (piece * 64 + lane) * 8, st.q + piece * 512, 16, 0, 0);
     }
 #pragma unroll
     for (int piece = 0; piece < 2; ++piece) {
         __builtin_amdgcn_global_load_lds(usrc + (piece * 64 + lane) * 8, st.u + piece * 512, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(ysrc + (piece * 64 + lane) * 8, st.y + piece * 512, 16, 0, 0);
+        if constexpr (kOut)
+            __builtin_amdgcn_global_load_lds(ysrc + (piece * 64 + lane) * 8, st.y + piece * 512, 16, 0, 0);
     }
     // (the casts keep this 4-byte copy from tripping a code-generation fault
     //  of the ROCm 7.2 compiler in this kernel)
@@ -567,10 +571,10 @@ __device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace&
 // output rows t0 .. t0 + len - 1 of the tile.  out_tile and snap point at
 // column 0 of the tile (row 0 of the chunk).  Rows past len go to the sink so
 // that the number of stores never changes.
-template <bool kSnap>
+template <bool kOut, bool kSnap>
 __device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st, float* out_tile,
                                             size_t row_stride, int len, float* snap, float* junk,
-                                            int lane, int gq, int ln) {
+                                            bool use_u, int lane, int gq, int ln) {
     // incoming chunk state as B fragments (d_k slots)
     f16x8 hb[4];
 #pragma unroll
@@ -581,11 +585,12 @@ __device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st,
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const f16x4 uf = *reinterpret_cast<const f16x4*>(&st.u[(p * 64 + lane) * 4]);
-        const f16x4 yf = *reinterpret_cast<const f16x4*>(&st.y[(p * 64 + lane) * 4]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc[p][e] = static_cast<float>(uf[e]);
-            oacc[p][e] = static_cast<float>(yf[e]);
+        for (int e = 0; e < 4; ++e) acc[p][e] = use_u ? static_cast<float>(uf[e]) : 0.f;
+        if constexpr (kOut) {
+            const f16x4 yf = *reinterpret_cast<const f16x4*>(&st.y[(p * 64 + lane) * 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oacc[p][e] = static_cast<float>(yf[e]);
         }
     }
     f16x8 wa[4][4], qa[4][4];
@@ -594,14 +599,14 @@ __device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st,
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             wa[qq][p] = *reinterpret_cast<const f16x8*>(&st.w[((p * 4 + qq) * 64 + lane) * 8]);
-            qa[qq][p] = *reinterpret_cast<const f16x8*>(&st.q[((p * 4 + qq) * 64 + lane) * 8]);
+            if constexpr (kOut) qa[qq][p] = *reinterpret_cast<const f16x8*>(&st.q[((p * 4 + qq) * 64 + lane) * 8]);
         }
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             acc[p] = mfma_f16(wa[qq][p], hb[qq], acc[p]);
-            oacc[p] = mfma_f16(qa[qq][p], hb[qq], oacc[p]);
+            if constexpr (kOut) oacc[p] = mfma_f16(qa[qq][p], hb[qq], oacc[p]);
         }
     // diag(e^{G_C - G}) U' as B fragments (position slots), the B operand of
     // the update  H <- e^{G_C} H + K^T (diag(e^{G_C - G}) U')
@@ -627,14 +632,16 @@ __device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st,
     for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
         for (int i = 0; i < 8; ++i) H[i] = mfma_f16(ka[qq][i], up[qq], H[i]);
+    if constexpr (kOut) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+        for (int p = 0; p < 4; ++p)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * p + 4 * gq + e;
-            float* d = row < len ? out_tile + (size_t)row * row_stride + ln : junk + lane;
-            *d = oacc[p][e];
-        }
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * p + 4 * gq + e;
+                float* d = row < len ? out_tile + (size_t)row * row_stride + ln : junk + lane;
+                *d = oacc[p][e];
+            }
+    }
     if constexpr (kSnap) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -643,23 +650,84 @@ __device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st,
     }
 }
 
-// Grid: 8 * ceil(U / 8) * 8 workgroups of 128 threads, U = n_seqs * h_v.
-// Workgroup b runs on XCD b % 8 (round-robin dispatch); it takes unit
-// 8 * (m / 8) + b % 8 and column tile m % 8, m = b / 8, so all tiles of a
-// unit share an XCD.
-template <bool kSnap>
+// ---------------------------------------------------------------------------
+// Segments of a sequence (the chunk-parallel affine scan).  A sequence of
+// nch chunks is cut into nseg = max(1, ceil(nch / sc)) segments of sc chunks.
+// Over one segment the recurrence is affine in its incoming state,
+// H_end = Phi H_start + R, and the maps compose: (Phi2, R2) o (Phi1, R1) =
+// (Phi2 Phi1, Phi2 R1 + R2).  Segment s of sequence n has the index
+// seg_base(n) + s, seg_base(n) = n + slot_base(n) / sc; consecutive
+// sequences never overlap and every index is below n + (n + T/64 + 1) / sc + 1.
+// ---------------------------------------------------------------------------
+struct SegArgs {
+    int seg_chunks;          // sc
+    int n_segslots;
+    const float* hstart;     // [segslot][h_v][128][128]: incoming state of segment s >= 1
+    float* maps;             // [segslot][h_v][2][128][128]: Phi, R of segments s < nseg - 1
+};
+
+__device__ __forceinline__ int seg_base(const int32_t* cu, int n, int sc) {
+    return n + slot_base(cu, n) / sc;
+}
+
+__device__ __forceinline__ int seg_count(int nch, int sc) {
+    return max(1, (nch + sc - 1) / sc);
+}
+
+// Map a segment slot to (sequence, segment, segment count); false if unused.
+__device__ __forceinline__ bool resolve_segslot(const int32_t* __restrict__ cu, int n_seqs, int gs, int sc,
+                                                int& seq, int& sg, int& nseg) {
+    int lo = 0, hi = n_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seg_base(cu, mid, sc) <= gs) lo = mid; else hi = mid - 1;
+    }
+    const int nch = (cu[lo + 1] - cu[lo] + kChunk - 1) / kChunk;
+    sg = gs - seg_base(cu, lo, sc);
+    nseg = seg_count(nch, sc);
+    seq = lo;
+    return sg >= 0 && sg < nseg;
+}
+
+enum : int {
+    kModeWhole = 0,          // whole sequences, with the output
+    kModeWholeSnap = 1,      // the same, plus the state after every chunk
+    kModeSegment = 2,        // one segment per workgroup, from its incoming state, with the output
+    kModeMap = 3,            // the affine map (Phi, R) of one segment, no output
+};
+
+// Grid: kTiles * 8 * ceil(U / 8) workgroups of 128 threads; U = n_seqs * h_v
+// for whole sequences, n_segslots * h_v for segments; kTiles = 8 column
+// tiles, or 16 for a map (8 of Phi, 8 of R).  Workgroup b runs on XCD b % 8
+// (round-robin dispatch); it takes unit 8 * (m / kTiles) + b % 8 and tile
+// m % kTiles, m = b / 8, so all tiles of a unit share an XCD.
+template <int kMode>
 __global__ __launch_bounds__(128) void gdn_chunk_state(
     const int32_t* __restrict__ cu, int n_seqs, int h_v,
     const float* s0, float* s_final, float* __restrict__ out, float* __restrict__ chunk_states,
-    ChunkWorkspace ws)
+    ChunkWorkspace ws, SegArgs sa)
 {
+    constexpr bool kOut = kMode != kModeMap;
+    constexpr bool kSnap = kMode == kModeWholeSnap;
+    constexpr int kTiles = kMode == kModeMap ? 16 : 8;
+    constexpr bool kSeg = kMode >= kModeSegment;
     const int b = blockIdx.x;
     const int m = b >> 3;
-    const int unit = ((m >> 3) << 3) + (b & 7);
-    if (unit >= n_seqs * h_v) return;
-    const int ct = m & 7;
-    const int seq = unit / h_v;
-    const int h = unit % h_v;
+    const int unit = ((m / kTiles) << 3) + (b & 7);
+    const int tile = m % kTiles;
+    const int ct = tile & 7;
+    int seq, h, sg = 0, nseg = 1, gs = 0;
+    if constexpr (!kSeg) {
+        if (unit >= n_seqs * h_v) return;
+        seq = unit / h_v;
+        h = unit % h_v;
+    } else {
+        if (unit >= sa.n_segslots * h_v) return;
+        gs = unit / h_v;
+        h = unit % h_v;
+        if (!resolve_segslot(cu, n_seqs, gs, sa.seg_chunks, seq, sg, nseg)) return;
+        if (kMode == kModeMap && sg >= nseg - 1) return;    // the last segment needs no map
+    }
     const int j = h / ws.group;
 
     const int lane = threadIdx.x & 63;
@@ -673,15 +741,30 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
     const int start = cu[seq];
     const int end = cu[seq + 1];
     const int nchunks = (end - start + kChunk - 1) / kChunk;
+    const int c_begin = kSeg ? sg * sa.seg_chunks : 0;
+    const int c_end = kSeg ? min(c_begin + sa.seg_chunks, nchunks) : nchunks;
     const int slot0 = slot_base(cu, seq);
-    const int last = nchunks - 1;
-    auto vidx = [&](int c) { return ws.vunit(slot0 + min(c, last), h); };
-    auto kidx = [&](int c) { return ws.kunit(slot0 + min(c, last), j); };
+    auto vidx = [&](int c) { return ws.vunit(slot0 + min(c, c_end - 1), h); };
+    auto kidx = [&](int c) { return ws.kunit(slot0 + min(c, c_end - 1), j); };
     const size_t sbase = ((size_t)seq * h_v + h) * kDim * kDim;
+    const size_t gbase = ((size_t)gs * h_v + h) * kDim * kDim;
 
     if (compute) {
         f32x4 H[8];
-        if (s0) {
+        if (kMode == kModeMap) {
+            // Phi starts at the identity (tiles 0-7), R at zero (tiles 8-15)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    H[i][e] = (tile < 8 && 16 * i + 4 * gq + e == col) ? 1.f : 0.f;
+        } else if (kSeg && sg > 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    H[i][e] = sa.hstart[gbase + (size_t)(16 * i + 4 * gq + e) * kDim + col];
+        } else if (s0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -692,40 +775,114 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
             for (int i = 0; i < 8; ++i) H[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         __builtin_amdgcn_s_waitcnt(0);
-        if (nchunks > 0) {
-            lds_barrier();                                   // B_0: chunk 0 has landed
-            for (int c = 0; c < nchunks; ++c) {
+        const bool use_u = !(kMode == kModeMap && tile < 8);   // Phi: the homogeneous part
+        if (c_end > c_begin) {
+            lds_barrier();                                   // B_0: the first chunk has landed
+            for (int c = c_begin; c < c_end; ++c) {
                 const int t0 = start + kChunk * c;
                 // tile bases (column 16 ct); each lane adds its column ln
                 float* snap = kSnap ? chunk_states + ((size_t)(slot0 + c) * h_v + h) * kDim * kDim + 16 * ct
                                     : nullptr;
-                state_chunk<kSnap>(H, stage[c % kStages], out + ((size_t)t0 * h_v + h) * kDim + 16 * ct,
-                                   (size_t)h_v * kDim, min(kChunk, end - t0), snap, ws.junk, lane, gq, ln);
+                state_chunk<kOut, kSnap>(H, stage[(c - c_begin) % kStages],
+                                         out + ((size_t)t0 * h_v + h) * kDim + 16 * ct, (size_t)h_v * kDim,
+                                         min(kChunk, end - t0), snap, ws.junk, use_u, lane, gq, ln);
                 lds_barrier();                               // B_{c+1}
             }
         }
-        if (s_final) {
+        if (kMode == kModeMap) {
+            float* dst = sa.maps + (gbase * 2 + (tile < 8 ? 0 : (size_t)kDim * kDim));
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(size_t)(16 * i + 4 * gq + e) * kDim + col] = H[i][e];
+        } else if (s_final && sg == nseg - 1) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     s_final[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col] = H[i][e];
         }
-    } else if (nchunks > 0) {
+    } else if (c_end > c_begin) {
         // copies for chunks past the last one are issued too (clamped, never
         // used) so the number of copies per chunk never changes
-        state_copy(stage[0], ws, vidx(0), kidx(0), ct, lane);
-        state_copy(stage[1], ws, vidx(1), kidx(1), ct, lane);
-        wait_vmcnt<kCopiesPerChunk>();                       // chunk 0 has landed
+        constexpr int kCopies = kOut ? kCopiesPerChunk : kCopiesPerChunkMap;
+        state_copy<kOut>(stage[0], ws, vidx(c_begin), kidx(c_begin), ct, lane);
+        state_copy<kOut>(stage[1], ws, vidx(c_begin + 1), kidx(c_begin + 1), ct, lane);
+        wait_vmcnt<kCopies>();                               // the first chunk has landed
         lds_barrier();                                       // B_0
-        for (int c = 0; c < nchunks; ++c) {
+        for (int c = c_begin; c < c_end; ++c) {
             // between B_c and B_{c+1}: the compute wave works on chunk c
-            state_copy(stage[(c + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), ct, lane);
-            wait_vmcnt<kCopiesPerChunk>();                   // chunk c + 1 has landed
+            state_copy<kOut>(stage[(c - c_begin + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), ct, lane);
+            wait_vmcnt<kCopies>();                           // chunk c + 1 has landed
             lds_barrier();                                   // B_{c+1}
         }
         // drain the copies past the end before the workgroup's LDS goes away
         __builtin_amdgcn_s_waitcnt(0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Scan over segments: the incoming state of segment s + 1 is Phi_s H_s + R_s,
+// in fp32.  One workgroup of 256 threads per (sequence, value head, 16-column
+// tile); Phi_s goes through LDS, the tile's state stays there.  Thread t
+// computes column t % 16 of rows t / 16 + 16 i.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gdn_chunk_seg_scan(
+    const int32_t* __restrict__ cu, int n_seqs, int h_v, const float* s0, SegArgs sa)
+{
+    const int b = blockIdx.x;
+    const int ct = b & 7;
+    const int unit = b >> 3;
+    if (unit >= n_seqs * h_v) return;
+    const int seq = unit / h_v;
+    const int h = unit % h_v;
+    const int nch = (cu[seq + 1] - cu[seq] + kChunk - 1) / kChunk;
+    const int nseg = seg_count(nch, sa.seg_chunks);
+    if (nseg <= 1) return;
+    const int g0 = seg_base(cu, seq, sa.seg_chunks);
+    const int tid = threadIdx.x;
+    const int c = tid & 15;
+    const int r0 = tid >> 4;
+    constexpr int kPS = kDim + 1;                     // padded row of Phi in LDS
+
+    __shared__ float Phi[kDim * kPS];
+    __shared__ float Ht[kDim * 16];
+    const size_t sbase = ((size_t)seq * h_v + h) * kDim * kDim;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = r0 + 16 * i;
+        Ht[r * 16 + c] = s0 ? s0[sbase + (size_t)r * kDim + 16 * ct + c] : 0.f;
+    }
+    for (int sg = 0; sg + 1 < nseg; ++sg) {
+        const size_t mbase = ((size_t)(g0 + sg) * h_v + h) * 2 * kDim * kDim;
+        const float* phi = sa.maps + mbase;
+        const float* rr = sa.maps + mbase + (size_t)kDim * kDim;
+#pragma unroll 4
+        for (int i = 0; i < 16; ++i) {                // 128 x 128 fp32, 16 B per thread per pass
+            const int idx = tid + 256 * i;            // float4 index
+            const int r = idx >> 5, k4 = (idx & 31) * 4;
+            const f32x4 x = *reinterpret_cast<const f32x4*>(phi + (size_t)r * kDim + k4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Phi[r * kPS + k4 + e] = x[e];
+        }
+        __syncthreads();
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = rr[(size_t)(r0 + 16 * i) * kDim + 16 * ct + c];
+        for (int k = 0; k < kDim; ++k) {
+            const float hk = Ht[k * 16 + c];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(Phi[(r0 + 16 * i) * kPS + k], hk, acc[i]);
+        }
+        __syncthreads();                              // every read of Phi and Ht is done
+        float* dst = const_cast<float*>(sa.hstart) + ((size_t)(g0 + sg + 1) * h_v + h) * kDim * kDim;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = r0 + 16 * i;
+            Ht[r * 16 + c] = acc[i];
+            dst[(size_t)r * kDim + 16 * ct + c] = acc[i];
+        }
+        __syncthreads();
     }
 }
 
@@ -737,21 +894,36 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
                             int n_seqs, int64_t total_tokens, int h_qk, int h_v,
                             const float* s0, float* out, float* s_final, float* chunk_states,
                             const ChunkWorkspace& ws, int n_slots, int stage_mask,
-                            hipStream_t stream)
+                            const SegLaunch* seg, hipStream_t stream)
 {
     if ((stage_mask & 1) && total_tokens > 0) {
         hipLaunchKernelGGL(gdn_chunk_prep, dim3(n_slots, h_v), dim3(256), 0, stream,
                            q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws);
     }
     if ((stage_mask & 2) && n_seqs > 0) {
-        const int units = n_seqs * h_v;
-        const dim3 grid(64 * ((units + 7) / 8));
-        if (chunk_states)
-            hipLaunchKernelGGL(gdn_chunk_state<true>, grid, dim3(128), 0, stream,
-                               cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws);
-        else
-            hipLaunchKernelGGL(gdn_chunk_state<false>, grid, dim3(128), 0, stream,
-                               cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws);
+        SegArgs sa = {};
+        if (!seg) {
+            const int units = n_seqs * h_v;
+            const dim3 grid(64 * ((units + 7) / 8));
+            if (chunk_states)
+                hipLaunchKernelGGL(gdn_chunk_state<kModeWholeSnap>, grid, dim3(128), 0, stream,
+                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+            else
+                hipLaunchKernelGGL(gdn_chunk_state<kModeWhole>, grid, dim3(128), 0, stream,
+                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+        } else {
+            sa.seg_chunks = seg->seg_chunks;
+            sa.n_segslots = seg->n_segslots;
+            sa.hstart = seg->hstart;
+            sa.maps = seg->maps;
+            const int units = seg->n_segslots * h_v;
+            hipLaunchKernelGGL(gdn_chunk_state<kModeMap>, dim3(128 * ((units + 7) / 8)), dim3(128), 0, stream,
+                               cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+            hipLaunchKernelGGL(gdn_chunk_seg_scan, dim3(8 * n_seqs * h_v), dim3(256), 0, stream,
+                               cu, n_seqs, h_v, s0, sa);
+            hipLaunchKernelGGL(gdn_chunk_state<kModeSegment>, dim3(64 * ((units + 7) / 8)), dim3(128), 0, stream,
+                               cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+        }
     }
     return hipGetLastError();
 }

@@ -8,14 +8,24 @@
 
 namespace gdn {
 
+// Segment-parallel recurrence: segments of seg_chunks chunks, their affine
+// maps and incoming states in caller memory (sizes from the host).
+struct SegLaunch {
+    int seg_chunks;
+    int n_segslots;
+    float* hstart;      // [n_segslots][h_v][128][128]
+    float* maps;        // [n_segslots][h_v][2][128][128]
+};
+
 // Enqueues the chunked prefill on `stream`: prep (stage bit 0) and the state
-// recurrence with the output (stage bit 1); chunk_states may be null.
+// recurrence with the output (stage bit 1); chunk_states may be null; seg
+// null runs each sequence's recurrence in one workgroup per column tile.
 hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* g, const float* beta, const int32_t* cu,
                             int n_seqs, int64_t total_tokens, int h_qk, int h_v,
                             const float* s0, float* out, float* s_final, float* chunk_states,
                             const ChunkWorkspace& ws, int n_slots, int stage_mask,
-                            hipStream_t stream);
+                            const SegLaunch* seg, hipStream_t stream);
 
 // Enqueues the per-token recurrent update on `stream`.
 hipError_t launch_recurrent_step(const uint16_t* q, const uint16_t* k, const uint16_t* v,

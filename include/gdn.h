@@ -147,6 +147,41 @@ gdn_status gdn_chunk_fwd_snapshots(const void* q, const void* k, const void* v,
                                    void* stream);
 
 /*
+ * Workspace bytes of gdn_chunk_fwd_segmented: gdn_chunk_fwd's plus, per
+ * segment slot and value head, the affine map (2 x 64 KiB) and the incoming
+ * state (64 KiB) of a segment; n_seqs + (n_seqs + floor(T / 64) + 1) /
+ * segment_chunks + 1 segment slots.  Host only.
+ */
+gdn_status gdn_chunk_fwd_segmented_workspace_size(const gdn_dims* dims, int32_t segment_chunks, size_t* bytes);
+
+/*
+ * gdn_chunk_fwd with the inter-chunk recurrence parallel over segments of
+ * segment_chunks chunks (a chunk-parallel affine scan; the pages run the
+ * recurrence serially, "2080 Ti runs Qwen3.8-27B: a vLLM plugin", section 2).
+ * Over a segment the recurrence is affine in its incoming state, H_end = Phi
+ * H_start + R, and such maps compose associatively.  Three launches after
+ * prep: every segment but the last of each sequence computes (Phi, R) from
+ * its own chunks; an fp32 scan over segments chains them into each segment's
+ * incoming state; every segment then runs the state recurrence with the
+ * output from its incoming state.  About three times the recurrence's work,
+ * for parallelism when one long sequence gives fewer workgroups than CUs.
+ * Results agree with gdn_chunk_fwd to the same tolerance (not bitwise).
+ *  segment_chunks  >= 1; GDN_ERR_INVALID_VALUE otherwise.
+ *  workspace       at least gdn_chunk_fwd_segmented_workspace_size bytes.
+ * Other arguments, results and errors as gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta,
+                                   const int32_t* cu_seqlens,
+                                   const float* initial_state,
+                                   float* out,
+                                   float* final_state,
+                                   int32_t segment_chunks,
+                                   const gdn_dims* dims,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * Runs only the selected stages of gdn_chunk_fwd, for callers that time or
  * schedule the stages one by one.  stage_mask bits: 1 = gdn_chunk_prep,
  * 2 = gdn_chunk_state with the output (3 = gdn_chunk_fwd).  The second stage

@@ -283,3 +283,26 @@ def test_snapshots_rejects_bad_arguments(lib):
     assert snap_call(lib, dims(n=2, T=130, dk=64, dv=64)) == gdn.GDN_ERR_NOT_SUPPORTED
     assert snap_call(lib, dims(n=0, T=0), cs=None, q=None, k=None, v=None, g=None, beta=None, cu=None,
                      out=None, ws=None, wsb=0) == gdn.GDN_SUCCESS
+
+
+def test_segmented_workspace_and_arguments(lib):
+    d = dims(n=2, T=1000, hqk=16, hv=32)
+    base = ws_size(lib, d)[1]
+    for sc in (1, 4, 64):
+        b = ctypes.c_size_t(0)
+        assert lib.gdn_chunk_fwd_segmented_workspace_size(ctypes.byref(d), sc, ctypes.byref(b)) == gdn.GDN_SUCCESS
+        segslots = 2 + (2 + 1000 // 64 + 1) // sc + 1
+        per = segslots * 32 * 128 * 128 * 4
+        assert base + 3 * per <= b.value < base + 3 * per + 3 * 256
+    b = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_segmented_workspace_size(ctypes.byref(d), 0, ctypes.byref(b)) == gdn.GDN_ERR_INVALID_VALUE
+    assert lib.gdn_chunk_fwd_segmented_workspace_size(ctypes.byref(d), 4, None) == gdn.GDN_ERR_INVALID_VALUE
+    need = ctypes.c_size_t(0)
+    lib.gdn_chunk_fwd_segmented_workspace_size(ctypes.byref(d), 4, ctypes.byref(need))
+    call = lambda sc, wsb, **o: lib.gdn_chunk_fwd_segmented(
+        o.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, sc, ctypes.byref(d), FAKE, wsb, None)
+    assert call(0, need.value) == gdn.GDN_ERR_INVALID_VALUE
+    assert call(-3, need.value) == gdn.GDN_ERR_INVALID_VALUE
+    assert call(4, need.value - 1) == gdn.GDN_ERR_WORKSPACE
+    assert call(4, need.value, q=None) == gdn.GDN_ERR_INVALID_VALUE
+    assert call(4, need.value, q=MIS) == gdn.GDN_ERR_MISALIGNED

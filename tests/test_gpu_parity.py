@@ -301,3 +301,69 @@ def test_chunk_snapshots_prefill_4000_sampled():
         print(f"[result] snapshot chunk {c}: state rel-L2 {e:.3e}", flush=True)
         assert e <= STATE_TOL
     np.testing.assert_array_equal(cs_np[62], fin.cpu().numpy()[0])
+
+
+# ------------------------------------------------------------ segment-parallel recurrence (affine scan)
+
+def _segmented(x, d, sc, initial_state="default"):
+    import hybrid_linear_attention_gdn_amd as gdn
+    s0 = d.s0 if isinstance(initial_state, str) else initial_state
+    nbytes = gdn.gdn_chunk_fwd_segmented_workspace_size(x.n_seqs, x.total_tokens, x.h_qk, x.h_v, sc)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")     # fp16 / fp32 NaN poison
+    out = torch.full((x.total_tokens, x.h_v, x.d_v), float("nan"), dtype=torch.float32, device="cuda")
+    fin = torch.full((x.n_seqs, x.h_v, 128, 128), float("nan"), dtype=torch.float32, device="cuda")
+    gdn.gdn_chunk_fwd_segmented(d.q, d.k, d.v, d.g, d.beta, d.cu, s0, out, fin, sc, ws)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+@pytest.mark.parametrize("sc", [1, 3, 4, 16, 1000])
+def test_segmented_varlen(sc):
+    """Segments of sc chunks (1 = every chunk its own segment; 1000 = one
+    segment) over a ragged batch with an empty sequence and random states."""
+    lengths = [300, 1, 700, 64, 0, 200]
+    x = gi.make_inputs(lengths, 2, 4, 128, 128, seed=90 + sc, state_std=0.02)
+    _print_case(f"segmented_varlen_sc{sc}", x)
+    d = DevInputs(x)
+    out, fin = _segmented(x, d, sc)
+    ro, rf, _ = oracle.forward_inputs(x, precision="f64")
+    o, f = out.cpu().numpy(), fin.cpu().numpy()
+    assert np.isfinite(o).all() and np.isfinite(f).all()
+    eo, ef = rel_l2(o, ro), rel_l2(f, rf)
+    print(f"[result] segmented sc={sc}: out {eo:.3e} state {ef:.3e}", flush=True)
+    assert eo <= OUT_TOL and ef <= STATE_TOL
+    # the empty sequence keeps its initial state exactly
+    np.testing.assert_array_equal(f[4], x.initial_state[4])
+
+
+def test_segmented_prefill_4000():
+    x = gi.prefill_4000()
+    _print_case("segmented_prefill_4000", x)
+    d = DevInputs(x)
+    out, fin = _segmented(x, d, 8)
+    ro, rf, _ = oracle.forward_inputs(x, precision="f64")
+    eo, ef = rel_l2(out.cpu().numpy(), ro), rel_l2(fin.cpu().numpy(), rf)
+    print(f"[result] segmented prefill_4000 sc=8: out {eo:.3e} state {ef:.3e}", flush=True)
+    assert eo <= OUT_TOL and ef <= STATE_TOL
+
+
+def test_segmented_long_131072_sampled():
+    """Full-size long context, 8 segments of 256 chunks: sampled value heads
+    against the oracle over the whole sequence, and the whole output against
+    the serial GPU path."""
+    x = gi.long_131072()
+    _print_case("segmented_long_131072", x)
+    d = DevInputs(x)
+    out, fin = _segmented(x, d, 256)
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(fin).all())
+    heads = [0, 1, 22, 23]
+    qk = sorted({h // 2 for h in heads})
+    ro, rf, _ = oracle.forward(x.q[:, qk], x.k[:, qk], x.v[:, heads], x.g[:, heads], x.beta[:, heads],
+                               x.cu_seqlens, None, precision="f64", n_threads=4)
+    eo = rel_l2(out[:, heads].cpu().numpy(), ro)
+    ef = rel_l2(fin[:, heads].cpu().numpy(), rf)
+    print(f"[result] segmented long_131072 heads {heads}: out {eo:.3e} state {ef:.3e}", flush=True)
+    assert eo <= OUT_TOL and ef <= STATE_TOL
+    so, sf = chunk_fwd(d, poison=False)
+    assert rel_l2(out.cpu().numpy(), so.cpu().numpy()) <= OUT_TOL
+    assert rel_l2(fin.cpu().numpy(), sf.cpu().numpy()) <= STATE_TOL
