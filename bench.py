@@ -120,6 +120,52 @@ def cpu_baseline(x, budget_s: float):
                       f"{t:.1f} s wall, threads over (sequence, value head)"}
 
 
+def long_context(args):
+    """The long-context workload (one sequence of 131072 tokens, g = -softplus(N(-2, 1))):
+    gdn_chunk_fwd against gdn_chunk_fwd_segmented at a few segment lengths, at the
+    configuration's 32 value / 16 q-k heads and at a two-way head shard (16 / 8)."""
+    import torch
+
+    import gdn_inputs as gi
+    import hybrid_linear_attention_gdn_amd as gdn
+
+    dev, bf, T = torch.device("cuda:0"), torch.bfloat16, 131072
+    reps = max(1, min(args.steps, 5))
+    res = {"metric": "long-context prefill ms per layer (T=131072)", "unit": "ms", "shapes": []}
+    for hqk, hv in ((16, 32), (8, 16)):
+        x = gi.make_inputs([T], hqk, hv, D, D, seed=0, g_mean=-2.0, name=f"long_{T}_hv{hv}_hqk{hqk}")
+        q = torch.from_numpy(x.q).to(dev, bf)
+        k = torch.from_numpy(x.k).to(dev, bf)
+        v = torch.from_numpy(x.v).to(dev, bf)
+        g = torch.from_numpy(x.g).to(dev)
+        beta = torch.from_numpy(x.beta).to(dev)
+        cu = torch.from_numpy(x.cu_seqlens).to(dev)
+        out = torch.empty((T, hv, D), device=dev)
+        fin = torch.empty((1, hv, D, D), device=dev)
+        ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(1, T, hqk, hv), dtype=torch.uint8, device=dev)
+        row = {"workload": x.name}
+
+        def timed(fn):
+            fn()
+            return time_launches(fn, reps, torch) * 1e3
+
+        row["serial_ms"] = timed(lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, cu, None, out, fin, ws))
+        row["serial_prep_ms"] = timed(lambda: gdn.gdn_chunk_fwd_stages(q, k, v, g, beta, cu, None, out, fin, ws, 1))
+        row["serial_state_ms"] = timed(lambda: gdn.gdn_chunk_fwd_stages(q, k, v, g, beta, cu, None, out, fin, ws, 2))
+        del ws
+        for sc in (1024, 512, 256):
+            wss = torch.empty(gdn.gdn_chunk_fwd_segmented_workspace_size(1, T, hqk, hv, sc),
+                              dtype=torch.uint8, device=dev)
+            row[f"segmented_sc{sc}_ms"] = timed(
+                lambda: gdn.gdn_chunk_fwd_segmented(q, k, v, g, beta, cu, None, out, fin, sc, wss))
+            del wss
+        row["tokens_per_s_serial"] = T / (row["serial_ms"] * 1e-3)
+        res["shapes"].append(row)
+        del q, k, v, out
+        torch.cuda.empty_cache()
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,7 +176,13 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 5 plain device-to-device copies of BYTES bytes (reference for "
                          "the HBM byte counters) and exit")
+    ap.add_argument("--long", action="store_true",
+                    help="only time the long-context prefill (T=131072) serially and segment-parallel "
+                         "(gdn_chunk_fwd_segmented) at 32/16 and 16/8 heads, print one JSON line and exit")
     args = ap.parse_args()
+    if args.long:
+        long_context(args)
+        return
     if args.copy_calibration:
         import torch
         src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda")
