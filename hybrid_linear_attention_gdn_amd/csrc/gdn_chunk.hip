@@ -489,35 +489,38 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 
 // ---------------------------------------------------------------------------
 // Stage 2: inter-chunk state recurrence with the output.  One workgroup of
-// two waves per (sequence, value head, 16-column tile), specialised:
-//   * the compute wave keeps the tile's 128 x 16 slice of the state in
+// three waves per (sequence, value head, 16-column tile), specialised:
+//   * the chain wave keeps the tile's 128 x 16 slice of the state in
 //     accumulator registers (8 tiles of 16 d_k rows) for the whole sequence.
-//     Per chunk it reads operand fragments from LDS and runs 48 matrix-core
-//     products: U' = U - W H0 and H_C = e^{G_C} H0 + K^T D U' (the chain
-//     from chunk to chunk), and the tile's output O = Y + Q' H0, which needs
-//     only the incoming state (Q' = diag(e^G) Q - P W and Y = P U come from
-//     the prep stage).  It stores O (and, when asked for, the state after the
-//     chunk) straight to global memory and never waits on memory itself;
+//     Per chunk it reads -W, U, K^T and the decay vector from LDS and runs the
+//     32 matrix-core products of U' = U - W H0 and H_C = e^{G_C} H0 +
+//     K^T D U', the dependency from chunk to chunk.  It then hands the new
+//     state, rounded to fp16 as the B operand of (Q' H0), to the output wave
+//     through a double-buffered 4 KB LDS slot;
+//   * the output wave computes the tile's O = Y + Q' H0 one chunk behind the
+//     chain, on its own SIMD (Q' = diag(e^G) Q - P W and Y = P U come from the
+//     prep stage), loads Y one chunk ahead straight into registers and stores
+//     O to global memory;
 //   * the copy wave issues direct global-to-LDS copies of -W, K^T, Q', the
-//     tile's U and Y and the decay vector into a ring of three stages, two
-//     chunks ahead, and touches the operands of the chunk two beyond those
-//     into L2.
+//     tile's U and the decay vector into a ring of three stages, two chunks
+//     ahead, and touches the operands of the chunk two beyond those into L2.
 // The waves meet at one barrier per chunk.  The copy wave issues a fixed
 // number of copies per chunk, so one memory-counter wait makes a stage ready
 // before that barrier.  The eight tiles of a head run on one XCD so that its
-// L2 serves the shared fragments.
+// L2 serves the shared fragments.  Without the output (an affine map) the
+// output wave idles at the barriers.
 // ---------------------------------------------------------------------------
 constexpr int kStages = 3;
 constexpr int kUTile = 4 * 64 * 4;                           // halves of U (or Y) fragments per tile
-constexpr int kCopiesPerChunk = 16 + 16 + 16 + 2 + 2 + 1;    // -W, K^T, Q', U, Y, decay vector
-constexpr int kCopiesPerChunkMap = 16 + 16 + 2 + 1;          // without the output's Q', Y
+constexpr int kHbElems = 4 * 64 * 8;                         // halves of the state's four B fragments
+constexpr int kCopiesPerChunk = 16 + 16 + 16 + 2 + 1;        // -W, K^T, Q', U, decay vector
+constexpr int kCopiesPerChunkMap = 16 + 16 + 2 + 1;          // without the output's Q'
 
 struct StateStage {
     f16 w[kWElems];
     f16 k[kKtElems];
     f16 q[kQtElems];
     f16 u[kUTile];
-    f16 y[kUTile];
     float dg[kChunk];         // e^{G_C - G_r} (r < 63), e^{G_C} in entry 63
 };
 
@@ -538,8 +541,8 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// One chunk's copies: 1 KB pieces (16 B per lane) of -W, K^T, Q', U and Y,
-// and the 256 B decay vector (4 B per lane).
+// One chunk's copies: 1 KB pieces (16 B per lane) of -W, K^T, Q' and U, and
+// the 256 B decay vector (4 B per lane).
 template <bool kOut>
 __device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace& ws, size_t vu, size_t ku,
                                            int ct, int lane) {
@@ -547,7 +550,6 @@ __device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace&
     const f16* ksrc = ws.kt + ku * kKtElems;
     const f16* qsrc = ws.qt + vu * kQtElems;
     const f16* usrc = ws.u + vu * kUElems + (size_t)ct * kUTile;
-    const f16* ysrc = ws.y + vu * kUElems + (size_t)ct * kUTile;
     const float* gsrc = ws.dg + vu * kGElems;
 #pragma unroll
     for (int piece = 0; piece < 16; ++piece) {
@@ -557,11 +559,8 @@ __device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace&
             __builtin_amdgcn_global_load_lds(qsrc + (piece * 64 + lane) * 8, st.q + piece * 512, 16, 0, 0);
     }
 #pragma unroll
-    for (int piece = 0; piece < 2; ++piece) {
+    for (int piece = 0; piece < 2; ++piece)
         __builtin_amdgcn_global_load_lds(usrc + (piece * 64 + lane) * 8, st.u + piece * 512, 16, 0, 0);
-        if constexpr (kOut)
-            __builtin_amdgcn_global_load_lds(ysrc + (piece * 64 + lane) * 8, st.y + piece * 512, 16, 0, 0);
-    }
     // (the casts keep this 4-byte copy from tripping a code-generation fault
     //  of the ROCm 7.2 compiler in this kernel)
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gsrc + lane), reinterpret_cast<void*>(st.dg),
@@ -583,47 +582,34 @@ __device__ __forceinline__ void state_touch(const ChunkWorkspace& ws, size_t vu,
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off), reinterpret_cast<void*>(sink), 4, 0, 0);
 }
 
-// One chunk for the compute wave's 16 columns: the recurrence step and the
-// output rows t0 .. t0 + len - 1 of the tile.  out_tile and snap point at
-// column 0 of the tile (row 0 of the chunk).  Rows past len go to the sink so
-// that the number of stores never changes.
-template <bool kOut, bool kSnap>
-__device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st, float* out_tile,
-                                            size_t row_stride, int len, float* snap, float* junk,
+// The chain wave's step for one chunk: H0 (fp32 accumulators H, its fp16 B
+// fragments hb) -> H_C, and hb <- fp16 B fragments of H_C.
+template <bool kSnap>
+__device__ __forceinline__ void chain_chunk(f32x4 (&H)[8], f16x8 (&hb)[4], const StateStage& st, float* snap,
                                             bool use_u, int lane, int gq, int ln) {
-    // incoming chunk state as B fragments (d_k slots)
-    f16x8 hb[4];
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) hb[qq] = cat_to_f16(H[2 * qq], H[2 * qq + 1]);
-    // U' = U + (-W) H0 and O = Y + Q' H0: all 32 fragments are read before
-    // the burst, whose 8 accumulator chains interleave
-    f32x4 acc[4], oacc[4];
+    // U' = U + (-W) H0: all 16 fragments are read before the burst, whose 4
+    // accumulator chains interleave
+    f32x4 acc[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const f16x4 uf = *reinterpret_cast<const f16x4*>(&st.u[(p * 64 + lane) * 4]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[p][e] = use_u ? static_cast<float>(uf[e]) : 0.f;
-        if constexpr (kOut) {
-            const f16x4 yf = *reinterpret_cast<const f16x4*>(&st.y[(p * 64 + lane) * 4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) oacc[p][e] = static_cast<float>(yf[e]);
-        }
     }
-    f16x8 wa[4][4], qa[4][4];
+    f16x8 wa[4][4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            wa[qq][p] = *reinterpret_cast<const f16x8*>(&st.w[((p * 4 + qq) * 64 + lane) * 8]);
-            if constexpr (kOut) qa[qq][p] = *reinterpret_cast<const f16x8*>(&st.q[((p * 4 + qq) * 64 + lane) * 8]);
-        }
+        for (int p = 0; p < 4; ++p) wa[qq][p] = *reinterpret_cast<const f16x8*>(&st.w[((p * 4 + qq) * 64 + lane) * 8]);
+    f16x8 ka[2][8];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ka[qq][i] = *reinterpret_cast<const f16x8*>(&st.k[((i * 2 + qq) * 64 + lane) * 8]);
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            acc[p] = mfma_f16(wa[qq][p], hb[qq], acc[p]);
-            if constexpr (kOut) oacc[p] = mfma_f16(qa[qq][p], hb[qq], oacc[p]);
-        }
+        for (int p = 0; p < 4; ++p) acc[p] = mfma_f16(wa[qq][p], hb[qq], acc[p]);
     // diag(e^{G_C - G}) U' as B fragments (position slots), the B operand of
     // the update  H <- e^{G_C} H + K^T (diag(e^{G_C - G}) U')
 #pragma unroll
@@ -635,11 +621,6 @@ __device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st,
     f16x8 up[2];
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) up[qq] = cat_to_f16(acc[2 * qq], acc[2 * qq + 1]);
-    f16x8 ka[2][8];
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ka[qq][i] = *reinterpret_cast<const f16x8*>(&st.k[((i * 2 + qq) * 64 + lane) * 8]);
     const float gam = st.dg[kChunk - 1];
 #pragma unroll
     for (int i = 0; i < 8; ++i) H[i] *= gam;
@@ -648,22 +629,60 @@ __device__ __forceinline__ void state_chunk(f32x4 (&H)[8], const StateStage& st,
     for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
         for (int i = 0; i < 8; ++i) H[i] = mfma_f16(ka[qq][i], up[qq], H[i]);
-    if constexpr (kOut) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * p + 4 * gq + e;
-                float* d = row < len ? out_tile + (size_t)row * row_stride + ln : junk + lane;
-                *d = oacc[p][e];
-            }
-    }
+    for (int qq = 0; qq < 4; ++qq) hb[qq] = cat_to_f16(H[2 * qq], H[2 * qq + 1]);
     if constexpr (kSnap) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) snap[(size_t)(16 * i + 4 * gq + e) * kDim + ln] = H[i][e];
     }
+}
+
+// The tile's Y fragments of one chunk, as four 8-byte register loads.
+struct YFrag {
+    f16x4 f[4];
+};
+
+__device__ __forceinline__ YFrag load_y(const ChunkWorkspace& ws, size_t vu, int ct, int lane) {
+    const f16* src = ws.y + vu * kUElems + (size_t)ct * kUTile;
+    YFrag y;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) y.f[p] = *reinterpret_cast<const f16x4*>(src + (p * 64 + lane) * 4);
+    return y;
+}
+
+// The output wave's step for one chunk: O = Y + Q' H0 for the output rows
+// t0 .. t0 + len - 1 of the tile.  out_tile points at column 0 of the tile
+// (row 0 of the chunk); rows past len go to the sink so that the number of
+// stores never changes.
+__device__ __forceinline__ void out_chunk(const StateStage& st, const f16* hsrc, const YFrag& y, float* out_tile,
+                                          size_t row_stride, int len, float* junk, int lane, int gq, int ln) {
+    f16x8 hb[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) hb[qq] = *reinterpret_cast<const f16x8*>(&hsrc[(qq * 64 + lane) * 8]);
+    f32x4 oacc[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[p][e] = static_cast<float>(y.f[p][e]);
+    f16x8 qa[4][4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) qa[qq][p] = *reinterpret_cast<const f16x8*>(&st.q[((p * 4 + qq) * 64 + lane) * 8]);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) oacc[p] = mfma_f16(qa[qq][p], hb[qq], oacc[p]);
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * p + 4 * gq + e;
+            float* d = row < len ? out_tile + (size_t)row * row_stride + ln : junk + lane;
+            *d = oacc[p][e];
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -712,13 +731,17 @@ enum : int {
     kModeMap = 3,            // the affine map (Phi, R) of one segment, no output
 };
 
-// Grid: kTiles * 8 * ceil(U / 8) workgroups of 128 threads; U = n_seqs * h_v
-// for whole sequences, n_segslots * h_v for segments; kTiles = 8 column
-// tiles, or 16 for a map (8 of Phi, 8 of R).  Workgroup b runs on XCD b % 8
-// (round-robin dispatch); it takes unit 8 * (m / kTiles) + b % 8 and tile
-// m % kTiles, m = b / 8, so all tiles of a unit share an XCD.
+// Threads of a state workgroup: chain, output and copy waves; an affine map
+// has no output wave.
+__host__ __device__ constexpr int state_threads(int mode) { return mode == kModeMap ? 128 : 192; }
+
+// Grid: kTiles * 8 * ceil(U / 8) workgroups; U = n_seqs * h_v for whole
+// sequences, n_segslots * h_v for segments; kTiles = 8 column tiles, or 16
+// for a map (8 of Phi, 8 of R).  Workgroup b runs on XCD b % 8 (round-robin
+// dispatch); it takes unit 8 * (m / kTiles) + b % 8 and tile m % kTiles,
+// m = b / 8, so all tiles of a unit share an XCD.
 template <int kMode>
-__global__ __launch_bounds__(128) void gdn_chunk_state(
+__global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
     const int32_t* __restrict__ cu, int n_seqs, int h_v,
     const float* s0, float* s_final, float* __restrict__ out, float* __restrict__ chunk_states,
     ChunkWorkspace ws, SegArgs sa)
@@ -727,6 +750,7 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
     constexpr bool kSnap = kMode == kModeWholeSnap;
     constexpr int kTiles = kMode == kModeMap ? 16 : 8;
     constexpr bool kSeg = kMode >= kModeSegment;
+    constexpr int kCopyRole = state_threads(kMode) / 64 - 1;
     const int b = blockIdx.x;
     const int m = b >> 3;
     const int unit = ((m / kTiles) << 3) + (b & 7);
@@ -747,12 +771,13 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
     const int j = h / ws.group;
 
     const int lane = threadIdx.x & 63;
-    const bool compute = threadIdx.x < 64;
+    const int role = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0 chain, 1 output, last copy
     const int gq = lane >> 4;
     const int ln = lane & 15;
     const int col = 16 * ct + ln;
 
     __shared__ __attribute__((aligned(16))) StateStage stage[kStages];
+    __shared__ __attribute__((aligned(16))) f16 hbuf[2][kHbElems];  // chain -> output: fp16 state
     __shared__ __attribute__((aligned(16))) float touch_sink[64];   // target of the L2 touches, never read
 
     const int start = cu[seq];
@@ -766,7 +791,7 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
     const size_t sbase = ((size_t)seq * h_v + h) * kDim * kDim;
     const size_t gbase = ((size_t)gs * h_v + h) * kDim * kDim;
 
-    if (compute) {
+    if (role == 0) {
         f32x4 H[8];
         if (kMode == kModeMap) {
             // Phi starts at the identity (tiles 0-7), R at zero (tiles 8-15)
@@ -792,17 +817,28 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
             for (int i = 0; i < 8; ++i) H[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         __builtin_amdgcn_s_waitcnt(0);
+        f16x8 hb[4];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) hb[qq] = cat_to_f16(H[2 * qq], H[2 * qq + 1]);
         const bool use_u = !(kMode == kModeMap && tile < 8);   // Phi: the homogeneous part
         if (c_end > c_begin) {
+            if constexpr (kOut) {
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<f16x8*>(&hbuf[0][(qq * 64 + lane) * 8]) = hb[qq];
+            }
             lds_barrier();                                   // B_0: the first chunk has landed
             for (int c = c_begin; c < c_end; ++c) {
-                const int t0 = start + kChunk * c;
-                // tile bases (column 16 ct); each lane adds its column ln
+                // tile base (column 16 ct); each lane adds its column ln
                 float* snap = kSnap ? chunk_states + ((size_t)(slot0 + c) * h_v + h) * kDim * kDim + 16 * ct
                                     : nullptr;
-                state_chunk<kOut, kSnap>(H, stage[(c - c_begin) % kStages],
-                                         out + ((size_t)t0 * h_v + h) * kDim + 16 * ct, (size_t)h_v * kDim,
-                                         min(kChunk, end - t0), snap, ws.junk, use_u, lane, gq, ln);
+                chain_chunk<kSnap>(H, hb, stage[(c - c_begin) % kStages], snap, use_u, lane, gq, ln);
+                if constexpr (kOut) {
+                    // the output wave reads this in the next interval; the
+                    // buffer it reads now is the other one
+                    f16* hdst = hbuf[(c - c_begin + 1) & 1];
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<f16x8*>(&hdst[(qq * 64 + lane) * 8]) = hb[qq];
+                }
                 lds_barrier();                               // B_{c+1}
             }
         }
@@ -819,6 +855,22 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
                 for (int e = 0; e < 4; ++e)
                     s_final[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col] = H[i][e];
         }
+    } else if (role < kCopyRole) {
+        // the output wave: chunk c's output in the interval between B_c and
+        // B_{c+1}, from the state the chain wave handed over before B_c
+        if (c_end > c_begin) {
+            YFrag y = load_y(ws, vidx(c_begin), ct, lane);
+            lds_barrier();                                   // B_0
+            for (int c = c_begin; c < c_end; ++c) {
+                const YFrag ynext = load_y(ws, vidx(c + 1), ct, lane);   // clamped past the end
+                const int t0 = start + kChunk * c;
+                out_chunk(stage[(c - c_begin) % kStages], hbuf[(c - c_begin) & 1], y,
+                          out + ((size_t)t0 * h_v + h) * kDim + 16 * ct, (size_t)h_v * kDim,
+                          min(kChunk, end - t0), ws.junk, lane, gq, ln);
+                y = ynext;
+                lds_barrier();                               // B_{c+1}
+            }
+        }
     } else if (c_end > c_begin) {
         // copies for chunks past the last one are issued too (clamped, never
         // used) so the number of copies per chunk never changes
@@ -828,7 +880,7 @@ __global__ __launch_bounds__(128) void gdn_chunk_state(
         wait_vmcnt<kCopies>();                               // the first chunk has landed
         lds_barrier();                                       // B_0
         for (int c = c_begin; c < c_end; ++c) {
-            // between B_c and B_{c+1}: the compute wave works on chunk c
+            // between B_c and B_{c+1}: the chain and output waves work on chunk c
             state_copy<kOut>(stage[(c - c_begin + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), ct, lane);
             state_touch(ws, vidx(c + 4), kidx(c + 4), ct, lane, touch_sink);
             wait_vmcnt<kCopies + 1>();                           // chunk c + 1 has landed
@@ -924,10 +976,10 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
             const int units = n_seqs * h_v;
             const dim3 grid(64 * ((units + 7) / 8));
             if (chunk_states)
-                hipLaunchKernelGGL(gdn_chunk_state<kModeWholeSnap>, grid, dim3(128), 0, stream,
+                hipLaunchKernelGGL(gdn_chunk_state<kModeWholeSnap>, grid, dim3(state_threads(kModeWholeSnap)), 0, stream,
                                    cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
             else
-                hipLaunchKernelGGL(gdn_chunk_state<kModeWhole>, grid, dim3(128), 0, stream,
+                hipLaunchKernelGGL(gdn_chunk_state<kModeWhole>, grid, dim3(state_threads(kModeWhole)), 0, stream,
                                    cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
         } else {
             sa.seg_chunks = seg->seg_chunks;
@@ -935,11 +987,11 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
             sa.hstart = seg->hstart;
             sa.maps = seg->maps;
             const int units = seg->n_segslots * h_v;
-            hipLaunchKernelGGL(gdn_chunk_state<kModeMap>, dim3(128 * ((units + 7) / 8)), dim3(128), 0, stream,
+            hipLaunchKernelGGL(gdn_chunk_state<kModeMap>, dim3(128 * ((units + 7) / 8)), dim3(state_threads(kModeMap)), 0, stream,
                                cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
             hipLaunchKernelGGL(gdn_chunk_seg_scan, dim3(8 * n_seqs * h_v), dim3(256), 0, stream,
                                cu, n_seqs, h_v, s0, sa);
-            hipLaunchKernelGGL(gdn_chunk_state<kModeSegment>, dim3(64 * ((units + 7) / 8)), dim3(128), 0, stream,
+            hipLaunchKernelGGL(gdn_chunk_state<kModeSegment>, dim3(64 * ((units + 7) / 8)), dim3(state_threads(kModeSegment)), 0, stream,
                                cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
         }
     }
