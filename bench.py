@@ -44,22 +44,24 @@ def algorithmic_work():
 
     Flops count each causal (triangular) product at half and the K K^T / Q K^T
     Grams once per q/k head; they are the layer's terms, each assigned to the
-    kernel that evaluates it: prep takes the decay, Grams, UT transform, W, U
-    and the intra-chunk output term (as P U); the state kernel the recurrence
-    (W H, K^T U') and Q S.  The extra P W product of the Q' = diag(e^G) Q - P W
-    rewrite is not counted.  Bytes count each tensor of a kernel's interface
-    read or written once: bf16 inputs, fp32 g / beta / decay vector / output,
-    fp16 intermediates (-W, U, Q', Y per value head, K^T per q/k head)."""
-    prep_f = H_V * (C * (D + D) + C * C / 3) + H_QK * (C * D) + H_QK * (C * D) + H_V * (C * D)
-    state_f = H_V * (4 * D * D) + H_V * (2 * D * D)
+    kernel that evaluates it: prep takes the decay, Grams, UT transform, W and
+    U; the state kernel the recurrence (W H, K^T U') and the output (Q S and
+    P U').  Bytes count each tensor of a kernel's interface read or written
+    once: bf16 inputs, fp32 g / beta / decay vectors / output, fp16
+    intermediates (-W, U and the six nonzero 16x32 blocks of P per value head,
+    K^T and Q fragments per q/k head)."""
+    prep_f = H_V * (C * (D + D) + C * C / 3) + H_QK * (C * D) + H_QK * (C * D)
+    state_f = H_V * (4 * D * D) + H_V * (2 * D * D) + H_V * (C * D)
     qk_b = H_QK * D * 2          # one of q or k, bf16
     v_b = H_V * D * 2
-    gb_b = H_V * 4               # one of g, beta or the e^G vector
-    f16_row = H_V * D * 2        # one of -W, U, Q', Y per token (per value head)
-    kt_row = H_QK * D * 2        # K^T fragments per token (per q/k head)
+    gb_b = H_V * 4               # one of g, beta, or one fp32 value per token and value head
+    f16_row = H_V * D * 2        # one of -W, U per token (per value head)
+    p_row = H_V * 6 * 16 * 32 * 2 // C   # P's six nonzero blocks per token (per value head)
+    qk_row = H_QK * D * 2        # K^T or Q fragments per token (per q/k head)
     out_b = H_V * D * 4
-    prep_b = 2 * qk_b + v_b + 2 * gb_b + 4 * f16_row + kt_row + gb_b
-    state_b = 4 * f16_row + kt_row + gb_b + out_b
+    work = 2 * f16_row + p_row + 2 * qk_row + 2 * gb_b   # the intermediates, each way
+    prep_b = 2 * qk_b + v_b + 2 * gb_b + work
+    state_b = work + out_b
     return {
         "prep": (prep_f, prep_b),
         "state": (state_f, state_b),

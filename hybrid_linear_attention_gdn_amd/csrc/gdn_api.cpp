@@ -64,7 +64,7 @@ int64_t n_chunk_slots(const gdn_dims* d) {
 }
 
 struct Layout {
-    size_t w, u, kt, qt, y, dg, junk, maps, hstart, total;
+    size_t w, u, p, dg, kt, qf, junk, maps, hstart, total;
 };
 
 // Segment slots of the segment-parallel recurrence (see gdn_chunk.hip).
@@ -76,12 +76,13 @@ Layout workspace_layout(const gdn_dims* d, int32_t seg_chunks = 0) {
     const size_t units = (size_t)n_chunk_slots(d) * (size_t)d->n_heads_v;
     Layout L;
     size_t off = 0;
+    const size_t qk_units = (size_t)n_chunk_slots(d) * (size_t)d->n_heads_qk;
     L.w = off;  off += round_up(units * gdn::kWElems * sizeof(gdn::f16));
     L.u = off;  off += round_up(units * gdn::kUElems * sizeof(gdn::f16));
-    L.kt = off; off += round_up((size_t)n_chunk_slots(d) * (size_t)d->n_heads_qk * gdn::kKtElems * sizeof(gdn::f16));
-    L.qt = off; off += round_up(units * gdn::kQtElems * sizeof(gdn::f16));
-    L.y = off;  off += round_up(units * gdn::kUElems * sizeof(gdn::f16));
+    L.p = off;  off += round_up(units * gdn::kPElems * sizeof(gdn::f16));
     L.dg = off; off += round_up(units * gdn::kGElems * sizeof(float));
+    L.kt = off; off += round_up(qk_units * gdn::kKtElems * sizeof(gdn::f16));
+    L.qf = off; off += round_up(qk_units * gdn::kQfElems * sizeof(gdn::f16));
     L.junk = off; off += round_up(gdn::kJunkBytes);
     L.maps = L.hstart = off;
     if (seg_chunks > 0) {
@@ -175,10 +176,10 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
     gdn::ChunkWorkspace ws;
     ws.w = reinterpret_cast<gdn::f16*>(base + L.w);
     ws.u = reinterpret_cast<gdn::f16*>(base + L.u);
-    ws.kt = reinterpret_cast<gdn::f16*>(base + L.kt);
-    ws.qt = reinterpret_cast<gdn::f16*>(base + L.qt);
-    ws.y = reinterpret_cast<gdn::f16*>(base + L.y);
+    ws.p = reinterpret_cast<gdn::f16*>(base + L.p);
     ws.dg = reinterpret_cast<float*>(base + L.dg);
+    ws.kt = reinterpret_cast<gdn::f16*>(base + L.kt);
+    ws.qf = reinterpret_cast<gdn::f16*>(base + L.qf);
     ws.junk = reinterpret_cast<float*>(base + L.junk);
     ws.n_slots = (int)slots;
     ws.group = dims->n_heads_v / dims->n_heads_qk;

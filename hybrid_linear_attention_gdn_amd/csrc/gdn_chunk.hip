@@ -73,7 +73,6 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     __shared__ __attribute__((aligned(16))) float Bs[kChunk];  // beta
     __shared__ __attribute__((aligned(16))) float Bw[kChunk];  // beta e^G
     __shared__ float Gs[kChunk];     // G
-    __shared__ float Es[kChunk];     // e^G
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -132,8 +131,8 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
         Gs[lane] = x;
         Bs[lane] = bt;
         Bw[lane] = bt * eg;
-        Es[lane] = eg;
         ws.dg[wsidx * kGElems + lane] = lane == kChunk - 1 ? eg : dc;
+        ws.dg[wsidx * kGElems + kChunk + lane] = eg;
     }
     __syncthreads();
 
@@ -189,9 +188,9 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 
     // ---- P = M o (Q K^T) for row tile p = wave, M_rs = e^{G_r - G_s} (s <= r),
     //      computed as (K Q^T)[s][r] so that the accumulators of two position
-    //      tiles stack into the A fragment of P over position slots.  Kept in
-    //      registers until the output-side products at the end.
-    f16x8 pf[2];
+    //      tiles stack into the A fragment of P over position slots, which is
+    //      how the output stage reads it: block (p, qq) at 2 p (p < 2) or
+    //      2 + 2 (p - 2) + qq; blocks (0, 1) and (1, 1) are zero and not stored.
     {
         const int p = wave;
         const int r = 16 * p + ln;
@@ -214,8 +213,11 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
                 dt[jt][e] = (sp <= r) ? exp_f(gr - Gs[sp]) * dt[jt][e] : 0.f;
             }
         }
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) pf[qq] = cat_to_f16(dt[2 * qq], dt[2 * qq + 1]);
+        f16* pdst = ws.p + wsidx * kPElems;
+        const int f0 = p < 2 ? p : 2 * p - 2;
+        *reinterpret_cast<f16x8*>(pdst + ((size_t)f0 * 64 + lane) * 8) = cat_to_f16(dt[0], dt[1]);
+        if (p >= 2)
+            *reinterpret_cast<f16x8*>(pdst + ((size_t)(f0 + 1) * 64 + lane) * 8) = cat_to_f16(dt[2], dt[3]);
     }
 
     __syncthreads();                                  // K rows in the A buffer are consumed
@@ -337,12 +339,11 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     }
     __syncthreads();
 
-    // ---- W = TW K (twice: dims on lanes and positions on lanes) and U = TU V.
-    //      Wave w owns d_k tiles 2w, 2w+1 and d_v tiles 2w, 2w+1.
-    f32x4 w2acc[4][2];   // W[pos tile p][d_k tile 2w + a]: d_k on lanes
-    f32x4 uacc[4][2];    // U[pos tile p][d_v tile 2w + a]: d_v on lanes
+    // ---- W = TW K (positions on lanes) and U = TU V (d_v on lanes).  Wave w
+    //      owns d_k tiles 2w, 2w+1 and d_v tiles 2w, 2w+1.
     {
         f32x4 wacc[2][4];   // W^T[d_k tile 2w + a][pos tile p]: positions on lanes
+        f32x4 uacc[4][2];   // U[pos tile p][d_v tile 2w + a]: d_v on lanes
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -378,111 +379,48 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
             const f16x8 fr = cat_to_f16(-wacc[0][p], -wacc[1][p]);
             *reinterpret_cast<f16x8*>(wdst + ((p * 4 + wave) * 64 + lane) * 8) = fr;
         }
-    }
-    // the same W with d_k on lanes, for P W below (a second pass keeps the
-    // register peak down)
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) w2acc[p][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-        f16x8 kfr[2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-            kfr[a] = *reinterpret_cast<const f16x8*>(KsT + tsw(16 * (2 * wave + a) + ln, 32 * kt + 8 * gq));
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const f16x8 tw = *reinterpret_cast<const f16x8*>(TWs + (16 * p + ln) * kTS + 32 * kt + 8 * gq);
-#pragma unroll
-            for (int a = 0; a < 2; ++a) w2acc[p][a] = mfma_f16(tw, kfr[a], w2acc[p][a]);
-        }
-    }
-    // U accumulator fragments (ct, p)
-    f16* udst = ws.u + wsidx * kUElems;
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-        const int ct = 2 * wave + a;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            f16x4 fr;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) fr[e] = static_cast<f16>(uacc[p][a][e]);
-            *reinterpret_cast<f16x4*>(udst + ((ct * 4 + p) * 64 + lane) * 4) = fr;
-        }
-    }
-
-    // ---- exchange P: every wave needs all four row tiles
-    __syncthreads();                                  // K, V, TW, TU are consumed
-    f16* Pl = KsT;                                    // [p][qq][lane][8]
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
-        *reinterpret_cast<f16x8*>(Pl + ((wave * 2 + qq) * 64 + lane) * 8) = pf[qq];
-    uint16_t* Qr = reinterpret_cast<uint16_t*>(VsT);  // Q rows [pos][dim] bf16, chunk-swizzled
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        *reinterpret_cast<u16x8*>(Qr + rsw(16 * wave + ln, 4 * kk + gq)) = __builtin_bit_cast(u16x8, qf[kk]);
-    __syncthreads();
-    // Q~^T = diag(e^G) Q, transposed, for this wave's d_k tiles in accumulator
-    // layout: d_k rows 16 (2w + a) + 4 gq + e, query row 16 p + ln
-    u16x4 qraw[2][4];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int dd = 16 * (2 * wave + a) + 4 * gq;
-            qraw[a][p] = *reinterpret_cast<const u16x4*>(Qr + rsw(16 * p + ln, dd >> 3) + (dd & 7));
-        }
-    f16x8 pa[4][2];
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) pa[p][qq] = *reinterpret_cast<const f16x8*>(Pl + ((p * 2 + qq) * 64 + lane) * 8);
-
-    // ---- Q' = diag(e^G) Q - P W as A fragments over the chunk state's d_k
-    //      slots: (Q')^T = Q~^T + (-W)^T P^T, d_k tiles 2w, 2w+1 = K-step w.
-    {
-        f16x8 wn[2][2];   // -W with d_k on lanes, positions on slots [a][pos step]
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int qq = 0; qq < 2; ++qq) wn[a][qq] = cat_to_f16(-w2acc[2 * qq][a], -w2acc[2 * qq + 1][a]);
-        f16* qdst = ws.qt + wsidx * kQtElems;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const float er = Es[16 * p + ln];
-            f32x4 acc[2];
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[a][e] = bf16_to_f32(qraw[a][p][e]) * er;
-#pragma unroll
-                for (int qq = 0; qq < 2; ++qq) acc[a] = mfma_f16(wn[a][qq], pa[p][qq], acc[a]);
-            }
-            *reinterpret_cast<f16x8*>(qdst + ((p * 4 + wave) * 64 + lane) * 8) = cat_to_f16(acc[0], acc[1]);
-        }
-    }
-    // ---- Y = P U in the output tile's accumulator layout (ct, p)
-    {
-        f16x8 ub[2][2];   // U with d_v on lanes, positions on slots [a][pos step]
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int qq = 0; qq < 2; ++qq) ub[a][qq] = cat_to_f16(uacc[2 * qq][a], uacc[2 * qq + 1][a]);
-        f16* ydst = ws.y + wsidx * kUElems;
+        // U accumulator fragments (ct, p)
+        f16* udst = ws.u + wsidx * kUElems;
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
             const int ct = 2 * wave + a;
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int qq = 0; qq < 2; ++qq) acc = mfma_f16(pa[p][qq], ub[a][qq], acc);
                 f16x4 fr;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) fr[e] = static_cast<f16>(acc[e]);
-                *reinterpret_cast<f16x4*>(ydst + ((ct * 4 + p) * 64 + lane) * 4) = fr;
+                for (int e = 0; e < 4; ++e) fr[e] = static_cast<f16>(uacc[p][a][e]);
+                *reinterpret_cast<f16x4*>(udst + ((ct * 4 + p) * 64 + lane) * 4) = fr;
             }
+        }
+    }
+
+    // ---- Q as A fragments over the chunk state's d_k slots, (p, qq = wave),
+    //      for the output stage's Q H0; the value heads of a q/k head share
+    //      them and the first one writes them.  The rows go through LDS (in
+    //      the K^T space, free once the products above have read it) because
+    //      a lane's slots span two 16-dim runs held by different lanes.
+    if (h % ws.group == 0) {
+        __syncthreads();                              // every read of K^T is done
+        uint16_t* Qr = reinterpret_cast<uint16_t*>(KsT);   // [pos][dim] bf16, chunk-swizzled
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            *reinterpret_cast<u16x8*>(Qr + rsw(16 * wave + ln, 4 * kk + gq)) = __builtin_bit_cast(u16x8, qf[kk]);
+        __syncthreads();
+        f16* qdst = ws.qf + ws.kunit(slot, j) * kQfElems;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int row = 16 * p + ln;
+            const int d0 = 32 * wave + 4 * gq;        // slots 0..3
+            const int d1 = d0 + 16;                   // slots 4..7
+            const u16x4 lo = *reinterpret_cast<const u16x4*>(Qr + rsw(row, d0 >> 3) + (d0 & 7));
+            const u16x4 hi = *reinterpret_cast<const u16x4*>(Qr + rsw(row, d1 >> 3) + (d1 & 7));
+            f16x8 fr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                fr[e] = static_cast<f16>(bf16_to_f32(lo[e]));
+                fr[e + 4] = static_cast<f16>(bf16_to_f32(hi[e]));
+            }
+            *reinterpret_cast<f16x8*>(qdst + ((p * 4 + wave) * 64 + lane) * 8) = fr;
         }
     }
 }
@@ -492,36 +430,37 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 // three waves per (sequence, value head, 16-column tile), specialised:
 //   * the chain wave keeps the tile's 128 x 16 slice of the state in
 //     accumulator registers (8 tiles of 16 d_k rows) for the whole sequence.
-//     Per chunk it reads -W, U, K^T and the decay vector from LDS and runs the
-//     32 matrix-core products of U' = U - W H0 and H_C = e^{G_C} H0 +
-//     K^T D U', the dependency from chunk to chunk.  It then hands the new
-//     state, rounded to fp16 as the B operand of (Q' H0), to the output wave
-//     through a double-buffered 4 KB LDS slot;
-//   * the output wave computes the tile's O = Y + Q' H0 one chunk behind the
-//     chain, on its own SIMD (Q' = diag(e^G) Q - P W and Y = P U come from the
-//     prep stage), loads Y one chunk ahead straight into registers and stores
-//     O to global memory;
-//   * the copy wave issues direct global-to-LDS copies of -W, K^T, Q', the
-//     tile's U and the decay vector into a ring of three stages, two chunks
-//     ahead, and touches the operands of the chunk two beyond those into L2.
+//     Per chunk it runs the 32 matrix-core products of U' = U - W H0 and
+//     H_C = e^{G_C} H0 + K^T D U', the dependency from chunk to chunk (-W,
+//     K^T and the decay vector from LDS, its U fragments by register loads
+//     one chunk ahead), and hands U' and the new state, rounded to fp16 as B
+//     operands, to the output wave through double-buffered LDS slots;
+//   * the output wave forms O = diag(e^G) (Q H0) + P U' on its own SIMD:
+//     the Q H0 half in the interval of the chunk (Q fragments and e^G from
+//     the stage), the P U' half one interval later, when U' has been handed
+//     over (P by register loads one chunk ahead); it stores O to global
+//     memory;
+//   * the copy wave issues direct global-to-LDS copies of -W, K^T, Q and the
+//     decay vectors into a ring of three stages, two chunks ahead, and
+//     touches the operands of the chunk two beyond those into L2.
 // The waves meet at one barrier per chunk.  The copy wave issues a fixed
 // number of copies per chunk, so one memory-counter wait makes a stage ready
 // before that barrier.  The eight tiles of a head run on one XCD so that its
-// L2 serves the shared fragments.  Without the output (an affine map) the
-// output wave idles at the barriers.
+// L2 serves the shared fragments.  An affine map has no output: its
+// workgroups have a chain and a copy wave only.
 // ---------------------------------------------------------------------------
 constexpr int kStages = 3;
-constexpr int kUTile = 4 * 64 * 4;                           // halves of U (or Y) fragments per tile
+constexpr int kUTile = 4 * 64 * 4;                           // halves of U fragments per column tile
 constexpr int kHbElems = 4 * 64 * 8;                         // halves of the state's four B fragments
-constexpr int kCopiesPerChunk = 16 + 16 + 16 + 2 + 1;        // -W, K^T, Q', U, decay vector
-constexpr int kCopiesPerChunkMap = 16 + 16 + 2 + 1;          // without the output's Q'
+constexpr int kUbElems = 2 * 64 * 8;                         // halves of U''s two B fragments
+constexpr int kCopiesPerChunk = 16 + 16 + 16 + 2;            // -W, K^T, Q, decay vectors
+constexpr int kCopiesPerChunkMap = 16 + 16 + 2;              // without the output's Q
 
 struct StateStage {
     f16 w[kWElems];
     f16 k[kKtElems];
-    f16 q[kQtElems];
-    f16 u[kUTile];
-    float dg[kChunk];         // e^{G_C - G_r} (r < 63), e^{G_C} in entry 63
+    f16 q[kQfElems];
+    float dg[kGElems];        // e^{G_C - G_r} (r < 63) and e^{G_C} in entry 63; then e^{G_r}
 };
 
 // s_waitcnt with vmcnt = N and the other counters left alone (gfx9 encoding).
@@ -541,15 +480,14 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// One chunk's copies: 1 KB pieces (16 B per lane) of -W, K^T, Q' and U, and
-// the 256 B decay vector (4 B per lane).
+// One chunk's copies: 1 KB pieces (16 B per lane) of -W, K^T and Q, and the
+// two 256 B decay vectors (4 B per lane).
 template <bool kOut>
 __device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace& ws, size_t vu, size_t ku,
-                                           int ct, int lane) {
+                                           int lane) {
     const f16* wsrc = ws.w + vu * kWElems;
     const f16* ksrc = ws.kt + ku * kKtElems;
-    const f16* qsrc = ws.qt + vu * kQtElems;
-    const f16* usrc = ws.u + vu * kUElems + (size_t)ct * kUTile;
+    const f16* qsrc = ws.qf + ku * kQfElems;
     const float* gsrc = ws.dg + vu * kGElems;
 #pragma unroll
     for (int piece = 0; piece < 16; ++piece) {
@@ -558,17 +496,16 @@ __device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace&
         if constexpr (kOut)
             __builtin_amdgcn_global_load_lds(qsrc + (piece * 64 + lane) * 8, st.q + piece * 512, 16, 0, 0);
     }
+    // (the casts keep these 4-byte copies from tripping a code-generation
+    //  fault of the ROCm 7.2 compiler in this kernel)
 #pragma unroll
-    for (int piece = 0; piece < 2; ++piece)
-        __builtin_amdgcn_global_load_lds(usrc + (piece * 64 + lane) * 8, st.u + piece * 512, 16, 0, 0);
-    // (the casts keep this 4-byte copy from tripping a code-generation fault
-    //  of the ROCm 7.2 compiler in this kernel)
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gsrc + lane), reinterpret_cast<void*>(st.dg),
-                                     4, 0, 0);
+    for (int half = 0; half < 2; ++half)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gsrc + kChunk * half + lane),
+                                         reinterpret_cast<void*>(st.dg + kChunk * half), 4, 0, 0);
 }
 
 // Touch one chunk's operands into L2 two chunks before their copies: the
-// 384 cache lines of -W, K^T and Q' are split over the 8 column tiles of a
+// 384 cache lines of -W, K^T and Q are split over the 8 column tiles of a
 // head, 48 lines each, one 4-byte direct-to-LDS copy per lane (lanes past 48
 // repeat a line) into a sink nobody reads.  A direct copy, unlike a register
 // load, is invisible to the compiler's counter waits, so the copy wave's own
@@ -578,24 +515,49 @@ __device__ __forceinline__ void state_touch(const ChunkWorkspace& ws, size_t vu,
                                             float* sink) {
     const int line = ct * 48 + min(lane, 47);
     const int arr = line >> 7, off = (line & 127) * 64;          // halves
-    const f16* base = arr == 0 ? ws.w + vu * kWElems : arr == 1 ? ws.kt + ku * kKtElems : ws.qt + vu * kQtElems;
+    const f16* base = arr == 0 ? ws.w + vu * kWElems : arr == 1 ? ws.kt + ku * kKtElems : ws.qf + ku * kQfElems;
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off), reinterpret_cast<void*>(sink), 4, 0, 0);
 }
 
+// The tile's U fragments of one chunk, as four 8-byte register loads.
+struct UFrag {
+    f16x4 f[4];
+};
+
+__device__ __forceinline__ UFrag load_u(const ChunkWorkspace& ws, size_t vu, int ct, int lane) {
+    const f16* src = ws.u + vu * kUElems + (size_t)ct * kUTile;
+    UFrag u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) u.f[p] = *reinterpret_cast<const f16x4*>(src + (p * 64 + lane) * 4);
+    return u;
+}
+
+// P's six nonzero A fragments of one chunk, as six 16-byte register loads.
+struct PFrag {
+    f16x8 f[6];
+};
+
+__device__ __forceinline__ PFrag load_p(const ChunkWorkspace& ws, size_t vu, int lane) {
+    const f16* src = ws.p + vu * kPElems;
+    PFrag pf;
+#pragma unroll
+    for (int f = 0; f < 6; ++f) pf.f[f] = *reinterpret_cast<const f16x8*>(src + (f * 64 + lane) * 8);
+    return pf;
+}
+
 // The chain wave's step for one chunk: H0 (fp32 accumulators H, its fp16 B
-// fragments hb) -> H_C, and hb <- fp16 B fragments of H_C.
-template <bool kSnap>
-__device__ __forceinline__ void chain_chunk(f32x4 (&H)[8], f16x8 (&hb)[4], const StateStage& st, float* snap,
-                                            bool use_u, int lane, int gq, int ln) {
-    // U' = U + (-W) H0: all 16 fragments are read before the burst, whose 4
+// fragments hb) -> H_C, and hb <- fp16 B fragments of H_C.  With the output,
+// U' goes to ub and H_C's fragments to hd for the output wave.
+template <bool kOut, bool kSnap>
+__device__ __forceinline__ void chain_chunk(f32x4 (&H)[8], f16x8 (&hb)[4], const StateStage& st, const UFrag& u,
+                                            f16* ub, f16* hd, float* snap, bool use_u, int lane, int gq, int ln) {
+    // U' = U + (-W) H0: the fragments are read before the burst, whose 4
     // accumulator chains interleave
     f32x4 acc[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const f16x4 uf = *reinterpret_cast<const f16x4*>(&st.u[(p * 64 + lane) * 4]);
+    for (int p = 0; p < 4; ++p)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[p][e] = use_u ? static_cast<float>(uf[e]) : 0.f;
-    }
+        for (int e = 0; e < 4; ++e) acc[p][e] = use_u ? static_cast<float>(u.f[p][e]) : 0.f;
     f16x8 wa[4][4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
@@ -610,6 +572,11 @@ __device__ __forceinline__ void chain_chunk(f32x4 (&H)[8], f16x8 (&hb)[4], const
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
         for (int p = 0; p < 4; ++p) acc[p] = mfma_f16(wa[qq][p], hb[qq], acc[p]);
+    if constexpr (kOut) {
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+            *reinterpret_cast<f16x8*>(&ub[(qq * 64 + lane) * 8]) = cat_to_f16(acc[2 * qq], acc[2 * qq + 1]);
+    }
     // diag(e^{G_C - G}) U' as B fragments (position slots), the B operand of
     // the update  H <- e^{G_C} H + K^T (diag(e^{G_C - G}) U')
 #pragma unroll
@@ -631,6 +598,10 @@ __device__ __forceinline__ void chain_chunk(f32x4 (&H)[8], f16x8 (&hb)[4], const
         for (int i = 0; i < 8; ++i) H[i] = mfma_f16(ka[qq][i], up[qq], H[i]);
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) hb[qq] = cat_to_f16(H[2 * qq], H[2 * qq + 1]);
+    if constexpr (kOut) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<f16x8*>(&hd[(qq * 64 + lane) * 8]) = hb[qq];
+    }
     if constexpr (kSnap) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -639,50 +610,55 @@ __device__ __forceinline__ void chain_chunk(f32x4 (&H)[8], f16x8 (&hb)[4], const
     }
 }
 
-// The tile's Y fragments of one chunk, as four 8-byte register loads.
-struct YFrag {
-    f16x4 f[4];
-};
+// The output is formed transposed, O^T = H0^T Q^T + U'^T P^T, so that an
+// accumulator lane holds 4 consecutive columns of one output row (a 16-byte
+// store) instead of 4 rows of one column.  The operands are the same
+// registers: an A and a B fragment share one lane layout, so the stacked
+// state and U' fragments serve as H0^T and U'^T, and the Q and P fragments
+// as Q^T and P^T.  oacc[p] holds output rows 16 p + ln, columns 4 gq .. +3
+// of the tile.
 
-__device__ __forceinline__ YFrag load_y(const ChunkWorkspace& ws, size_t vu, int ct, int lane) {
-    const f16* src = ws.y + vu * kUElems + (size_t)ct * kUTile;
-    YFrag y;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) y.f[p] = *reinterpret_cast<const f16x4*>(src + (p * 64 + lane) * 4);
-    return y;
-}
-
-// The output wave's step for one chunk: O = Y + Q' H0 for the output rows
-// t0 .. t0 + len - 1 of the tile.  out_tile points at column 0 of the tile
-// (row 0 of the chunk); rows past len go to the sink so that the number of
-// stores never changes.
-__device__ __forceinline__ void out_chunk(const StateStage& st, const f16* hsrc, const YFrag& y, float* out_tile,
-                                          size_t row_stride, int len, float* junk, int lane, int gq, int ln) {
+// The output wave's first half of a chunk: diag(e^G) (Q H0) into oacc.
+__device__ __forceinline__ void out_begin(f32x4 (&oacc)[4], const StateStage& st, const f16* hsrc, int lane, int ln) {
     f16x8 hb[4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) hb[qq] = *reinterpret_cast<const f16x8*>(&hsrc[(qq * 64 + lane) * 8]);
-    f32x4 oacc[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) oacc[p][e] = static_cast<float>(y.f[p][e]);
     f16x8 qa[4][4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
         for (int p = 0; p < 4; ++p) qa[qq][p] = *reinterpret_cast<const f16x8*>(&st.q[((p * 4 + qq) * 64 + lane) * 8]);
 #pragma unroll
+    for (int p = 0; p < 4; ++p) oacc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) oacc[p] = mfma_f16(qa[qq][p], hb[qq], oacc[p]);
+        for (int p = 0; p < 4; ++p) oacc[p] = mfma_f16(hb[qq], qa[qq][p], oacc[p]);
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+    for (int p = 0; p < 4; ++p) oacc[p] *= st.dg[kChunk + 16 * p + ln];
+}
+
+// The output wave's second half: + P U', then the stores of the output rows
+// t0 .. t0 + len - 1 of the tile.  out_tile points at column 0 of the tile
+// (row 0 of the chunk); rows past len go to the sink so that the number of
+// stores never changes.
+__device__ __forceinline__ void out_end(f32x4 (&oacc)[4], const PFrag& pf, const f16* usrc, float* out_tile,
+                                        size_t row_stride, int len, float* junk, int lane, int gq, int ln) {
+    f16x8 ua[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * p + 4 * gq + e;
-            float* d = row < len ? out_tile + (size_t)row * row_stride + ln : junk + lane;
-            *d = oacc[p][e];
-        }
+    for (int qq = 0; qq < 2; ++qq) ua[qq] = *reinterpret_cast<const f16x8*>(&usrc[(qq * 64 + lane) * 8]);
+    oacc[0] = mfma_f16(ua[0], pf.f[0], oacc[0]);
+    oacc[1] = mfma_f16(ua[0], pf.f[1], oacc[1]);
+    oacc[2] = mfma_f16(ua[0], pf.f[2], oacc[2]);
+    oacc[3] = mfma_f16(ua[0], pf.f[4], oacc[3]);
+    oacc[2] = mfma_f16(ua[1], pf.f[3], oacc[2]);
+    oacc[3] = mfma_f16(ua[1], pf.f[5], oacc[3]);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int row = 16 * p + ln;
+        float* d = row < len ? out_tile + (size_t)row * row_stride + 4 * gq : junk + 4 * lane;
+        *reinterpret_cast<f32x4*>(d) = oacc[p];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -778,6 +754,7 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
 
     __shared__ __attribute__((aligned(16))) StateStage stage[kStages];
     __shared__ __attribute__((aligned(16))) f16 hbuf[2][kHbElems];  // chain -> output: fp16 state
+    __shared__ __attribute__((aligned(16))) f16 ubuf[2][kUbElems];  // chain -> output: fp16 U'
     __shared__ __attribute__((aligned(16))) float touch_sink[64];   // target of the L2 touches, never read
 
     const int start = cu[seq];
@@ -826,19 +803,18 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<f16x8*>(&hbuf[0][(qq * 64 + lane) * 8]) = hb[qq];
             }
+            UFrag un = load_u(ws, vidx(c_begin), ct, lane);
             lds_barrier();                                   // B_0: the first chunk has landed
             for (int c = c_begin; c < c_end; ++c) {
+                const UFrag uc = un;
+                un = load_u(ws, vidx(c + 1), ct, lane);       // clamped past the end
                 // tile base (column 16 ct); each lane adds its column ln
                 float* snap = kSnap ? chunk_states + ((size_t)(slot0 + c) * h_v + h) * kDim * kDim + 16 * ct
                                     : nullptr;
-                chain_chunk<kSnap>(H, hb, stage[(c - c_begin) % kStages], snap, use_u, lane, gq, ln);
-                if constexpr (kOut) {
-                    // the output wave reads this in the next interval; the
-                    // buffer it reads now is the other one
-                    f16* hdst = hbuf[(c - c_begin + 1) & 1];
-#pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<f16x8*>(&hdst[(qq * 64 + lane) * 8]) = hb[qq];
-                }
+                // U'(c) and H0(c + 1) for the output wave; the buffers it
+                // reads in this interval are the other ones
+                chain_chunk<kOut, kSnap>(H, hb, stage[(c - c_begin) % kStages], uc, ubuf[(c - c_begin) & 1],
+                                         hbuf[(c - c_begin + 1) & 1], snap, use_u, lane, gq, ln);
                 lds_barrier();                               // B_{c+1}
             }
         }
@@ -856,32 +832,42 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
                     s_final[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col] = H[i][e];
         }
     } else if (role < kCopyRole) {
-        // the output wave: chunk c's output in the interval between B_c and
-        // B_{c+1}, from the state the chain wave handed over before B_c
+        // the output wave: Q H0 of chunk c between B_c and B_{c+1}, from the
+        // state the chain wave handed over before B_c; P U' of chunk c one
+        // interval later, from the U' handed over before B_{c+1}.  P comes by
+        // register loads one chunk ahead.
         if (c_end > c_begin) {
-            YFrag y = load_y(ws, vidx(c_begin), ct, lane);
+            PFrag pn = load_p(ws, vidx(c_begin), lane);
+            PFrag pc;
+            f32x4 oacc[4];
             lds_barrier();                                   // B_0
             for (int c = c_begin; c < c_end; ++c) {
-                const YFrag ynext = load_y(ws, vidx(c + 1), ct, lane);   // clamped past the end
-                const int t0 = start + kChunk * c;
-                out_chunk(stage[(c - c_begin) % kStages], hbuf[(c - c_begin) & 1], y,
-                          out + ((size_t)t0 * h_v + h) * kDim + 16 * ct, (size_t)h_v * kDim,
-                          min(kChunk, end - t0), ws.junk, lane, gq, ln);
-                y = ynext;
+                if (c > c_begin) {
+                    const int t0 = start + kChunk * (c - 1);
+                    out_end(oacc, pc, ubuf[(c - 1 - c_begin) & 1],
+                            out + ((size_t)t0 * h_v + h) * kDim + 16 * ct, (size_t)h_v * kDim,
+                            min(kChunk, end - t0), ws.junk, lane, gq, ln);
+                }
+                pc = pn;
+                pn = load_p(ws, vidx(c + 1), lane);           // clamped past the end
+                out_begin(oacc, stage[(c - c_begin) % kStages], hbuf[(c - c_begin) & 1], lane, ln);
                 lds_barrier();                               // B_{c+1}
             }
+            const int t0 = start + kChunk * (c_end - 1);
+            out_end(oacc, pc, ubuf[(c_end - 1 - c_begin) & 1], out + ((size_t)t0 * h_v + h) * kDim + 16 * ct,
+                    (size_t)h_v * kDim, min(kChunk, end - t0), ws.junk, lane, gq, ln);
         }
     } else if (c_end > c_begin) {
         // copies for chunks past the last one are issued too (clamped, never
         // used) so the number of copies per chunk never changes
         constexpr int kCopies = kOut ? kCopiesPerChunk : kCopiesPerChunkMap;
-        state_copy<kOut>(stage[0], ws, vidx(c_begin), kidx(c_begin), ct, lane);
-        state_copy<kOut>(stage[1], ws, vidx(c_begin + 1), kidx(c_begin + 1), ct, lane);
+        state_copy<kOut>(stage[0], ws, vidx(c_begin), kidx(c_begin), lane);
+        state_copy<kOut>(stage[1], ws, vidx(c_begin + 1), kidx(c_begin + 1), lane);
         wait_vmcnt<kCopies>();                               // the first chunk has landed
         lds_barrier();                                       // B_0
         for (int c = c_begin; c < c_end; ++c) {
             // between B_c and B_{c+1}: the chain and output waves work on chunk c
-            state_copy<kOut>(stage[(c - c_begin + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), ct, lane);
+            state_copy<kOut>(stage[(c - c_begin + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), lane);
             state_touch(ws, vidx(c + 4), kidx(c + 4), ct, lane, touch_sink);
             wait_vmcnt<kCopies + 1>();                           // chunk c + 1 has landed
             lds_barrier();                                   // B_{c+1}

@@ -39,15 +39,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // in matrix-core fragment order.
 constexpr size_t kWElems = 16 * 64 * 8;    // -W, A fragments [p][qq][lane][8]
 constexpr size_t kUElems = 8 * 4 * 64 * 4;  // U, accumulator fragments [ct][p][lane][4]
-// K^T as A fragments of the state update [d_k tile][pos step][lane][8], one
-// per (chunk slot, q/k head)
+// P = M o (Q K^T), A fragments over positions of its six nonzero (row tile,
+// K-step) blocks (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+constexpr size_t kPElems = 6 * 64 * 8;
+// decay vectors: e^{G_C - G_r} for r < 63 (the factor of row 63 is 1) with
+// e^{G_C} in entry 63, then e^{G_r} for r = 0..63
+constexpr size_t kGElems = 128;
+// Per (chunk slot, q/k head): K^T as A fragments of the state update
+// [d_k tile][pos step][lane][8], and Q as A fragments over d_k [p][qq][lane][8]
 constexpr size_t kKtElems = 8 * 2 * 64 * 8;
-// Q' = diag(e^G) Q - (M o Q K^T) W, A fragments over d_k [p][qq][lane][8]
-constexpr size_t kQtElems = 4 * 4 * 64 * 8;
-// Y = (M o Q K^T) U shares U's accumulator-fragment layout and size (kUElems)
-// decay vector: e^{G_C - G_r} for r < 63 (the factor of row 63 is 1), and
-// e^{G_C} in entry 63
-constexpr size_t kGElems = 64;
+constexpr size_t kQfElems = 4 * 4 * 64 * 8;
 constexpr size_t kJunkBytes = 1024;         // sink for the lanes of masked-off stores
 
 // Workspace regions are head-major: unit (slot, head) sits at head * n_slots
@@ -56,16 +57,16 @@ constexpr size_t kJunkBytes = 1024;         // sink for the lanes of masked-off 
 struct ChunkWorkspace {
     f16* w;
     f16* u;
-    f16* kt;
-    f16* qt;
-    f16* y;
+    f16* p;
     float* dg;
+    f16* kt;
+    f16* qf;
     float* junk;
     int n_slots;
     int group;     // value heads per q/k head
 
     __device__ __forceinline__ size_t vunit(int slot, int h) const { return (size_t)h * n_slots + slot; }
-    // K^T fragments are per q/k head j
+    // K^T and Q fragments are per q/k head j
     __device__ __forceinline__ size_t kunit(int slot, int j) const { return (size_t)j * n_slots + slot; }
 };
 

@@ -78,7 +78,8 @@ typedef struct {
  * allocates; contents undefined before and after a call).  It holds the
  * intra-chunk products of the chunkwise form (W, U, corrected U', the
  * per-chunk incoming states and the decay cumsums), one 64-token chunk slot
- * per chunk: at most N + T/64 + 1 slots, about 82 KB per slot and value head.
+ * per chunk: at most N + T/64 + 1 slots, about 55 KB per slot and value head
+ * at two value heads per q/k head.
  */
 gdn_status gdn_chunk_fwd_workspace_size(const gdn_dims* dims, size_t* bytes);
 
@@ -88,11 +89,11 @@ gdn_status gdn_chunk_fwd_workspace_size(const gdn_dims* dims, size_t* bytes);
  * of the "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page, section 2, in two
  * kernels:
  *   gdn_chunk_prep  -- decay cumsum, masked K K^T, (I + A)^{-1}, W and U, and
- *                      the state-independent parts of the output
- *                      (Q' = diag(e^G) Q - P W, Y = P U, P = M o Q K^T);
+ *                      the output's intra-chunk matrix P = M o Q K^T;
  *   gdn_chunk_state -- inter-chunk recurrence with the state held in
  *                      matrix-core accumulators and the next chunks
- *                      prefetched, and the output O = Y + Q' S_chunk.
+ *                      prefetched, and the output
+ *                      O = diag(e^G) Q S_chunk + P U'.
  *  q, k, v       bf16 device tensors, layouts above.
  *  g, beta       float32 [T, H_v].
  *  cu_seqlens    int32 [N + 1], device.

@@ -71,8 +71,8 @@ def test_workspace_size_formula(lib):
     st, b = ws_size(lib, dims(n=1, T=4000, hqk=16, hv=32))
     assert st == 0
     slots = 1 + 4000 // 64 + 1
-    per_v = 8192 * 4 * 2 + 64 * 4    # per value head: -W, U, Q', Y (fp16), decay vector (fp32)
-    per_qk = 8192 * 2                 # per q/k head: K^T (fp16)
+    per_v = 8192 * 2 * 2 + 3072 * 2 + 128 * 4   # per value head: -W, U, P (fp16), decay vectors (fp32)
+    per_qk = 8192 * 2 * 2                        # per q/k head: K^T, Q (fp16)
     need = slots * (32 * per_v + 16 * per_qk) + 1024  # + the sink of masked-off stores
     assert need <= b < need + 7 * 256
 
