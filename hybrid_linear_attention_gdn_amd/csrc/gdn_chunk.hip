@@ -504,19 +504,29 @@ __device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace&
                                          reinterpret_cast<void*>(st.dg + kChunk * half), 4, 0, 0);
 }
 
-// Touch one chunk's operands into L2 two chunks before their copies: the
-// 384 cache lines of -W, K^T and Q are split over the 8 column tiles of a
-// head, 48 lines each, one 4-byte direct-to-LDS copy per lane (lanes past 48
-// repeat a line) into a sink nobody reads.  A direct copy, unlike a register
-// load, is invisible to the compiler's counter waits, so the copy wave's own
-// single wait still covers it.  It pays where the operands come from HBM
-// (long sequences: the recurrence 20% faster at 131072 tokens).
+// Touch one chunk's operands into L2 two chunks before their copies, with
+// 4-byte direct-to-LDS copies into a sink nobody reads (one cache line per
+// lane).  First copy: the 384 lines of -W, K^T and Q, split over the 8
+// column tiles of a head (lanes 0-47), and the 16 lines of the tile's own U
+// (lanes 48-63).  Second copy: the 48 lines of P, 6 per tile (lanes past 6
+// repeat a line).  A direct copy, unlike a register load, is invisible to the
+// compiler's counter waits, so the copy wave's own single wait still covers
+// it.  It pays where the operands come from HBM (long sequences).
+constexpr int kTouchesPerChunk = 2;
+
 __device__ __forceinline__ void state_touch(const ChunkWorkspace& ws, size_t vu, size_t ku, int ct, int lane,
                                             float* sink) {
-    const int line = ct * 48 + min(lane, 47);
-    const int arr = line >> 7, off = (line & 127) * 64;          // halves
-    const f16* base = arr == 0 ? ws.w + vu * kWElems : arr == 1 ? ws.kt + ku * kKtElems : ws.qf + ku * kQfElems;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off), reinterpret_cast<void*>(sink), 4, 0, 0);
+    const f16* base;
+    if (lane < 48) {
+        const int line = ct * 48 + lane;
+        const int arr = line >> 7, off = (line & 127) * 64;      // halves
+        base = (arr == 0 ? ws.w + vu * kWElems : arr == 1 ? ws.kt + ku * kKtElems : ws.qf + ku * kQfElems) + off;
+    } else {
+        base = ws.u + vu * kUElems + (size_t)ct * kUTile + (lane - 48) * 64;
+    }
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base), reinterpret_cast<void*>(sink), 4, 0, 0);
+    const f16* pl = ws.p + vu * kPElems + (ct * 6 + min(lane, 5)) * 64;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(pl), reinterpret_cast<void*>(sink), 4, 0, 0);
 }
 
 // The tile's U fragments of one chunk, as four 8-byte register loads.
@@ -869,7 +879,7 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
             // between B_c and B_{c+1}: the chain and output waves work on chunk c
             state_copy<kOut>(stage[(c - c_begin + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), lane);
             state_touch(ws, vidx(c + 4), kidx(c + 4), ct, lane, touch_sink);
-            wait_vmcnt<kCopies + 1>();                           // chunk c + 1 has landed
+            wait_vmcnt<kCopies + kTouchesPerChunk>();            // chunk c + 1 has landed
             lds_barrier();                                   // B_{c+1}
         }
         // drain the copies past the end before the workgroup's LDS goes away
