@@ -721,11 +721,17 @@ enum : int {
 // has no output wave.
 __host__ __device__ constexpr int state_threads(int mode) { return mode == kModeMap ? 128 : 192; }
 
-// Grid: kTiles * 8 * ceil(U / 8) workgroups; U = n_seqs * h_v for whole
+// Workgroups of a state launch over `units` units of kTiles tiles each.
+constexpr unsigned state_grid(int units, int tiles) { return 8u * tiles * 2u * (unsigned)((units + 15) / 16); }
+
+// Grid: state_grid(U, kTiles) workgroups; U = n_seqs * h_v for whole
 // sequences, n_segslots * h_v for segments; kTiles = 8 column tiles, or 16
-// for a map (8 of Phi, 8 of R).  Workgroup b runs on XCD b % 8 (round-robin
-// dispatch); it takes unit 8 * (m / kTiles) + b % 8 and tile m % kTiles,
-// m = b / 8, so all tiles of a unit share an XCD.
+// for a map (8 of Phi, 8 of R).  Workgroup b runs on XCD x = b % 8
+// (round-robin dispatch); with m = b / 8 it takes tile m % kTiles of unit
+// 16 (g / 2) + 2 x + g % 2, g = m / kTiles.  All tiles of a unit share an
+// XCD, and so do units 2i and 2i + 1, the two value heads of a q/k head at
+// two value heads per q/k head, whose K^T and Q fragments one L2 then
+// serves; consecutive unit pairs go to different XCDs.
 template <int kMode>
 __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
     const int32_t* __restrict__ cu, int n_seqs, int h_v,
@@ -739,7 +745,8 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
     constexpr int kCopyRole = state_threads(kMode) / 64 - 1;
     const int b = blockIdx.x;
     const int m = b >> 3;
-    const int unit = ((m / kTiles) << 3) + (b & 7);
+    const int gu = m / kTiles;
+    const int unit = ((gu >> 1) << 4) + ((b & 7) << 1) + (gu & 1);
     const int tile = m % kTiles;
     const int ct = tile & 7;
     int seq, h, sg = 0, nseg = 1, gs = 0;
@@ -970,7 +977,7 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
         SegArgs sa = {};
         if (!seg) {
             const int units = n_seqs * h_v;
-            const dim3 grid(64 * ((units + 7) / 8));
+            const dim3 grid(state_grid(units, 8));
             if (chunk_states)
                 hipLaunchKernelGGL(gdn_chunk_state<kModeWholeSnap>, grid, dim3(state_threads(kModeWholeSnap)), 0, stream,
                                    cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
@@ -983,11 +990,11 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
             sa.hstart = seg->hstart;
             sa.maps = seg->maps;
             const int units = seg->n_segslots * h_v;
-            hipLaunchKernelGGL(gdn_chunk_state<kModeMap>, dim3(128 * ((units + 7) / 8)), dim3(state_threads(kModeMap)), 0, stream,
+            hipLaunchKernelGGL(gdn_chunk_state<kModeMap>, dim3(state_grid(units, 16)), dim3(state_threads(kModeMap)), 0, stream,
                                cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
             hipLaunchKernelGGL(gdn_chunk_seg_scan, dim3(8 * n_seqs * h_v), dim3(256), 0, stream,
                                cu, n_seqs, h_v, s0, sa);
-            hipLaunchKernelGGL(gdn_chunk_state<kModeSegment>, dim3(64 * ((units + 7) / 8)), dim3(state_threads(kModeSegment)), 0, stream,
+            hipLaunchKernelGGL(gdn_chunk_state<kModeSegment>, dim3(state_grid(units, 8)), dim3(state_threads(kModeSegment)), 0, stream,
                                cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
         }
     }
