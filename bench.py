@@ -264,6 +264,21 @@ def main():
     step()
     torch.cuda.synchronize()
 
+    # Cold steps: a 1 GiB fill between steps (outside the timed interval)
+    # evicts the 256 MB last-level cache and L2, so each timed step reads its
+    # inputs and intermediates from HBM.  Reported beside the warm figure.
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    n_cold = min(args.steps, 20)
+    cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_cold)]
+    for i in range(n_cold):
+        flush.fill_(float(i))
+        cold_ev[i][0].record(s)
+        step()
+        cold_ev[i][1].record(s)
+    torch.cuda.synchronize()
+    t_cold = sorted(e[0].elapsed_time(e[1]) for e in cold_ev)[n_cold // 2] / 1e3
+    del flush
+
     work = algorithmic_work()
     state_bytes = H_V * D * D * 4          # one fp32 state per sequence (final state written)
     per_seq = {"prep": 0, "state": state_bytes, "layer": state_bytes}
@@ -287,6 +302,7 @@ def main():
     prefill = {
         "ms_per_layer": t_step * 1e3,
         "ms_per_layer_with_events": t_step_evented * 1e3,
+        "ms_per_layer_cold_median": t_cold * 1e3,
         "pct_mfma_peak": 100 * f_layer * T / t_step / PEAK_MFMA_F16,
         "pct_hbm_peak": 100 * (b_layer * T + per_seq["layer"]) / t_step / PEAK_HBM,
         "algorithmic_flops": f_layer * T,

@@ -29,7 +29,10 @@ namespace gdn {
 
 namespace {
 
-constexpr int kTS = 72;   // LDS row stride (halves or floats) of 64-wide tiles
+constexpr int kTS = 72;   // LDS row stride (halves) of 64-wide fp16 tiles
+// LDS row stride (floats) of the fp32 64 x 64 A / Tm: rows 4 apart (the rows
+// of one accumulator store) fall 16 banks apart
+constexpr int kTA = 68;
 constexpr int kQS = 136;  // LDS row stride (halves) of 128-wide tiles
 
 // Transposed [dim][pos] fp16 tiles, 64 positions per row, no padding.  Rows
@@ -220,17 +223,36 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
             *reinterpret_cast<f16x8*>(pdst + ((size_t)(f0 + 1) * 64 + lane) * 8) = cat_to_f16(dt[2], dt[3]);
     }
 
+    // ---- A into the A buffer (row stride kTA).  The diagonal blocks A_ii go
+    //      transposed into blocks above the diagonal, which nothing else uses:
+    //      A_ii^T at block (0, 1 + i) for i < 3 and A_33^T at block (1, 2), so
+    //      that the diagonal solve reads columns of A_ii as contiguous rows.
     __syncthreads();                                  // K rows in the A buffer are consumed
     {
         const int p = wave;
+        float gr[4], br[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            gr[e] = Gs[16 * p + 4 * gq + e];
+            br[e] = Bs[16 * p + 4 * gq + e];
+        }
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             if (jt > p) continue;
             const int s = 16 * jt + ln;
+            const float gsv = Gs[s];
+            f32x4 a;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * p + 4 * gq + e;
-                Ab[r * kTS + s] = (s < r) ? Bs[r] * exp_f(Gs[r] - Gs[s]) * gacc[jt][e] : 0.f;
+                a[e] = (s < r) ? br[e] * exp_f(gr[e] - gsv) * gacc[jt][e] : 0.f;
+            }
+            if (jt < p) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Ab[(16 * p + 4 * gq + e) * kTA + s] = a[e];
+            } else {
+                const int ur = p < 3 ? 0 : 1, uc = p < 3 ? 1 + p : 2;
+                *reinterpret_cast<f32x4*>(Ab + (16 * ur + ln) * kTA + 16 * uc + 4 * gq) = a;
             }
         }
     }
@@ -238,22 +260,31 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
 
     // ---- Tm = (I + A)^{-1}, blocked by 16, in place.
     //  (1) Diagonal blocks Tm_ii = (I + A_ii)^{-1}: wave i, lane c % 16 holds
-    //      column c; x_r = delta_rc - sum_{t<r} A_rt x_t (x_t = 0 for t < c).
+    //      column c of x = (I + A_ii)^{-1} e_c.  Forward substitution by
+    //      columns of A_ii: once x_t is final, x_r -= A_rt x_t for r > t (each
+    //      x_r sees the same subtractions in the same order as the row form).
     {
         const int ib = wave;
+        const int ur = ib < 3 ? 0 : 1, uc = ib < 3 ? 1 + ib : 2;
+        const float* at = Ab + 16 * ur * kTA + 16 * uc;   // at[t * kTA + r] = A_ii[r][t]
         float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == ln) ? 1.f : 0.f;
-            const float* arow = Ab + (16 * ib + r) * kTS + 16 * ib;
+        for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
 #pragma unroll
-            for (int t = 0; t < r; ++t) acc -= arow[t] * x[t];
-            x[r] = acc;
+        for (int t = 0; t < 15; ++t) {
+            float col[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 c4 = *reinterpret_cast<const f32x4*>(at + t * kTA + 4 * q4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) col[4 * q4 + e] = c4[e];
+            }
+#pragma unroll
+            for (int r = t + 1; r < 16; ++r) x[r] -= col[r] * x[t];
         }
-        // this wave's reads of its block are done before these writes
         if (gq == 0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Ab[(16 * ib + r) * kTS + 16 * ib + ln] = x[r];
+            for (int r = 0; r < 16; ++r) Ab[(16 * ib + r) * kTA + 16 * ib + ln] = x[r];
         }
     }
     __syncthreads();
@@ -273,17 +304,17 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
             if (kb != jb) continue;
             f32x4 t;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) t[e] = Ab[(16 * kb + 4 * gq + e) * kTS + 16 * kb + ln];
+            for (int e = 0; e < 4; ++e) t[e] = Ab[(16 * kb + 4 * gq + e) * kTA + 16 * kb + ln];
             tcol[kb] = split16(t);
         }
 #pragma unroll
         for (int i2 = 1; i2 < 4; ++i2) {
             if (i2 <= jb) continue;
-            tii[i2] = *reinterpret_cast<const f32x4*>(Ab + (16 * i2 + ln) * kTS + 16 * i2 + 4 * gq);
+            tii[i2] = *reinterpret_cast<const f32x4*>(Ab + (16 * i2 + ln) * kTA + 16 * i2 + 4 * gq);
 #pragma unroll
             for (int kb = 0; kb < i2; ++kb) {
                 if (kb < jb) continue;
-                aik[i2][kb] = *reinterpret_cast<const f32x4*>(Ab + (16 * i2 + ln) * kTS + 16 * kb + 4 * gq);
+                aik[i2][kb] = *reinterpret_cast<const f32x4*>(Ab + (16 * i2 + ln) * kTA + 16 * kb + 4 * gq);
             }
         }
     }
@@ -301,7 +332,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
             const f32x4 y = mfma_split16(split16(tii[i2]), split16(xs), f32x4{0.f, 0.f, 0.f, 0.f});
             tcol[i2] = split16(-y);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Ab[(16 * i2 + 4 * gq + e) * kTS + 16 * jb + ln] = -y[e];
+            for (int e = 0; e < 4; ++e) Ab[(16 * i2 + 4 * gq + e) * kTA + 16 * jb + ln] = -y[e];
         }
     }
     __syncthreads();
@@ -318,7 +349,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
             const int idx = tid + 256 * it;
             const int r = idx >> 4, t = (idx & 15) * 4;
             tv[it] = ((t >> 4) > (r >> 4)) ? f32x4{0.f, 0.f, 0.f, 0.f}
-                                            : *reinterpret_cast<const f32x4*>(Ab + r * kTS + t);
+                                            : *reinterpret_cast<const f32x4*>(Ab + r * kTA + t);
         }
         __syncthreads();
 #pragma unroll
