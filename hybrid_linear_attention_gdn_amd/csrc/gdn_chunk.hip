@@ -54,6 +54,95 @@ __device__ __forceinline__ int rsw(int r, int c) {
 }
 
 // ---------------------------------------------------------------------------
+// Stage 1 helpers.  The Gram blocks (p, jt), jt <= p, of row tiles of K, and
+// P's row tile p (owned by wave p, which holds Q's row tile p), spread so that
+// every wave runs five 16 x 16 x 128 products and their decay factors: wave
+// w computes P's blocks (w, 0..w) and the Gram blocks listed here.
+template <int W> struct GramBlocks;
+template <> struct GramBlocks<0> { static constexpr int n = 4, p[4] = {1, 2, 3, 3}, jt[4] = {0, 0, 0, 1}; };
+template <> struct GramBlocks<1> { static constexpr int n = 3, p[4] = {1, 2, 3, 0}, jt[4] = {1, 1, 2, 0}; };
+template <> struct GramBlocks<2> { static constexpr int n = 2, p[4] = {2, 3, 0, 0}, jt[4] = {2, 3, 0, 0}; };
+template <> struct GramBlocks<3> { static constexpr int n = 1, p[4] = {0, 0, 0, 0}, jt[4] = {0, 0, 0, 0}; };
+
+// Where the transposed diagonal block A_ii goes: block (0, 1 + i) for i < 3,
+// (1, 2) for i = 3 (above the diagonal, which nothing else uses).
+__device__ __forceinline__ int diag_row_block(int i) { return i < 3 ? 0 : 1; }
+__device__ __forceinline__ int diag_col_block(int i) { return i < 3 ? 1 + i : 2; }
+
+// The products of wave W: the A values of its Gram blocks into av (A_rs for
+// rows r = 16 p + 4 gq + e, column s = 16 jt + ln; 0 for s >= r), and P's
+// row tile W, stored to pdst.  K row tiles come from Kr (row-major bf16,
+// chunk-swizzled), the wave's own from kown.
+template <int W>
+__device__ __forceinline__ void prep_products(f32x4 (&av)[4], const bf16x8 (&kown)[4], const bf16x8 (&qf)[4],
+                                              const uint16_t* Kr, const float* Gs, const float* Bs, f16* pdst,
+                                              int lane, int gq, int ln) {
+    bf16x8 kt[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            kt[t][kk] = t == W ? kown[kk]
+                               : __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(Kr + rsw(16 * t + ln, 4 * kk + gq)));
+    using B = GramBlocks<W>;
+#pragma unroll
+    for (int i = 0; i < B::n; ++i) {
+        const int p = B::p[i], jt = B::jt[i];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};   // exact bf16 inputs
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(kt[p][kk], kt[jt][kk], acc);
+        const int s = 16 * jt + ln;
+        const float gsv = Gs[s];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * p + 4 * gq + e;
+            av[i][e] = (s < r) ? Bs[r] * exp_f(Gs[r] - gsv) * acc[e] : 0.f;
+        }
+    }
+    // P = M o (Q K^T) for row tile W, M_rs = e^{G_r - G_s} (s <= r), computed
+    // as (K Q^T)[s][r] so that the accumulators of two position tiles stack
+    // into the A fragment of P over position slots, which is how the output
+    // stage reads it: block (p, qq) at 2 p (p < 2) or 2 + 2 (p - 2) + qq;
+    // blocks (0, 1) and (1, 1) are zero and not stored.
+    const int r = 16 * W + ln;
+    const float gr = Gs[r];
+    f32x4 dt[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+        dt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (jt > W) continue;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) dt[jt] = mfma_bf16(kt[jt][kk], qf[kk], dt[jt]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int sp = 16 * jt + 4 * gq + e;
+            dt[jt][e] = (sp <= r) ? exp_f(gr - Gs[sp]) * dt[jt][e] : 0.f;
+        }
+    }
+    constexpr int f0 = W < 2 ? W : 2 * W - 2;
+    *reinterpret_cast<f16x8*>(pdst + ((size_t)f0 * 64 + lane) * 8) = cat_to_f16(dt[0], dt[1]);
+    if constexpr (W >= 2)
+        *reinterpret_cast<f16x8*>(pdst + ((size_t)(f0 + 1) * 64 + lane) * 8) = cat_to_f16(dt[2], dt[3]);
+}
+
+// A values of wave W's Gram blocks into the A buffer (row stride kTA); a
+// diagonal block goes transposed to its place above the diagonal.
+template <int W>
+__device__ __forceinline__ void store_a(float* Ab, const f32x4 (&av)[4], int gq, int ln) {
+    using B = GramBlocks<W>;
+#pragma unroll
+    for (int i = 0; i < B::n; ++i) {
+        const int p = B::p[i], jt = B::jt[i];
+        if (jt < p) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ab[(16 * p + 4 * gq + e) * kTA + 16 * jt + ln] = av[i][e];
+        } else {
+            *reinterpret_cast<f32x4*>(Ab + (16 * diag_row_block(p) + ln) * kTA + 16 * diag_col_block(p) + 4 * gq) = av[i];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Stage 1: intra-chunk preparation.  One workgroup per (chunk slot, value
 // head); 51 KB of LDS so that three workgroups share a CU.  The UT transform
 // runs in place in the A buffer: A, then Tm = (I + A)^{-1}, then the fp16
@@ -139,17 +228,6 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     }
     __syncthreads();
 
-    // K row tiles jt < w for this wave's Gram rows
-    bf16x8 kf[3][4];
-#pragma unroll
-    for (int jt = 0; jt < 3; ++jt)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            kf[jt][kk] = bf16x8{};
-            if (jt < wave)
-                kf[jt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(Kr + rsw(16 * jt + ln, 4 * kk + gq)));
-        }
-
     // ---- K^T as A-operand fragments of the state update (which applies the
     //      decay e^{G_C - G} to U' instead): fragment (i, qq), lane (gq, ln) =
     //      K[p][16 i + ln] at the position slots p(gq, s) of K-step qq.  The
@@ -168,93 +246,22 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
         }
     }
 
-    // ---- Gram rows of A = strictly lower (beta_r e^{G_r-G_s} K K^T); wave w
-    //      owns row tile w (tiles above the diagonal are never written or read
-    //      as A).  The accumulators wait in registers until every wave has read
-    //      its K tiles from the A buffer.
-    f32x4 gacc[4];
-    {
-        const int p = wave;
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            gacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};   // exact bf16 inputs
-            if (jt > p) continue;
-            if (jt == p) {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) gacc[jt] = mfma_bf16(kown[kk], kown[kk], gacc[jt]);
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) gacc[jt] = mfma_bf16(kown[kk], kf[jt < 3 ? jt : 0][kk], gacc[jt]);
-            }
-        }
+    // ---- The Gram blocks of A = strictly lower (beta_r e^{G_r-G_s} K K^T) and
+    //      P's row tile, balanced over the waves (prep_products); then, once
+    //      every wave has read its K tiles from the A buffer, A into it.
+    f32x4 av[4];
+    switch (wave) {
+        case 0: prep_products<0>(av, kown, qf, Kr, Gs, Bs, ws.p + wsidx * kPElems, lane, gq, ln); break;
+        case 1: prep_products<1>(av, kown, qf, Kr, Gs, Bs, ws.p + wsidx * kPElems, lane, gq, ln); break;
+        case 2: prep_products<2>(av, kown, qf, Kr, Gs, Bs, ws.p + wsidx * kPElems, lane, gq, ln); break;
+        default: prep_products<3>(av, kown, qf, Kr, Gs, Bs, ws.p + wsidx * kPElems, lane, gq, ln); break;
     }
-
-    // ---- P = M o (Q K^T) for row tile p = wave, M_rs = e^{G_r - G_s} (s <= r),
-    //      computed as (K Q^T)[s][r] so that the accumulators of two position
-    //      tiles stack into the A fragment of P over position slots, which is
-    //      how the output stage reads it: block (p, qq) at 2 p (p < 2) or
-    //      2 + 2 (p - 2) + qq; blocks (0, 1) and (1, 1) are zero and not stored.
-    {
-        const int p = wave;
-        const int r = 16 * p + ln;
-        f32x4 dt[4];
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            dt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (jt > p) continue;
-            if (jt == p) {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) dt[jt] = mfma_bf16(kown[kk], qf[kk], dt[jt]);
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) dt[jt] = mfma_bf16(kf[jt < 3 ? jt : 0][kk], qf[kk], dt[jt]);
-            }
-            const float gr = Gs[r];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int sp = 16 * jt + 4 * gq + e;
-                dt[jt][e] = (sp <= r) ? exp_f(gr - Gs[sp]) * dt[jt][e] : 0.f;
-            }
-        }
-        f16* pdst = ws.p + wsidx * kPElems;
-        const int f0 = p < 2 ? p : 2 * p - 2;
-        *reinterpret_cast<f16x8*>(pdst + ((size_t)f0 * 64 + lane) * 8) = cat_to_f16(dt[0], dt[1]);
-        if (p >= 2)
-            *reinterpret_cast<f16x8*>(pdst + ((size_t)(f0 + 1) * 64 + lane) * 8) = cat_to_f16(dt[2], dt[3]);
-    }
-
-    // ---- A into the A buffer (row stride kTA).  The diagonal blocks A_ii go
-    //      transposed into blocks above the diagonal, which nothing else uses:
-    //      A_ii^T at block (0, 1 + i) for i < 3 and A_33^T at block (1, 2), so
-    //      that the diagonal solve reads columns of A_ii as contiguous rows.
     __syncthreads();                                  // K rows in the A buffer are consumed
-    {
-        const int p = wave;
-        float gr[4], br[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            gr[e] = Gs[16 * p + 4 * gq + e];
-            br[e] = Bs[16 * p + 4 * gq + e];
-        }
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            if (jt > p) continue;
-            const int s = 16 * jt + ln;
-            const float gsv = Gs[s];
-            f32x4 a;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * p + 4 * gq + e;
-                a[e] = (s < r) ? br[e] * exp_f(gr[e] - gsv) * gacc[jt][e] : 0.f;
-            }
-            if (jt < p) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Ab[(16 * p + 4 * gq + e) * kTA + s] = a[e];
-            } else {
-                const int ur = p < 3 ? 0 : 1, uc = p < 3 ? 1 + p : 2;
-                *reinterpret_cast<f32x4*>(Ab + (16 * ur + ln) * kTA + 16 * uc + 4 * gq) = a;
-            }
-        }
+    switch (wave) {
+        case 0: store_a<0>(Ab, av, gq, ln); break;
+        case 1: store_a<1>(Ab, av, gq, ln); break;
+        case 2: store_a<2>(Ab, av, gq, ln); break;
+        default: store_a<3>(Ab, av, gq, ln); break;
     }
     __syncthreads();
 
@@ -265,8 +272,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     //      x_r sees the same subtractions in the same order as the row form).
     {
         const int ib = wave;
-        const int ur = ib < 3 ? 0 : 1, uc = ib < 3 ? 1 + ib : 2;
-        const float* at = Ab + 16 * ur * kTA + 16 * uc;   // at[t * kTA + r] = A_ii[r][t]
+        const float* at = Ab + 16 * diag_row_block(ib) * kTA + 16 * diag_col_block(ib);   // at[t * kTA + r] = A_ii[r][t]
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
