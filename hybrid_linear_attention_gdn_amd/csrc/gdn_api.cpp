@@ -183,6 +183,8 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
     ws.junk = reinterpret_cast<float*>(base + L.junk);
     ws.n_slots = (int)slots;
     ws.group = dims->n_heads_v / dims->n_heads_qk;
+    ws.h_v = dims->n_heads_v;
+    ws.h_qk = dims->n_heads_qk;
 
     gdn::SegLaunch seg;
     if (seg_chunks > 0) {

@@ -51,9 +51,10 @@ constexpr size_t kKtElems = 8 * 2 * 64 * 8;
 constexpr size_t kQfElems = 4 * 4 * 64 * 8;
 constexpr size_t kJunkBytes = 1024;         // sink for the lanes of masked-off stores
 
-// Workspace regions are head-major: unit (slot, head) sits at head * n_slots
-// + slot, so one head's consecutive chunks are contiguous in memory and the
-// state recurrence streams through them in address order.
+// Workspace regions are chunk-slot-major: unit (slot, head) sits at slot *
+// heads + head, so the units of all heads for one chunk are contiguous (a
+// few large pages per chunk step for the state recurrence, whose 256 or more
+// workgroups walk the chunks in step).
 struct ChunkWorkspace {
     f16* w;
     f16* u;
@@ -64,10 +65,11 @@ struct ChunkWorkspace {
     float* junk;
     int n_slots;
     int group;     // value heads per q/k head
+    int h_v, h_qk;
 
-    __device__ __forceinline__ size_t vunit(int slot, int h) const { return (size_t)h * n_slots + slot; }
+    __device__ __forceinline__ size_t vunit(int slot, int h) const { return (size_t)slot * h_v + h; }
     // K^T and Q fragments are per q/k head j
-    __device__ __forceinline__ size_t kunit(int slot, int j) const { return (size_t)j * n_slots + slot; }
+    __device__ __forceinline__ size_t kunit(int slot, int j) const { return (size_t)slot * h_qk + j; }
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
