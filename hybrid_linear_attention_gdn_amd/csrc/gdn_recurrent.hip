@@ -106,20 +106,92 @@ __global__ __launch_bounds__(256) void gdn_recurrent_kernel(RecurrentArgs a)
     __shared__ int wss[kTokBlock];              // pool layout: write slot per token
     __shared__ float4 red[2][4][16];            // per-wave column partials (prediction, output)
 
+    // Load order: everything that does not depend on a slot index first.
+    // (1) the request's token range and accepted count; (2) the incoming slot
+    // and the first block of token inputs; (3) the state.  The write slots are
+    // checked while the state loads are in flight.
     int64_t t_begin;
     int n;
-    const StateT* src;
     const int32_t* row = nullptr;       // this request's slot-table row
+    int rs = 0;
     if constexpr (kPooled) {
         // Every index below is checked before it is used to address memory.
         const int64_t tb = a.cu_tokens[req], te = a.cu_tokens[req + 1];
+        const int col = a.accepted ? a.accepted[req] : 0;
         if (tb < 0 || te < tb || te > a.total_tokens || te - tb > a.max_tok) return;  // rows unknown
         t_begin = tb;
         n = (int)(te - tb);
         row = a.table + (size_t)req * (a.max_tok + 1);
-        const int col = a.accepted ? a.accepted[req] : 0;
-        int rs = -1;
-        if (col >= 0 && col <= a.max_tok) rs = row[col];
+        rs = (col >= 0 && col <= a.max_tok) ? row[col] : -1;
+    } else {
+        t_begin = (int64_t)req * a.n_tok;
+        n = a.n_tok;
+    }
+
+    // Stage token inputs [blk, blk + nb) in LDS: loads into registers first
+    // (stage_load), the LDS writes later (stage_store), so that other loads
+    // can be issued in between.
+    struct Staged {
+        u16x8 kq[2];
+        u16x4 v;
+        float g, b;
+        int w;
+    };
+    auto stage_load = [&](int blk, int nb) {
+        Staged st = {};
+        const int idx = tid;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {     // nb <= 16: k, q in two passes of 8 tokens
+            const int i2 = idx + 256 * pass;
+            if (i2 < nb * 32) {
+                const int tt = i2 >> 5, e = (i2 & 31) * 8;
+                const size_t t = (size_t)(t_begin + blk + tt);
+                const uint16_t* srcp = e < kDim ? a.k + (t * h_qk + j) * kDim + e
+                                                : a.q + (t * h_qk + j) * kDim + e - kDim;
+                st.kq[pass] = *reinterpret_cast<const u16x8*>(srcp);
+            }
+        }
+        if (idx < nb * 16) {
+            const int tt = idx >> 4, c4 = idx & 15;
+            const size_t t = (size_t)(t_begin + blk + tt);
+            st.v = *reinterpret_cast<const u16x4*>(a.v + (t * h_v + h) * kDim + 64 * blockIdx.y + 4 * c4);
+        }
+        if (idx < nb) {
+            const size_t t = (size_t)(t_begin + blk + idx);
+            st.g = a.g[t * h_v + h];
+            st.b = a.beta[t * h_v + h];
+            if constexpr (kPooled) st.w = row[1 + blk + idx];
+        }
+        return st;
+    };
+    auto stage_store = [&](const Staged& st, int nb) {
+        const int idx = tid;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int i2 = idx + 256 * pass;
+            if (i2 < nb * 32) {
+                const int tt = i2 >> 5, e = (i2 & 31) * 8;
+                float* d = &kqs[tt][0][0] + e;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) d[c] = bf16_to_f32(st.kq[pass][c]);
+            }
+        }
+        if (idx < nb * 16) {
+            const int tt = idx >> 4, c4 = idx & 15;
+            vs[tt][c4] = make_float4(bf16_to_f32(st.v[0]), bf16_to_f32(st.v[1]), bf16_to_f32(st.v[2]), bf16_to_f32(st.v[3]));
+        }
+        if (idx < nb) {
+            gs[idx] = exp_f(st.g);
+            bs[idx] = st.b;
+            wss[idx] = st.w;
+        }
+    };
+
+    const int nb0 = min(kTokBlock, n);
+    Staged st0 = stage_load(0, nb0);
+
+    const StateT* src;
+    if constexpr (kPooled) {
         int bad = (rs < 0 || rs >= a.pool_slots) ? 1 : 0;
         for (int t = tid; t < n; t += 256) bad |= (row[1 + t] >= a.pool_slots) ? 1 : 0;
         if (__syncthreads_or(bad)) {
@@ -132,8 +204,6 @@ __global__ __launch_bounds__(256) void gdn_recurrent_kernel(RecurrentArgs a)
         }
         src = static_cast<const StateT*>(a.pool) + ((size_t)rs * h_v + h) * kHeadElems;
     } else {
-        t_begin = (int64_t)req * a.n_tok;
-        n = a.n_tok;
         src = static_cast<const StateT*>(a.s_in) + ((size_t)req * h_v + h) * kHeadElems;
     }
 
@@ -143,30 +213,11 @@ __global__ __launch_bounds__(256) void gdn_recurrent_kernel(RecurrentArgs a)
 
     for (int blk = 0; blk < n; blk += kTokBlock) {
         const int nb = min(kTokBlock, n - blk);
-        if (blk > 0) __syncthreads();   // previous block's staged inputs are consumed
-        // k and q: 32 threads per token, 8 values each; two tokens per pass of 64
-        for (int idx = tid; idx < nb * 32; idx += 256) {
-            const int tt = idx >> 5, e = (idx & 31) * 8;
-            const size_t t = (size_t)(t_begin + blk + tt);
-            const uint16_t* srcp = e < kDim ? a.k + (t * h_qk + j) * kDim + e
-                                            : a.q + (t * h_qk + j) * kDim + e - kDim;
-            const u16x8 x = *reinterpret_cast<const u16x8*>(srcp);
-            float* d = &kqs[tt][0][0] + e;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) d[c] = bf16_to_f32(x[c]);
-        }
-        // v: 16 threads per token, 4 columns each
-        for (int idx = tid; idx < nb * 16; idx += 256) {
-            const int tt = idx >> 4, c4 = idx & 15;
-            const size_t t = (size_t)(t_begin + blk + tt);
-            const u16x4 x = *reinterpret_cast<const u16x4*>(a.v + (t * h_v + h) * kDim + 64 * blockIdx.y + 4 * c4);
-            vs[tt][c4] = make_float4(bf16_to_f32(x[0]), bf16_to_f32(x[1]), bf16_to_f32(x[2]), bf16_to_f32(x[3]));
-        }
-        if (tid < nb) {
-            const size_t t = (size_t)(t_begin + blk + tid);
-            gs[tid] = exp_f(a.g[t * h_v + h]);
-            bs[tid] = a.beta[t * h_v + h];
-            if constexpr (kPooled) wss[tid] = row[1 + blk + tid];
+        if (blk > 0) {
+            __syncthreads();   // previous block's staged inputs are consumed
+            stage_store(stage_load(blk, nb), nb);
+        } else {
+            stage_store(st0, nb);
         }
         __syncthreads();
 

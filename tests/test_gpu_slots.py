@@ -162,3 +162,20 @@ def test_slots_zero_token_requests():
     ro, rpool = slots_step(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, pool, table)
     assert rel_l2(out, ro) <= OUT_TOL
     check_pool(gpool, rpool, pool, written_slots(table, x.cu_seqlens))
+
+
+@pytest.mark.parametrize("f16", [False, True], ids=["f32", "f16"])
+def test_slots_requests_longer_than_a_staging_block(f16):
+    """Requests of 9..20 tokens: token inputs are staged 16 at a time, k and q
+    in two passes of 8 tokens; the last request spans two staging blocks."""
+    lengths = [9, 12, 16, 20]
+    x = gi.verify_variable(lengths, seed=71)
+    R, M = len(lengths), max(lengths)
+    pool = gi.state_pool(x, R * M, f16=f16, seed=71)
+    table = gi.slot_table_contiguous(R, M, R)
+    out, gpool = run_slots(x, pool, table)
+    ro, rpool = slots_step(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, pool, table)
+    e = rel_l2(out, ro)
+    print(f"[result] out rel-L2 {e:.3e}", flush=True)
+    assert e <= OUT_TOL
+    check_pool(gpool, rpool, pool, written_slots(table, x.cu_seqlens))
