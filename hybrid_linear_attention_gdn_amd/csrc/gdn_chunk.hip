@@ -148,7 +148,7 @@ __device__ __forceinline__ void store_a(float* Ab, const f32x4 (&av)[4], int gq,
 // runs in place in the A buffer: A, then Tm = (I + A)^{-1}, then the fp16
 // rows of Tm diag(beta e^G) and Tm diag(beta).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gdn_chunk_prep(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void gdn_chunk_prep(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, int n_seqs, int h_qk, int h_v, ChunkWorkspace ws)
@@ -159,8 +159,9 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     if (!resolve_slot(cu, n_seqs, slot, seq, t0, len)) return;
     const int j = h / (h_v / h_qk);
 
-    __shared__ __attribute__((aligned(16))) f16 KsT[kDim * kChunk];  // K^T [dim][pos], swizzled
-    __shared__ __attribute__((aligned(16))) f16 VsT[kDim * kChunk];  // V^T [dim][pos], swizzled
+    // K^T [dim][pos] (swizzled), then V^T, then Q rows: one buffer, so that
+    // four workgroups (35 KB of LDS each) share a CU
+    __shared__ __attribute__((aligned(16))) f16 KsT[kDim * kChunk];
     __shared__ __attribute__((aligned(16))) float Ab[kChunk * kTS];  // A, then Tm, then TW | TU
     __shared__ __attribute__((aligned(16))) float Bs[kChunk];  // beta
     __shared__ __attribute__((aligned(16))) float Bw[kChunk];  // beta e^G
@@ -178,7 +179,8 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     //      transposed (fp16) for the products over positions; K also goes to
     //      LDS row-major (bf16, in the A buffer, which is still free) so that
     //      every wave can read the row tiles its Gram rows need.  Q stays in
-    //      registers.  Pad rows are zero.
+    //      registers.  V is loaded after the UT transform, into the K^T space
+    //      once W has been formed.  Pad rows are zero.
     uint16_t* Kr = reinterpret_cast<uint16_t*>(Ab);   // [pos][dim] bf16, chunk-swizzled
     bf16x8 kown[4], qf[4];
     {
@@ -188,23 +190,16 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
         for (int kk = 0; kk < 4; ++kk) {
             u16x8 kb = {0, 0, 0, 0, 0, 0, 0, 0};
             u16x8 qb = {0, 0, 0, 0, 0, 0, 0, 0};
-            u16x8 vb = {0, 0, 0, 0, 0, 0, 0, 0};
             if (r < len) {
                 kb = *reinterpret_cast<const u16x8*>(k + krow + 32 * kk + 8 * gq);
                 qb = *reinterpret_cast<const u16x8*>(q + krow + 32 * kk + 8 * gq);
-                vb = *reinterpret_cast<const u16x8*>(v + ((size_t)(t0 + r) * h_v + h) * kDim + 32 * kk + 8 * gq);
             }
             kown[kk] = __builtin_bit_cast(bf16x8, kb);
             qf[kk] = __builtin_bit_cast(bf16x8, qb);
             *reinterpret_cast<u16x8*>(Kr + rsw(r, 4 * kk + gq)) = kb;
             const f16x8 kt8 = bf16x8_to_f16x8(kb);
-            const f16x8 vt8 = bf16x8_to_f16x8(vb);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = 32 * kk + 8 * gq + e;
-                KsT[tsw(d, r)] = kt8[e];
-                VsT[tsw(d, r)] = vt8[e];
-            }
+            for (int e = 0; e < 8; ++e) KsT[tsw(32 * kk + 8 * gq + e, r)] = kt8[e];
         }
     }
     // ---- decay cumsum (wave 0, one lane per position) and the decay vectors
@@ -343,6 +338,18 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     }
     __syncthreads();
 
+    // ---- This wave's row tile of V, loaded now (its latency overlaps TW / TU
+    //      and the W products) and written to LDS once K^T is no longer read.
+    u16x8 vrow[4];
+    {
+        const int r = 16 * wave + ln;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            vrow[kk] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            if (r < len) vrow[kk] = *reinterpret_cast<const u16x8*>(v + ((size_t)(t0 + r) * h_v + h) * kDim + 32 * kk + 8 * gq);
+        }
+    }
+
     // ---- TW = Tm diag(beta e^G), TU = Tm diag(beta) as fp16, in place; blocks
     //      above the diagonal are zero.
     f16* TWs = reinterpret_cast<f16*>(Ab);          // [pos][t]
@@ -376,37 +383,26 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     }
     __syncthreads();
 
-    // ---- W = TW K (positions on lanes) and U = TU V (d_v on lanes).  Wave w
-    //      owns d_k tiles 2w, 2w+1 and d_v tiles 2w, 2w+1.
+    // ---- W = TW K (positions on lanes), then U = TU V (d_v on lanes), with V^T
+    //      in the K^T space in between.  Wave w owns d_k tiles 2w, 2w+1 and
+    //      d_v tiles 2w, 2w+1.
     {
         f32x4 wacc[2][4];   // W^T[d_k tile 2w + a][pos tile p]: positions on lanes
-        f32x4 uacc[4][2];   // U[pos tile p][d_v tile 2w + a]: d_v on lanes
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                wacc[a][p] = f32x4{0.f, 0.f, 0.f, 0.f};
-                uacc[p][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            for (int p = 0; p < 4; ++p) wacc[a][p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-            f16x8 kfr[2], vfr[2];
+            f16x8 kfr[2];
 #pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const int d = 16 * (2 * wave + a) + ln;
-                kfr[a] = *reinterpret_cast<const f16x8*>(KsT + tsw(d, 32 * kt + 8 * gq));
-                vfr[a] = *reinterpret_cast<const f16x8*>(VsT + tsw(d, 32 * kt + 8 * gq));
-            }
+            for (int a = 0; a < 2; ++a)
+                kfr[a] = *reinterpret_cast<const f16x8*>(KsT + tsw(16 * (2 * wave + a) + ln, 32 * kt + 8 * gq));
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const int row = 16 * p + ln;
-                const f16x8 tw = *reinterpret_cast<const f16x8*>(TWs + row * kTS + 32 * kt + 8 * gq);
-                const f16x8 tu = *reinterpret_cast<const f16x8*>(TUs + row * kTS + 32 * kt + 8 * gq);
+                const f16x8 tw = *reinterpret_cast<const f16x8*>(TWs + (16 * p + ln) * kTS + 32 * kt + 8 * gq);
 #pragma unroll
-                for (int a = 0; a < 2; ++a) {
-                    wacc[a][p] = mfma_f16(kfr[a], tw, wacc[a][p]);
-                    uacc[p][a] = mfma_f16(tu, vfr[a], uacc[p][a]);
-                }
+                for (int a = 0; a < 2; ++a) wacc[a][p] = mfma_f16(kfr[a], tw, wacc[a][p]);
             }
         }
         // -W fragments (p, qq = wave): stacked d_k tiles 2w, 2w+1 of W^T
@@ -415,6 +411,38 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
         for (int p = 0; p < 4; ++p) {
             const f16x8 fr = cat_to_f16(-wacc[0][p], -wacc[1][p]);
             *reinterpret_cast<f16x8*>(wdst + ((p * 4 + wave) * 64 + lane) * 8) = fr;
+        }
+    }
+    __syncthreads();                                  // every read of K^T is done
+    f16* VsT = KsT;                                   // V^T [dim][pos], swizzled
+    {
+        const int r = 16 * wave + ln;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const f16x8 vt8 = bf16x8_to_f16x8(vrow[kk]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) VsT[tsw(32 * kk + 8 * gq + e, r)] = vt8[e];
+        }
+    }
+    __syncthreads();
+    {
+        f32x4 uacc[4][2];   // U[pos tile p][d_v tile 2w + a]: d_v on lanes
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) uacc[p][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            f16x8 vfr[2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+                vfr[a] = *reinterpret_cast<const f16x8*>(VsT + tsw(16 * (2 * wave + a) + ln, 32 * kt + 8 * gq));
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const f16x8 tu = *reinterpret_cast<const f16x8*>(TUs + (16 * p + ln) * kTS + 32 * kt + 8 * gq);
+#pragma unroll
+                for (int a = 0; a < 2; ++a) uacc[p][a] = mfma_f16(tu, vfr[a], uacc[p][a]);
+            }
         }
         // U accumulator fragments (ct, p)
         f16* udst = ws.u + wsidx * kUElems;
@@ -434,10 +462,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep(
     // ---- Q as A fragments over the chunk state's d_k slots, (p, qq = wave),
     //      for the output stage's Q H0; the value heads of a q/k head share
     //      them and the first one writes them.  The rows go through LDS (in
-    //      the K^T space, free once the products above have read it) because
+    //      the K^T / V^T space, free once the products above have read it) because
     //      a lane's slots span two 16-dim runs held by different lanes.
     if (h % ws.group == 0) {
-        __syncthreads();                              // every read of K^T is done
+        __syncthreads();                              // every read of V^T is done
         uint16_t* Qr = reinterpret_cast<uint16_t*>(KsT);   // [pos][dim] bf16, chunk-swizzled
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
