@@ -338,18 +338,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
     __syncthreads();
 
-    // ---- This wave's row tile of V, loaded now (its latency overlaps TW / TU
-    //      and the W products) and written to LDS once K^T is no longer read.
-    u16x8 vrow[4];
-    {
-        const int r = 16 * wave + ln;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            vrow[kk] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (r < len) vrow[kk] = *reinterpret_cast<const u16x8*>(v + ((size_t)(t0 + r) * h_v + h) * kDim + 32 * kk + 8 * gq);
-        }
-    }
-
     // ---- TW = Tm diag(beta e^G), TU = Tm diag(beta) as fp16, in place; blocks
     //      above the diagonal are zero.
     f16* TWs = reinterpret_cast<f16*>(Ab);          // [pos][t]
@@ -411,6 +399,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         for (int p = 0; p < 4; ++p) {
             const f16x8 fr = cat_to_f16(-wacc[0][p], -wacc[1][p]);
             *reinterpret_cast<f16x8*>(wdst + ((p * 4 + wave) * 64 + lane) * 8) = fr;
+        }
+    }
+    // ---- This wave's row tile of V, loaded after W (out of the register peak
+    //      of the W products; the other workgroups on the CU cover the wait)
+    //      and written to LDS once every wave is done with K^T.
+    u16x8 vrow[4];
+    {
+        const int r = 16 * wave + ln;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            vrow[kk] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            if (r < len) vrow[kk] = *reinterpret_cast<const u16x8*>(v + ((size_t)(t0 + r) * h_v + h) * kDim + 32 * kk + 8 * gq);
         }
     }
     __syncthreads();                                  // every read of K^T is done
