@@ -1,9 +1,11 @@
-// Chunked Gated DeltaNet prefill for gfx950: three kernels, chunk length 64.
+// Chunked Gated DeltaNet prefill for gfx950, chunk length 64.
 //
-// The split follows the "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page,
+// The stages follow the "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page,
 // section 2 ("GDN prefill"): intra-chunk preparation, inter-chunk state
 // recurrence with the state resident in matrix-core accumulators and the
-// next chunk prefetched, then the output.  The chunkwise algebra (state
+// next chunk prefetched, and the output, which here runs inside the
+// recurrence's workgroups (two kernels; a segment scan for the
+// chunk-parallel path).  The chunkwise algebra (state
 // H = S^T, d_k x d_v; chunk positions r, s; incoming state H0):
 //
 //   G_r  = sum_{t<=r} g_t              A_rs = beta_r e^{G_r-G_s} k_r.k_s  (s < r)
@@ -15,7 +17,9 @@
 //
 // Intermediates live in the caller's workspace in matrix-core fragment
 // order, written by each producer exactly as its consumer's operand needs:
-//   prep  -> -W as A fragments of (W H), U as accumulators of U' = U - W H
+//   prep  -> -W as A fragments of (W H), U as accumulators of U' = U - W H,
+//            K^T as A fragments of the state update, Q and P as A fragments
+//            of the output's (Q H0) and (P U')
 //   state -> chunk state H0 and U' as B fragments of (Q H0) and (P U')
 // Contraction slot maps (lane group gq = lane / 16, slot s = 0..7):
 //   dim a(gq, s)   = 32 qq + 16 (s / 4) + 4 gq + s % 4   for K-step qq over d_k
@@ -144,9 +148,10 @@ __device__ __forceinline__ void store_a(float* Ab, const f32x4 (&av)[4], int gq,
 
 // ---------------------------------------------------------------------------
 // Stage 1: intra-chunk preparation.  One workgroup per (chunk slot, value
-// head); 51 KB of LDS so that three workgroups share a CU.  The UT transform
-// runs in place in the A buffer: A, then Tm = (I + A)^{-1}, then the fp16
-// rows of Tm diag(beta e^G) and Tm diag(beta).
+// head); 35 KB of LDS and at most 128 registers per lane so that four
+// workgroups share a CU.  The UT transform runs in place in the A buffer: A,
+// then Tm = (I + A)^{-1}, then the fp16 rows of Tm diag(beta e^G) and
+// Tm diag(beta).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void gdn_chunk_prep(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
