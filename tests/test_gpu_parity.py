@@ -94,6 +94,16 @@ def test_chunk_head_groupings(hqk, hv):
     check_chunk(x, f"groups_{hqk}x{hv}")
 
 
+def test_chunk_many_short_sequences_eight_heads_per_qk_head():
+    """40 sequences of 1..200 tokens at 16 value / 2 q-k heads: 640 (sequence,
+    head) units, more than one XCD round of the state kernel's unit map, odd
+    chunk counts, and eight value heads sharing one q/k head's K^T and Q."""
+    rng = np.random.default_rng(91)
+    lengths = [int(n) for n in rng.integers(1, 201, size=40)]
+    x = gi.make_inputs(lengths, 2, 16, 128, 128, seed=91, state_std=0.02)
+    check_chunk(x, "many_short_group8")
+
+
 def test_chunk_prefill_4000():
     x = gi.prefill_4000()
     out, fin = check_chunk(x, "prefill_4000")
