@@ -34,6 +34,19 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Launch-size limits.  A dispatch holds at most 2^32 work-items per grid
+// dimension: the state launch runs 8 column tiles of 192 threads (an affine
+// map 16 of 128, the segment scan 8 of 256) per (sequence or segment, value
+// head) pair, prep 256 threads per chunk slot with the value heads as the
+// second grid dimension (at most 65535 workgroups there).
+constexpr long long kMaxHeadUnits = 1LL << 21;
+constexpr long long kMaxChunkSlots = 1LL << 24;
+constexpr int kMaxValueHeads = 65535;
+
+int64_t n_chunk_slots(const gdn_dims* d) {
+    return (int64_t)d->n_seqs + d->total_tokens / gdn::kChunk + 1;
+}
+
 gdn_status check_dims(const gdn_dims* d) {
     if (!d) return fail(GDN_ERR_INVALID_VALUE, "dims is NULL");
     if (d->n_seqs < 0) return fail(GDN_ERR_INVALID_VALUE, "n_seqs = %d is negative", d->n_seqs);
@@ -53,14 +66,15 @@ gdn_status check_dims(const gdn_dims* d) {
         return fail(GDN_ERR_INVALID_VALUE, "head dims must be positive (d_k = %d, d_v = %d)", d->d_k, d->d_v);
     if (d->d_k != gdn::kDim || d->d_v != gdn::kDim)
         return fail(GDN_ERR_NOT_SUPPORTED, "only d_k = d_v = 128 is supported (got %d, %d)", d->d_k, d->d_v);
-    // grid dimensions: x counts slots or (sequence, head) pairs
+    if (d->n_heads_v > kMaxValueHeads)
+        return fail(GDN_ERR_INVALID_VALUE, "H_v = %d exceeds %d", d->n_heads_v, kMaxValueHeads);
     const long long nh = (long long)d->n_seqs * d->n_heads_v;
-    if (nh > 0x7fffffffLL) return fail(GDN_ERR_INVALID_VALUE, "n_seqs * H_v too large");
+    if (nh > kMaxHeadUnits)
+        return fail(GDN_ERR_INVALID_VALUE, "n_seqs * H_v = %lld exceeds %lld", nh, kMaxHeadUnits);
+    if (n_chunk_slots(d) > kMaxChunkSlots)
+        return fail(GDN_ERR_INVALID_VALUE, "%lld chunk slots (N + T/64 + 1) exceed %lld",
+                    (long long)n_chunk_slots(d), kMaxChunkSlots);
     return GDN_SUCCESS;
-}
-
-int64_t n_chunk_slots(const gdn_dims* d) {
-    return (int64_t)d->n_seqs + d->total_tokens / gdn::kChunk + 1;
 }
 
 struct Layout {
@@ -170,7 +184,6 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
     if (workspace_bytes < L.total)
         return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, L.total);
     const int64_t slots = n_chunk_slots(dims);
-    if (slots > 0x7fffffffLL) return fail(GDN_ERR_INVALID_VALUE, "too many chunk slots");
 
     char* base = static_cast<char*>(workspace);
     gdn::ChunkWorkspace ws;
@@ -189,7 +202,9 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
     gdn::SegLaunch seg;
     if (seg_chunks > 0) {
         const int64_t segslots = n_seg_slots(dims, seg_chunks);
-        if (segslots * dims->n_heads_v > 0x7fffffffLL / 16) return fail(GDN_ERR_INVALID_VALUE, "too many segments");
+        if (segslots * dims->n_heads_v > kMaxHeadUnits)
+            return fail(GDN_ERR_INVALID_VALUE, "%lld segments x H_v exceed %lld (segment_chunks too small)",
+                        (long long)segslots, kMaxHeadUnits);
         seg.seg_chunks = seg_chunks;
         seg.n_segslots = (int)segslots;
         seg.maps = reinterpret_cast<float*>(base + L.maps);

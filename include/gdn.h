@@ -63,7 +63,10 @@ typedef enum {
 } gdn_status;
 
 /* Host-side problem sizes.  n_seqs and total_tokens are host copies of
- * what cu_seqlens holds on the device (N and cu_seqlens[N]). */
+ * what cu_seqlens holds on the device (N and cu_seqlens[N]).  Limits (so
+ * that every launch fits the dispatch grid; GDN_ERR_INVALID_VALUE beyond
+ * them): n_seqs * n_heads_v <= 2^21, n_heads_v <= 65535, and
+ * n_seqs + total_tokens / 64 + 1 <= 2^24 (about 10^9 tokens). */
 typedef struct {
     int32_t n_seqs;
     int64_t total_tokens;

@@ -86,6 +86,9 @@ def test_workspace_size_formula(lib):
     (dims(T=-5), gdn.GDN_ERR_INVALID_VALUE),
     (dims(n=0, T=10), gdn.GDN_ERR_INVALID_VALUE),
     (dims(T=2**31), gdn.GDN_ERR_INVALID_VALUE),
+    (dims(T=2**30), gdn.GDN_ERR_INVALID_VALUE),            # more than 2^24 chunk slots
+    (dims(n=2**16, hqk=32, hv=64), gdn.GDN_ERR_INVALID_VALUE),  # more than 2^21 (sequence, head) pairs
+    (dims(hqk=1, hv=70000), gdn.GDN_ERR_INVALID_VALUE),     # more value heads than a grid dimension holds
     (dims(dk=0), gdn.GDN_ERR_INVALID_VALUE),
 ])
 def test_workspace_size_rejects_bad_dims(lib, d, code):
