@@ -142,6 +142,74 @@ def make_dims(n_seqs: int, total_tokens: int, h_qk: int, h_v: int, d_k: int = 12
     return gdn_dims(int(n_seqs), int(total_tokens), int(h_qk), int(h_v), int(d_k), int(d_v))
 
 
+def _check_arg(x, name: str, dtypes, shape=None) -> None:
+    """Refuse a tensor argument whose dtype, shape or layout the kernels would
+    misread.  The C ABI sees bare addresses, so this is the only place where a
+    short or strided buffer can be caught before a kernel reads past it.  None
+    and int addresses pass unchecked (the caller then vouches for them)."""
+    if x is None or isinstance(x, int):
+        return
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise GDNError(GDN_ERR_INVALID_VALUE, f"{name} must be a tensor, a device address or None")
+    if dtypes is not None and x.dtype not in dtypes:
+        raise GDNError(GDN_ERR_INVALID_VALUE, f"{name} has dtype {x.dtype}, expected one of {list(dtypes)}")
+    if shape is not None and tuple(x.shape) != tuple(shape):
+        raise GDNError(GDN_ERR_INVALID_VALUE, f"{name} has shape {tuple(x.shape)}, expected {tuple(shape)}")
+    if not x.is_contiguous():
+        raise GDNError(GDN_ERR_INVALID_VALUE, f"{name} is not contiguous")
+    if not x.is_cuda:
+        raise GDNError(GDN_ERR_INVALID_VALUE, f"{name} is not a GPU tensor (there is no CPU path)")
+
+
+def _check_tokens(q, k, v, g, beta, out, dims: gdn_dims, what: str) -> None:
+    import torch
+    bf16, f32 = (torch.bfloat16,), (torch.float32,)
+    T, hqk, hv, dk, dv = dims.total_tokens, dims.n_heads_qk, dims.n_heads_v, dims.d_k, dims.d_v
+    _check_arg(q, f"{what}: q", bf16, (T, hqk, dk))
+    _check_arg(k, f"{what}: k", bf16, (T, hqk, dk))
+    _check_arg(v, f"{what}: v", bf16, (T, hv, dv))
+    _check_arg(g, f"{what}: g", f32, (T, hv))
+    _check_arg(beta, f"{what}: beta", f32, (T, hv))
+    _check_arg(out, f"{what}: out", f32, (T, hv, dv))
+
+
+def _check_prefill(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace,
+                   dims: gdn_dims, what: str) -> None:
+    import torch
+    _check_tokens(q, k, v, g, beta, out, dims, what)
+    state = (dims.n_seqs, dims.n_heads_v, dims.d_k, dims.d_v)
+    _check_arg(cu_seqlens, f"{what}: cu_seqlens", (torch.int32,), (dims.n_seqs + 1,))
+    _check_arg(initial_state, f"{what}: initial_state", (torch.float32,), state)
+    _check_arg(final_state, f"{what}: final_state", (torch.float32,), state)
+    _check_arg(workspace, f"{what}: workspace", None)
+
+
+def _nbytes(workspace, workspace_bytes: Optional[int]) -> int:
+    if workspace_bytes is not None:
+        return int(workspace_bytes)
+    if workspace is None:
+        return 0
+    if isinstance(workspace, int):
+        raise GDNError(GDN_ERR_INVALID_VALUE, "workspace_bytes is required with a workspace address")
+    return workspace.numel() * workspace.element_size()
+
+
+def _dims_from(q, v, n_seqs: int, total_tokens: int) -> gdn_dims:
+    import torch
+    for name, t in (("q", q), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 3:
+            raise GDNError(GDN_ERR_INVALID_VALUE, f"{name} must be a [tokens, heads, dim] tensor unless dims is given")
+    return make_dims(n_seqs, total_tokens, q.shape[1], v.shape[1], q.shape[2], v.shape[2])
+
+
+def _prefill_dims(q, v, cu_seqlens) -> gdn_dims:
+    import torch
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1:
+        raise GDNError(GDN_ERR_INVALID_VALUE, "cu_seqlens must be a 1-D tensor unless dims is given")
+    return _dims_from(q, v, cu_seqlens.shape[0] - 1, q.shape[0] if hasattr(q, "shape") else 0)
+
+
 def gdn_chunk_fwd_workspace_size(n_seqs: int, total_tokens: int, h_qk: int, h_v: int,
                                  d_k: int = 128, d_v: int = 128) -> int:
     lib = load_library()
@@ -158,9 +226,9 @@ def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
     """Chunked prefill.  Tensors are device tensors (or raw int addresses with ``dims``)."""
     lib = load_library()
     if dims is None:
-        dims = make_dims(cu_seqlens.shape[0] - 1, q.shape[0], q.shape[1], v.shape[1], q.shape[2], v.shape[2])
-    if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        dims = _prefill_dims(q, v, cu_seqlens)
+    _check_prefill(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace, dims, "gdn_chunk_fwd")
+    workspace_bytes = _nbytes(workspace, workspace_bytes)
     st = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                            _ptr(initial_state), _ptr(out), _ptr(final_state), ctypes.byref(dims),
                            _ptr(workspace), int(workspace_bytes),
@@ -174,9 +242,9 @@ def gdn_chunk_fwd_stages(q, k, v, g, beta, cu_seqlens, initial_state, out, final
     """Selected stages of the chunked prefill (1 = prep, 2 = state with output)."""
     lib = load_library()
     if dims is None:
-        dims = make_dims(cu_seqlens.shape[0] - 1, q.shape[0], q.shape[1], v.shape[1], q.shape[2], v.shape[2])
-    if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        dims = _prefill_dims(q, v, cu_seqlens)
+    _check_prefill(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace, dims, "gdn_chunk_fwd_stages")
+    workspace_bytes = _nbytes(workspace, workspace_bytes)
     st = lib.gdn_chunk_fwd_stages(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                   _ptr(initial_state), _ptr(out), _ptr(final_state), ctypes.byref(dims),
                                   _ptr(workspace), int(workspace_bytes), int(stage_mask),
@@ -199,9 +267,15 @@ def gdn_chunk_fwd_snapshots(q, k, v, g, beta, cu_seqlens, initial_state, out, fi
     """Chunked prefill that also writes the state after every chunk (see include/gdn.h)."""
     lib = load_library()
     if dims is None:
-        dims = make_dims(cu_seqlens.shape[0] - 1, q.shape[0], q.shape[1], v.shape[1], q.shape[2], v.shape[2])
-    if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        dims = _prefill_dims(q, v, cu_seqlens)
+    _check_prefill(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace, dims, "gdn_chunk_fwd_snapshots")
+    if not isinstance(chunk_states, int):
+        import torch
+        slots = gdn_chunk_state_slots(dims.n_seqs, dims.total_tokens, dims.n_heads_qk, dims.n_heads_v,
+                                      dims.d_k, dims.d_v)
+        _check_arg(chunk_states, "gdn_chunk_fwd_snapshots: chunk_states", (torch.float32,),
+                   (slots, dims.n_heads_v, dims.d_k, dims.d_v))
+    workspace_bytes = _nbytes(workspace, workspace_bytes)
     st = lib.gdn_chunk_fwd_snapshots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                      _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(chunk_states),
                                      ctypes.byref(dims), _ptr(workspace), int(workspace_bytes),
@@ -226,9 +300,9 @@ def gdn_chunk_fwd_segmented(q, k, v, g, beta, cu_seqlens, initial_state, out, fi
     """Chunked prefill with the recurrence parallel over segments (see include/gdn.h)."""
     lib = load_library()
     if dims is None:
-        dims = make_dims(cu_seqlens.shape[0] - 1, q.shape[0], q.shape[1], v.shape[1], q.shape[2], v.shape[2])
-    if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        dims = _prefill_dims(q, v, cu_seqlens)
+    _check_prefill(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace, dims, "gdn_chunk_fwd_segmented")
+    workspace_bytes = _nbytes(workspace, workspace_bytes)
     st = lib.gdn_chunk_fwd_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                      _ptr(initial_state), _ptr(out), _ptr(final_state), int(segment_chunks),
                                      ctypes.byref(dims), _ptr(workspace), int(workspace_bytes),
@@ -242,8 +316,14 @@ def gdn_recurrent_step(q, k, v, g, beta, n_requests: int, tokens_per_request: in
     """Per-token update for decode / speculative verify (see include/gdn.h)."""
     lib = load_library()
     if dims is None:
-        dims = make_dims(n_requests, n_requests * tokens_per_request, q.shape[1], v.shape[1],
-                         q.shape[2], v.shape[2])
+        dims = _dims_from(q, v, n_requests, n_requests * tokens_per_request)
+    import torch
+    _check_tokens(q, k, v, g, beta, out, dims, "gdn_recurrent_step")
+    state = (dims.n_seqs, dims.n_heads_v, dims.d_k, dims.d_v)
+    _check_arg(state_in, "gdn_recurrent_step: state_in", (torch.float32,), state)
+    _check_arg(state_out, "gdn_recurrent_step: state_out", (torch.float32,), state)
+    _check_arg(intermediate_states, "gdn_recurrent_step: intermediate_states", (torch.float32,),
+               (dims.n_seqs, tokens_per_request) + state[1:])
     st = lib.gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 int(n_requests), int(tokens_per_request),
                                 _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(intermediate_states),
@@ -272,11 +352,20 @@ def gdn_recurrent_step_slots(q, k, v, g, beta, cu_tokens, n_requests: int, max_t
     """
     lib = load_library()
     if dims is None:
-        dims = make_dims(n_requests, q.shape[0], q.shape[1], v.shape[1], q.shape[2], v.shape[2])
+        dims = _dims_from(q, v, n_requests, q.shape[0])
     if state_dtype is None:
         state_dtype = _state_dtype(state_pool)
     if pool_slots is None:
         pool_slots = state_pool.shape[0]
+    import torch
+    _check_tokens(q, k, v, g, beta, out, dims, "gdn_recurrent_step_slots")
+    i32 = (torch.int32,)
+    _check_arg(cu_tokens, "gdn_recurrent_step_slots: cu_tokens", i32, (dims.n_seqs + 1,))
+    _check_arg(state_pool, "gdn_recurrent_step_slots: state_pool",
+               (torch.float16,) if state_dtype == GDN_STATE_F16 else (torch.float32,),
+               (pool_slots, dims.n_heads_v, dims.d_k, dims.d_v))
+    _check_arg(slot_table, "gdn_recurrent_step_slots: slot_table", i32, (dims.n_seqs, int(max_tokens) + 1))
+    _check_arg(num_accepted, "gdn_recurrent_step_slots: num_accepted", i32, (dims.n_seqs,))
     st = lib.gdn_recurrent_step_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_tokens),
                                       int(n_requests), int(max_tokens), _ptr(state_pool), int(state_dtype),
                                       int(pool_slots), _ptr(slot_table), _ptr(num_accepted), _ptr(out),
