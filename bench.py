@@ -73,9 +73,9 @@ def algorithmic_work():
 # FETCH_SIZE / WRITE_SIZE runs scaled by a plain 1 GiB copy (fetch x 2.0,
 # write x 1.0); valid only for the kernel source they were taken with.
 MEASURED_TRAFFIC = {
-    "gdn_chunk_prep": {"bytes": 181955463, "source_sha256_prefix": "1b9cc0c493f6fcd3",
+    "gdn_chunk_prep": {"bytes": 181931982, "source_sha256_prefix": "a69f0960f6972ce7",
                        "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
-    "gdn_chunk_state": {"bytes": 180345006, "source_sha256_prefix": "1b9cc0c493f6fcd3",
+    "gdn_chunk_state": {"bytes": 180418084, "source_sha256_prefix": "a69f0960f6972ce7",
                         "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
 }
 

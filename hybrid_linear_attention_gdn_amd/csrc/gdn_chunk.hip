@@ -506,13 +506,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 //     one chunk ahead), and hands U' and the new state, rounded to fp16 as B
 //     operands, to the output wave through double-buffered LDS slots;
 //   * the output wave forms O = diag(e^G) (Q H0) + P U' on its own SIMD:
-//     the Q H0 half in the interval of the chunk (Q fragments and e^G from
-//     the stage), the P U' half one interval later, when U' has been handed
-//     over (P by register loads one chunk ahead); it stores O to global
-//     memory;
-//   * the copy wave issues direct global-to-LDS copies of -W, K^T, Q and the
+//     the Q H0 half in the interval of the chunk (Q fragments by register
+//     loads one interval ahead, e^G from the stage), the P U' half one
+//     interval later, when U' has been handed over (P by register loads in
+//     the chunk's interval); it stores O to global memory.  Taking Q
+//     straight to its registers keeps 16 KB per chunk off the copy wave and
+//     out of LDS;
+//   * the copy wave issues direct global-to-LDS copies of -W, K^T and the
 //     decay vectors into a ring of three stages, two chunks ahead, and
-//     touches the operands of the chunk two beyond those into L2.
+//     touches the operands of the chunk two beyond those (Q, U and P
+//     included) into L2.
 // The waves meet at one barrier per chunk.  The copy wave issues a fixed
 // number of copies per chunk, so one memory-counter wait makes a stage ready
 // before that barrier.  The eight tiles of a head run on one XCD so that its
@@ -523,13 +526,11 @@ constexpr int kStages = 3;
 constexpr int kUTile = 4 * 64 * 4;                           // halves of U fragments per column tile
 constexpr int kHbElems = 4 * 64 * 8;                         // halves of the state's four B fragments
 constexpr int kUbElems = 2 * 64 * 8;                         // halves of U''s two B fragments
-constexpr int kCopiesPerChunk = 16 + 16 + 16 + 2;            // -W, K^T, Q, decay vectors
-constexpr int kCopiesPerChunkMap = 16 + 16 + 2;              // without the output's Q
+constexpr int kCopiesPerChunk = 16 + 16 + 2;                 // -W, K^T, decay vectors
 
 struct StateStage {
     f16 w[kWElems];
     f16 k[kKtElems];
-    f16 q[kQfElems];
     float dg[kGElems];        // e^{G_C - G_r} (r < 63) and e^{G_C} in entry 63; then e^{G_r}
 };
 
@@ -550,21 +551,17 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// One chunk's copies: 1 KB pieces (16 B per lane) of -W, K^T and Q, and the
+// One chunk's copies: 1 KB pieces (16 B per lane) of -W and K^T, and the
 // two 256 B decay vectors (4 B per lane).
-template <bool kOut>
 __device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace& ws, size_t vu, size_t ku,
                                            int lane) {
     const f16* wsrc = ws.w + vu * kWElems;
     const f16* ksrc = ws.kt + ku * kKtElems;
-    const f16* qsrc = ws.qf + ku * kQfElems;
     const float* gsrc = ws.dg + vu * kGElems;
 #pragma unroll
     for (int piece = 0; piece < 16; ++piece) {
         __builtin_amdgcn_global_load_lds(wsrc + (piece * 64 + lane) * 8, st.w + piece * 512, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(ksrc + (piece * 64 + lane) * 8, st.k + piece * 512, 16, 0, 0);
-        if constexpr (kOut)
-            __builtin_amdgcn_global_load_lds(qsrc + (piece * 64 + lane) * 8, st.q + piece * 512, 16, 0, 0);
     }
     // (the casts keep these 4-byte copies from tripping a code-generation
     //  fault of the ROCm 7.2 compiler in this kernel)
@@ -610,6 +607,19 @@ __device__ __forceinline__ UFrag load_u(const ChunkWorkspace& ws, size_t vu, int
 #pragma unroll
     for (int p = 0; p < 4; ++p) u.f[p] = *reinterpret_cast<const f16x4*>(src + (p * 64 + lane) * 4);
     return u;
+}
+
+// Q's 16 fragments of one chunk, as sixteen 16-byte register loads.
+struct QFrag {
+    f16x8 f[16];
+};
+
+__device__ __forceinline__ QFrag load_q(const ChunkWorkspace& ws, size_t ku, int lane) {
+    const f16* src = ws.qf + ku * kQfElems;
+    QFrag qf;
+#pragma unroll
+    for (int f = 0; f < 16; ++f) qf.f[f] = *reinterpret_cast<const f16x8*>(src + (f * 64 + lane) * 8);
+    return qf;
 }
 
 // P's six nonzero A fragments of one chunk, as six 16-byte register loads.
@@ -699,7 +709,8 @@ __device__ __forceinline__ void chain_chunk(f32x4 (&H)[8], f16x8 (&hb)[4], const
 // of the tile.
 
 // The output wave's first half of a chunk: diag(e^G) (Q H0) into oacc.
-__device__ __forceinline__ void out_begin(f32x4 (&oacc)[4], const StateStage& st, const f16* hsrc, int lane, int ln) {
+__device__ __forceinline__ void out_begin(f32x4 (&oacc)[4], const StateStage& st, const QFrag& qf, const f16* hsrc,
+                                          int lane, int ln) {
     f16x8 hb[4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) hb[qq] = *reinterpret_cast<const f16x8*>(&hsrc[(qq * 64 + lane) * 8]);
@@ -707,7 +718,7 @@ __device__ __forceinline__ void out_begin(f32x4 (&oacc)[4], const StateStage& st
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) qa[qq][p] = *reinterpret_cast<const f16x8*>(&st.q[((p * 4 + qq) * 64 + lane) * 8]);
+        for (int p = 0; p < 4; ++p) qa[qq][p] = qf.f[p * 4 + qq];
 #pragma unroll
     for (int p = 0; p < 4; ++p) oacc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -921,40 +932,48 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
     } else if (role < kCopyRole) {
         // the output wave: Q H0 of chunk c between B_c and B_{c+1}, from the
         // state the chain wave handed over before B_c; P U' of chunk c one
-        // interval later, from the U' handed over before B_{c+1}.  P comes by
-        // register loads one chunk ahead.
+        // interval later, from the U' handed over before B_{c+1}.  Q and P
+        // come by register loads.
         if (c_end > c_begin) {
-            PFrag pn = load_p(ws, vidx(c_begin), lane);
-            PFrag pc;
+            // unrolled by two so that the loaded fragments never need a
+            // register copy (which would wait for the loads): Q of chunk c
+            // is loaded one interval ahead, P of chunk c in its interval
+            QFrag q0 = load_q(ws, kidx(c_begin), lane), q1;
+            PFrag p0, p1;
             f32x4 oacc[4];
+            auto end_of = [&](int cc, const PFrag& pf) {
+                const int t0 = start + kChunk * cc;
+                out_end(oacc, pf, ubuf[(cc - c_begin) & 1], out + ((size_t)t0 * h_v + h) * kDim + 16 * ct,
+                        (size_t)h_v * kDim, min(kChunk, end - t0), ws.junk, lane, gq, ln);
+            };
             lds_barrier();                                   // B_0
-            for (int c = c_begin; c < c_end; ++c) {
-                if (c > c_begin) {
-                    const int t0 = start + kChunk * (c - 1);
-                    out_end(oacc, pc, ubuf[(c - 1 - c_begin) & 1],
-                            out + ((size_t)t0 * h_v + h) * kDim + 16 * ct, (size_t)h_v * kDim,
-                            min(kChunk, end - t0), ws.junk, lane, gq, ln);
-                }
-                pc = pn;
-                pn = load_p(ws, vidx(c + 1), lane);           // clamped past the end
-                out_begin(oacc, stage[(c - c_begin) % kStages], hbuf[(c - c_begin) & 1], lane, ln);
+            for (int c = c_begin; c < c_end; c += 2) {
+                if (c > c_begin) end_of(c - 1, p1);
+                p0 = load_p(ws, vidx(c), lane);
+                q1 = load_q(ws, kidx(c + 1), lane);          // clamped past the end
+                out_begin(oacc, stage[(c - c_begin) % kStages], q0, hbuf[(c - c_begin) & 1], lane, ln);
                 lds_barrier();                               // B_{c+1}
+                if (c + 1 == c_end) break;
+                end_of(c, p0);
+                p1 = load_p(ws, vidx(c + 1), lane);
+                q0 = load_q(ws, kidx(c + 2), lane);
+                out_begin(oacc, stage[(c + 1 - c_begin) % kStages], q1, hbuf[(c + 1 - c_begin) & 1], lane, ln);
+                lds_barrier();                               // B_{c+2}
             }
-            const int t0 = start + kChunk * (c_end - 1);
-            out_end(oacc, pc, ubuf[(c_end - 1 - c_begin) & 1], out + ((size_t)t0 * h_v + h) * kDim + 16 * ct,
-                    (size_t)h_v * kDim, min(kChunk, end - t0), ws.junk, lane, gq, ln);
+            if (((c_end - 1 - c_begin) & 1) == 0) end_of(c_end - 1, p0);
+            else end_of(c_end - 1, p1);
         }
     } else if (c_end > c_begin) {
         // copies for chunks past the last one are issued too (clamped, never
         // used) so the number of copies per chunk never changes
-        constexpr int kCopies = kOut ? kCopiesPerChunk : kCopiesPerChunkMap;
-        state_copy<kOut>(stage[0], ws, vidx(c_begin), kidx(c_begin), lane);
-        state_copy<kOut>(stage[1], ws, vidx(c_begin + 1), kidx(c_begin + 1), lane);
+        constexpr int kCopies = kCopiesPerChunk;
+        state_copy(stage[0], ws, vidx(c_begin), kidx(c_begin), lane);
+        state_copy(stage[1], ws, vidx(c_begin + 1), kidx(c_begin + 1), lane);
         wait_vmcnt<kCopies>();                               // the first chunk has landed
         lds_barrier();                                       // B_0
         for (int c = c_begin; c < c_end; ++c) {
             // between B_c and B_{c+1}: the chain and output waves work on chunk c
-            state_copy<kOut>(stage[(c - c_begin + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), lane);
+            state_copy(stage[(c - c_begin + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), lane);
             state_touch(ws, vidx(c + 4), kidx(c + 4), ct, lane, touch_sink);
             wait_vmcnt<kCopies + kTouchesPerChunk>();            // chunk c + 1 has landed
             lds_barrier();                                   // B_{c+1}
