@@ -365,6 +365,29 @@ def main():
         "pct_hbm_peak": 100 * s_bytes / t_slots / PEAK_HBM,
     }
 
+    # ---------------- decode: the same 8 requests, one token each (the first of
+    #                  each request's verify tokens), state advanced in place
+    dq, dk, dv = (t[::n_tok].contiguous() for t in (vq, vk, vv))
+    dg, db = vg[::n_tok].contiguous(), vb[::n_tok].contiguous()
+    d_state = s_in.clone()
+    dout = torch.empty((R, H_V, D), device=dev)
+
+    def dstep():
+        gdn.gdn_recurrent_step(dq, dk, dv, dg, db, R, 1, d_state, d_state, dout, None, False)
+
+    for _ in range(args.warmup):
+        dstep()
+    t_decode = time_launches(dstep, args.steps, torch)
+    d_bytes = 2 * R * state_b + R * (2 * H_QK * D * 2 + H_V * D * 2 + 2 * H_V * 4 + H_V * D * 4)
+    decode = {
+        "workload": "decode_8req_1tok_hv32_hqk16_d128",
+        "us_per_step": t_decode * 1e6,
+        "tokens_per_s": R / t_decode,
+        "algorithmic_bytes": d_bytes,
+        "achieved_GBps": d_bytes / t_decode / 1e9,
+        "pct_hbm_peak": 100 * d_bytes / t_decode / PEAK_HBM,
+    }
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(x, args.cpu_seconds)
@@ -392,6 +415,7 @@ def main():
         "roofline": roof,
         "verify": verify,
         "verify_fp16_slots": verify_f16,
+        "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
