@@ -73,9 +73,9 @@ def algorithmic_work():
 # FETCH_SIZE / WRITE_SIZE runs scaled by a plain 1 GiB copy (fetch x 2.0,
 # write x 1.0); valid only for the kernel source they were taken with.
 MEASURED_TRAFFIC = {
-    "gdn_chunk_prep": {"bytes": 181931982, "source_sha256_prefix": "a69f0960f6972ce7",
+    "gdn_chunk_prep": {"bytes": 181932949, "source_sha256_prefix": "00c901044b57008c",
                        "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
-    "gdn_chunk_state": {"bytes": 180418084, "source_sha256_prefix": "a69f0960f6972ce7",
+    "gdn_chunk_state": {"bytes": 180763755, "source_sha256_prefix": "00c901044b57008c",
                         "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
 }
 

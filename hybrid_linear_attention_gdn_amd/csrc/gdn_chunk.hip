@@ -520,7 +520,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 // number of copies per chunk, so one memory-counter wait makes a stage ready
 // before that barrier.  The eight tiles of a head run on one XCD so that its
 // L2 serves the shared fragments.  An affine map has no output: its
-// workgroups have a chain and a copy wave only.
+// workgroups have a chain and a copy wave only.  When a batch has more tiles
+// than the GPU has CUs, so that the workgroups run in rounds, a workgroup
+// takes a pair of adjacent tiles: two chain waves on two SIMDs share the
+// copy ring (-W, K^T and the decay vectors are the same for both) and one
+// output wave forms both tiles' output from one set of Q and P fragments,
+// which halves the operand traffic per tile and the number of rounds.
 // ---------------------------------------------------------------------------
 constexpr int kStages = 3;
 constexpr int kUTile = 4 * 64 * 4;                           // halves of U fragments per column tile
@@ -796,18 +801,21 @@ enum : int {
     kModeWholeSnap = 1,      // the same, plus the state after every chunk
     kModeSegment = 2,        // one segment per workgroup, from its incoming state, with the output
     kModeMap = 3,            // the affine map (Phi, R) of one segment, no output
+    kModeWholePair = 4,      // whole sequences, two column tiles per workgroup, with the output
 };
 
 // Threads of a state workgroup: chain, output and copy waves; an affine map
-// has no output wave.
-__host__ __device__ constexpr int state_threads(int mode) { return mode == kModeMap ? 128 : 192; }
+// has no output wave; a tile pair has two chain waves.
+__host__ __device__ constexpr int state_threads(int mode) {
+    return mode == kModeMap ? 128 : mode == kModeWholePair ? 256 : 192;
+}
 
 // Workgroups of a state launch over `units` units of kTiles tiles each.
 constexpr unsigned state_grid(int units, int tiles) { return 8u * tiles * 2u * (unsigned)((units + 15) / 16); }
 
 // Grid: state_grid(U, kTiles) workgroups; U = n_seqs * h_v for whole
-// sequences, n_segslots * h_v for segments; kTiles = 8 column tiles, or 16
-// for a map (8 of Phi, 8 of R).  Workgroup b runs on XCD x = b % 8
+// sequences, n_segslots * h_v for segments; kTiles = 8 column tiles, 4 tile
+// pairs, or 16 for a map (8 of Phi, 8 of R).  Workgroup b runs on XCD x = b % 8
 // (round-robin dispatch); with m = b / 8 it takes tile m % kTiles of unit
 // 16 (g / 2) + 2 x + g % 2, g = m / kTiles.  All tiles of a unit share an
 // XCD, and so do units 2i and 2i + 1, the two value heads of a q/k head at
@@ -821,15 +829,16 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
 {
     constexpr bool kOut = kMode != kModeMap;
     constexpr bool kSnap = kMode == kModeWholeSnap;
-    constexpr int kTiles = kMode == kModeMap ? 16 : 8;
-    constexpr bool kSeg = kMode >= kModeSegment;
+    constexpr bool kPair = kMode == kModeWholePair;
+    constexpr int kChains = kPair ? 2 : 1;                   // chain waves: roles 0 .. kChains - 1
+    constexpr int kTiles = kMode == kModeMap ? 16 : kPair ? 4 : 8;
+    constexpr bool kSeg = kMode == kModeSegment || kMode == kModeMap;
     constexpr int kCopyRole = state_threads(kMode) / 64 - 1;
     const int b = blockIdx.x;
     const int m = b >> 3;
     const int gu = m / kTiles;
     const int unit = ((gu >> 1) << 4) + ((b & 7) << 1) + (gu & 1);
     const int tile = m % kTiles;
-    const int ct = tile & 7;
     int seq, h, sg = 0, nseg = 1, gs = 0;
     if constexpr (!kSeg) {
         if (unit >= n_seqs * h_v) return;
@@ -845,14 +854,17 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
     const int j = h / ws.group;
 
     const int lane = threadIdx.x & 63;
-    const int role = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0 chain, 1 output, last copy
+    // roles: chain waves first (one per column tile), then the output wave,
+    // then the copy wave
+    const int role = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int gq = lane >> 4;
     const int ln = lane & 15;
-    const int col = 16 * ct + ln;
+    // column tile of chain wave r (the output wave takes all of them)
+    auto tile_of = [&](int r) { return kPair ? 2 * tile + r : (tile & 7); };
 
     __shared__ __attribute__((aligned(16))) StateStage stage[kStages];
-    __shared__ __attribute__((aligned(16))) f16 hbuf[2][kHbElems];  // chain -> output: fp16 state
-    __shared__ __attribute__((aligned(16))) f16 ubuf[2][kUbElems];  // chain -> output: fp16 U'
+    __shared__ __attribute__((aligned(16))) f16 hbuf[kChains][2][kHbElems];  // chain -> output: fp16 state
+    __shared__ __attribute__((aligned(16))) f16 ubuf[kChains][2][kUbElems];  // chain -> output: fp16 U'
     __shared__ __attribute__((aligned(16))) float touch_sink[64];   // target of the L2 touches, never read
 
     const int start = cu[seq];
@@ -866,7 +878,9 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
     const size_t sbase = ((size_t)seq * h_v + h) * kDim * kDim;
     const size_t gbase = ((size_t)gs * h_v + h) * kDim * kDim;
 
-    if (role == 0) {
+    if (role < kChains) {
+        const int ct = tile_of(role);
+        const int col = 16 * ct + ln;
         f32x4 H[8];
         if (kMode == kModeMap) {
             // Phi starts at the identity (tiles 0-7), R at zero (tiles 8-15)
@@ -899,7 +913,7 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
         if (c_end > c_begin) {
             if constexpr (kOut) {
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<f16x8*>(&hbuf[0][(qq * 64 + lane) * 8]) = hb[qq];
+                for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<f16x8*>(&hbuf[role][0][(qq * 64 + lane) * 8]) = hb[qq];
             }
             UFrag un = load_u(ws, vidx(c_begin), ct, lane);
             lds_barrier();                                   // B_0: the first chunk has landed
@@ -911,8 +925,8 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
                                     : nullptr;
                 // U'(c) and H0(c + 1) for the output wave; the buffers it
                 // reads in this interval are the other ones
-                chain_chunk<kOut, kSnap>(H, hb, stage[(c - c_begin) % kStages], uc, ubuf[(c - c_begin) & 1],
-                                         hbuf[(c - c_begin + 1) & 1], snap, use_u, lane, gq, ln);
+                chain_chunk<kOut, kSnap>(H, hb, stage[(c - c_begin) % kStages], uc, ubuf[role][(c - c_begin) & 1],
+                                         hbuf[role][(c - c_begin + 1) & 1], snap, use_u, lane, gq, ln);
                 lds_barrier();                               // B_{c+1}
             }
         }
@@ -940,24 +954,32 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
             // is loaded one interval ahead, P of chunk c in its interval
             QFrag q0 = load_q(ws, kidx(c_begin), lane), q1;
             PFrag p0, p1;
-            f32x4 oacc[4];
+            f32x4 oacc[kChains][4];
             auto end_of = [&](int cc, const PFrag& pf) {
                 const int t0 = start + kChunk * cc;
-                out_end(oacc, pf, ubuf[(cc - c_begin) & 1], out + ((size_t)t0 * h_v + h) * kDim + 16 * ct,
-                        (size_t)h_v * kDim, min(kChunk, end - t0), ws.junk, lane, gq, ln);
+#pragma unroll
+                for (int r = 0; r < kChains; ++r)
+                    out_end(oacc[r], pf, ubuf[r][(cc - c_begin) & 1],
+                            out + ((size_t)t0 * h_v + h) * kDim + 16 * tile_of(r), (size_t)h_v * kDim,
+                            min(kChunk, end - t0), ws.junk, lane, gq, ln);
+            };
+            auto begin_of = [&](int cc, const QFrag& qf) {
+#pragma unroll
+                for (int r = 0; r < kChains; ++r)
+                    out_begin(oacc[r], stage[(cc - c_begin) % kStages], qf, hbuf[r][(cc - c_begin) & 1], lane, ln);
             };
             lds_barrier();                                   // B_0
             for (int c = c_begin; c < c_end; c += 2) {
                 if (c > c_begin) end_of(c - 1, p1);
                 p0 = load_p(ws, vidx(c), lane);
                 q1 = load_q(ws, kidx(c + 1), lane);          // clamped past the end
-                out_begin(oacc, stage[(c - c_begin) % kStages], q0, hbuf[(c - c_begin) & 1], lane, ln);
+                begin_of(c, q0);
                 lds_barrier();                               // B_{c+1}
                 if (c + 1 == c_end) break;
                 end_of(c, p0);
                 p1 = load_p(ws, vidx(c + 1), lane);
                 q0 = load_q(ws, kidx(c + 2), lane);
-                out_begin(oacc, stage[(c + 1 - c_begin) % kStages], q1, hbuf[(c + 1 - c_begin) & 1], lane, ln);
+                begin_of(c + 1, q1);
                 lds_barrier();                               // B_{c+2}
             }
             if (((c_end - 1 - c_begin) & 1) == 0) end_of(c_end - 1, p0);
@@ -973,9 +995,17 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
         lds_barrier();                                       // B_0
         for (int c = c_begin; c < c_end; ++c) {
             // between B_c and B_{c+1}: the chain and output waves work on chunk c
+            // the touches go out before the copies for one tile of whole
+            // sequences, after them for segments, maps and tile pairs (whose
+            // four touches would delay the copies): measured
+            constexpr bool kTouchFirst = kMode == kModeWhole || kMode == kModeWholeSnap;
+            if constexpr (kTouchFirst) state_touch(ws, vidx(c + 4), kidx(c + 4), tile_of(0), lane, touch_sink);
             state_copy(stage[(c - c_begin + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), lane);
-            state_touch(ws, vidx(c + 4), kidx(c + 4), ct, lane, touch_sink);
-            wait_vmcnt<kCopies + kTouchesPerChunk>();            // chunk c + 1 has landed
+            if constexpr (!kTouchFirst) {
+#pragma unroll
+                for (int r = 0; r < kChains; ++r) state_touch(ws, vidx(c + 4), kidx(c + 4), tile_of(r), lane, touch_sink);
+            }
+            wait_vmcnt<kCopies + kChains * kTouchesPerChunk>();  // chunk c + 1 has landed
             lds_barrier();                                   // B_{c+1}
         }
         // drain the copies past the end before the workgroup's LDS goes away
@@ -1051,6 +1081,15 @@ __global__ __launch_bounds__(256) void gdn_chunk_seg_scan(
 }  // namespace
 
 // ---------------------------------------------------------------------------
+// Compute units of the current device (host query, no device work).
+static int state_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    return n;
+}
+
 hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* g, const float* beta, const int32_t* cu,
                             int n_seqs, int64_t total_tokens, int h_qk, int h_v,
@@ -1069,6 +1108,12 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
             const dim3 grid(state_grid(units, 8));
             if (chunk_states)
                 hipLaunchKernelGGL(gdn_chunk_state<kModeWholeSnap>, grid, dim3(state_threads(kModeWholeSnap)), 0, stream,
+                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+            else if (8 * units > state_cus())
+                // more tiles than CUs: the workgroups run in rounds, and a
+                // pair of tiles sharing one copy ring halves them
+                hipLaunchKernelGGL(gdn_chunk_state<kModeWholePair>, dim3(state_grid(units, 4)),
+                                   dim3(state_threads(kModeWholePair)), 0, stream,
                                    cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
             else
                 hipLaunchKernelGGL(gdn_chunk_state<kModeWhole>, grid, dim3(state_threads(kModeWhole)), 0, stream,

@@ -389,3 +389,23 @@ def test_segmented_long_131072_sampled():
     so, sf = chunk_fwd(d, poison=False)
     assert rel_l2(out.cpu().numpy(), so.cpu().numpy()) <= OUT_TOL
     assert rel_l2(fin.cpu().numpy(), sf.cpu().numpy()) <= STATE_TOL
+
+
+def test_batch_with_more_tiles_than_cus_matches_separate_runs_bitwise():
+    """Nine sequences at 32 value heads are 2304 column tiles, more than the
+    CUs, so the state kernel runs them as tile pairs (two chain waves sharing
+    one copy ring); one sequence alone is 256 tiles and runs one tile per
+    workgroup.  The arithmetic per tile is the same either way: every output
+    row and final state of the batch equals the separate run's bit for bit,
+    and the batch matches the oracle."""
+    lengths = [300, 1, 129, 64, 700, 0, 65, 200, 33]
+    x = gi.make_inputs(lengths, 16, 32, 128, 128, seed=23, state_std=0.02)
+    out, fin = check_chunk(x, "batch_tile_pairs")
+    out, fin = out.cpu(), fin.cpu()
+    for n in range(len(lengths)):
+        xs = x.slice_seq(n)
+        _print_case(f"batch_tile_pairs[{n}] alone", xs)
+        o1, f1 = chunk_fwd(DevInputs(xs), poison=True)
+        a, b = int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1])
+        assert torch.equal(o1.cpu(), out[a:b]), n
+        assert torch.equal(f1.cpu()[0], fin[n]), n
