@@ -17,6 +17,10 @@ Printed as one JSON line:
              snapshots kept) timed the same way, as a fraction of HBM bandwidth
   verify_fp16_slots  the same verify over an fp16 state pool addressed through
              a slot table (gdn_recurrent_step_slots)
+  decode     the same 8 requests, one token each, state advanced in place
+  prefill_snapshots  the prefill that also writes the fp32 state after every
+             64-token chunk (gdn_chunk_fwd_snapshots, for a prefix cache), as
+             a fraction of HBM bandwidth on its bytes
   cpu_baseline  the CPU oracle (fp32 token recurrence) on host cores
 """
 
@@ -279,6 +283,19 @@ def main():
     t_cold = sorted(e[0].elapsed_time(e[1]) for e in cold_ev)[n_cold // 2] / 1e3
     del flush
 
+    # The same prefill writing the state after every chunk (a prefix cache's
+    # snapshots): 63 chunk states of 32 heads x 64 KB at T = 4000.
+    n_snap = gdn.gdn_chunk_state_slots(1, T, H_QK, H_V)
+    chunk_states = torch.empty((n_snap, H_V, D, D), dtype=torch.float32, device=dev)
+
+    def snap_step():
+        gdn.gdn_chunk_fwd_snapshots(q, k, v, g, beta, cu, None, out, fin, chunk_states, ws)
+
+    for _ in range(args.warmup):
+        snap_step()
+    t_snap = time_launches(snap_step, args.steps, torch)
+    del chunk_states
+
     work = algorithmic_work()
     state_bytes = H_V * D * D * 4          # one fp32 state per sequence (final state written)
     per_seq = {"prep": 0, "state": state_bytes, "layer": state_bytes}
@@ -311,6 +328,18 @@ def main():
         "stage_pct_of_roofline": {
             n: 100 * max(work[n][0] * T / PEAK_MFMA_F16, (work[n][1] * T + per_seq[n]) / PEAK_HBM) / stage_t[n]
             for n in stage_t},
+    }
+
+    snap_bytes = ((T + C - 1) // C) * state_bytes
+    snap_total = work["layer"][1] * T + per_seq["layer"] + snap_bytes
+    prefill_snapshots = {
+        "workload": x.name + "_chunk_snapshots",
+        "us_per_step": t_snap * 1e6,
+        "tokens_per_s": T / t_snap,
+        "snapshot_bytes": snap_bytes,
+        "algorithmic_bytes": snap_total,
+        "pct_hbm_peak": 100 * snap_total / t_snap / PEAK_HBM,
+        "us_over_prefill": (t_snap - t_step) * 1e6,
     }
 
     # ---------------- verify workload: 8 requests x (1 + 5) tokens, snapshots kept
@@ -416,6 +445,7 @@ def main():
         "verify": verify,
         "verify_fp16_slots": verify_f16,
         "decode": decode,
+        "prefill_snapshots": prefill_snapshots,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
