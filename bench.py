@@ -77,9 +77,9 @@ def algorithmic_work():
 # FETCH_SIZE / WRITE_SIZE runs scaled by a plain 1 GiB copy (fetch x 2.0,
 # write x 1.0); valid only for the kernel source they were taken with.
 MEASURED_TRAFFIC = {
-    "gdn_chunk_prep": {"bytes": 181932949, "source_sha256_prefix": "00c901044b57008c",
+    "gdn_chunk_prep": {"bytes": 181992049, "source_sha256_prefix": "41da3e4fe513d85b",
                        "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
-    "gdn_chunk_state": {"bytes": 180763755, "source_sha256_prefix": "00c901044b57008c",
+    "gdn_chunk_state": {"bytes": 180630578, "source_sha256_prefix": "41da3e4fe513d85b",
                         "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
 }
 

@@ -698,10 +698,14 @@ __device__ __forceinline__ void chain_chunk(f32x4 (&H)[8], f16x8 (&hb)[4], const
         for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<f16x8*>(&hd[(qq * 64 + lane) * 8]) = hb[qq];
     }
     if constexpr (kSnap) {
+        // non-temporal: 64 KB per head and chunk that this launch never reads
+        // back, kept from evicting the chunks touched ahead in L2 (measured:
+        // 122 -> 103 us per 4000-token prefill)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) snap[(size_t)(16 * i + 4 * gq + e) * kDim + ln] = H[i][e];
+            for (int e = 0; e < 4; ++e)
+                __builtin_nontemporal_store(H[i][e], &snap[(size_t)(16 * i + 4 * gq + e) * kDim + ln]);
     }
 }
 
