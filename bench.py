@@ -78,7 +78,7 @@ def algorithmic_work():
 # write x 1.0); valid only for the kernel source they were taken with.
 MEASURED_TRAFFIC = {
     "gdn_chunk_prep": {"bytes": 181992049, "source_sha256_prefix": "41da3e4fe513d85b",
-                       "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
+                       "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_prep.h"},
     "gdn_chunk_state": {"bytes": 180630578, "source_sha256_prefix": "41da3e4fe513d85b",
                         "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
 }

@@ -17,6 +17,16 @@ struct SegLaunch {
     float* maps;        // [n_segslots][h_v][2][128][128]
 };
 
+// Enqueues the intra-chunk preparation (one workgroup per chunk slot and
+// value head) on `stream`, with ordinary or with non-temporal stores of the
+// intermediates.
+hipError_t launch_prep(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
+                       const int32_t* cu, int n_seqs, int h_qk, int h_v, const ChunkWorkspace& ws, int n_slots,
+                       hipStream_t stream);
+hipError_t launch_prep_stream(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                              const float* beta, const int32_t* cu, int n_seqs, int h_qk, int h_v,
+                              const ChunkWorkspace& ws, int n_slots, hipStream_t stream);
+
 // Enqueues the chunked prefill on `stream`: prep (stage bit 0) and the state
 // recurrence with the output (stage bit 1); chunk_states may be null; seg
 // null runs each sequence's recurrence in one workgroup per column tile.

@@ -1,0 +1,18 @@
+// The intra-chunk preparation kernel with ordinary stores (one store kind per
+// translation unit; see gdn_prep.h).
+
+#include "gdn_prep.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+hipError_t launch_prep(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
+                       const int32_t* cu, int n_seqs, int h_qk, int h_v, const ChunkWorkspace& ws, int n_slots,
+                       hipStream_t stream)
+{
+    hipLaunchKernelGGL(gdn_chunk_prep<false>, dim3(n_slots, h_v), dim3(256), 0, stream,
+                       q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

