@@ -77,9 +77,9 @@ def algorithmic_work():
 # FETCH_SIZE / WRITE_SIZE runs scaled by a plain 1 GiB copy (fetch x 2.0,
 # write x 1.0); valid only for the kernel source they were taken with.
 MEASURED_TRAFFIC = {
-    "gdn_chunk_prep": {"bytes": 181992049, "source_sha256_prefix": "41da3e4fe513d85b",
+    "gdn_chunk_prep": {"bytes": 181953684, "source_sha256_prefix": "0ac48beff45649f9",
                        "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_prep.h"},
-    "gdn_chunk_state": {"bytes": 180630578, "source_sha256_prefix": "41da3e4fe513d85b",
+    "gdn_chunk_state": {"bytes": 180862315, "source_sha256_prefix": "23480474e6f8abee",
                         "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
 }
 
