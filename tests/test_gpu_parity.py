@@ -409,3 +409,27 @@ def test_batch_with_more_tiles_than_cus_matches_separate_runs_bitwise():
         a, b = int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1])
         assert torch.equal(o1.cpu(), out[a:b]), n
         assert torch.equal(f1.cpu()[0], fin[n]), n
+
+
+def test_streaming_prep_matches_ordinary_prep_bitwise():
+    """Prep writes its intermediates with non-temporal stores once they exceed
+    160 MiB, and with ordinary stores below.  The store kind changes no value:
+    the eight-sequence varlen batch (~0.5 GB of intermediates, streaming prep)
+    equals each of its sequences run alone (at most ~0.11 GB, ordinary prep)
+    bit for bit, outputs and final states."""
+    import hybrid_linear_attention_gdn_amd as gdn
+    x = gi.varlen_8()
+    big = gdn.gdn_chunk_fwd_workspace_size(x.n_seqs, x.total_tokens, x.h_qk, x.h_v)
+    assert big > 170 << 20, big
+    _print_case("varlen_8 streaming prep", x)
+    out, fin = chunk_fwd(DevInputs(x), poison=True)
+    out, fin = out.cpu(), fin.cpu()
+    for n in range(x.n_seqs):
+        xs = x.slice_seq(n)
+        small = gdn.gdn_chunk_fwd_workspace_size(1, xs.total_tokens, xs.h_qk, xs.h_v)
+        assert small < 150 << 20, small
+        _print_case(f"varlen_8[{n}] alone, ordinary prep", xs)
+        o1, f1 = chunk_fwd(DevInputs(xs), poison=True)
+        a, b = int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1])
+        assert torch.equal(o1.cpu(), out[a:b]), n
+        assert torch.equal(f1.cpu()[0], fin[n]), n
