@@ -18,6 +18,8 @@ Printed as one JSON line:
   verify_fp16_slots  the same verify over an fp16 state pool addressed through
              a slot table (gdn_recurrent_step_slots)
   decode     the same 8 requests, one token each, state advanced in place
+             (verify and decode also replayed from a HIP graph of 20 calls:
+             *_graph, the launch cost a serving loop does not pay per step)
   prefill_snapshots  the prefill that also writes the fp32 state after every
              64-token chunk (gdn_chunk_fwd_snapshots, for a prefix cache), as
              a fraction of HBM bandwidth on its bytes
@@ -107,6 +109,27 @@ def time_launches(fn, n, torch):
     e1.record(s)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / 1e3 / n
+
+
+def time_graph(fn, n_inner, reps, torch):
+    """Mean time per call of fn() replayed from a HIP graph of n_inner calls
+    (captured once; the calls allocate nothing and launch on the current
+    stream), as a serving loop replays its decode step."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n_inner):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    t = time_launches(g.replay, reps, torch) / n_inner
+    del g
+    return t
 
 
 def cpu_baseline(x, budget_s: float):
@@ -360,6 +383,7 @@ def main():
     for _ in range(args.warmup):
         vstep()
     t_verify = time_launches(vstep, args.steps, torch)
+    t_verify_graph = time_graph(vstep, 20, max(1, args.steps // 20), torch)
     state_b = H_V * D * D * 4
     v_bytes = R * state_b + R * n_tok * state_b + R * n_tok * (2 * H_QK * D * 2 + H_V * D * 2 + 2 * H_V * 4 + H_V * D * 4)
     verify = {
@@ -369,6 +393,8 @@ def main():
         "algorithmic_bytes": v_bytes,
         "achieved_GBps": v_bytes / t_verify / 1e9,
         "pct_hbm_peak": 100 * v_bytes / t_verify / PEAK_HBM,
+        "us_per_step_graph": t_verify_graph * 1e6,
+        "pct_hbm_peak_graph": 100 * v_bytes / t_verify_graph / PEAK_HBM,
     }
 
     # ---------------- the same verify over an fp16 slot pool (state slots picked by
@@ -407,6 +433,7 @@ def main():
     for _ in range(args.warmup):
         dstep()
     t_decode = time_launches(dstep, args.steps, torch)
+    t_decode_graph = time_graph(dstep, 20, max(1, args.steps // 20), torch)
     d_bytes = 2 * R * state_b + R * (2 * H_QK * D * 2 + H_V * D * 2 + 2 * H_V * 4 + H_V * D * 4)
     decode = {
         "workload": "decode_8req_1tok_hv32_hqk16_d128",
@@ -415,6 +442,8 @@ def main():
         "algorithmic_bytes": d_bytes,
         "achieved_GBps": d_bytes / t_decode / 1e9,
         "pct_hbm_peak": 100 * d_bytes / t_decode / PEAK_HBM,
+        "us_per_step_graph": t_decode_graph * 1e6,
+        "pct_hbm_peak_graph": 100 * d_bytes / t_decode_graph / PEAK_HBM,
     }
 
     cpu = None

@@ -22,7 +22,10 @@
  *  - All tensor pointers are DEVICE pointers on the current HIP device, owned
  *    by the caller.  The library allocates nothing, keeps no device state and
  *    is re-entrant; calls are asynchronous on `stream` (a hipStream_t, NULL =
- *    the default stream).
+ *    the default stream).  A call enqueues only kernel launches on `stream`
+ *    (no allocation, copy, memset or synchronisation), so it may be captured
+ *    into a HIP graph and replayed; every replay reads the buffers the
+ *    captured call named, with their contents at replay time.
  *  - Layouts are dense, row-major, token-major:
  *      q, k : [T, H_qk, d_k]  bfloat16      v : [T, H_v, d_v]  bfloat16
  *      g    : [T, H_v] float32 natural-log decay (alpha = exp(g), g <= 0)
