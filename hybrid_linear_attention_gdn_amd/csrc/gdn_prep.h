@@ -492,6 +492,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
 }
 
+// Grid width of a prep launch: the chunk slots rounded up to a multiple of 8.
+// Workgroup (slot, h) has the linear index slot + width * h and runs on XCD
+// index % 8, so with the width a multiple of 8 every value head of a chunk
+// slot runs on the same XCD, and the value heads of a q/k head, which read
+// the same q and k rows, share that XCD's L2.  The padding workgroups find
+// no chunk and leave at once.
+__host__ __forceinline__ unsigned slots_x8(int n_slots) { return ((unsigned)n_slots + 7u) & ~7u; }
+
 }  // namespace
 
 }  // namespace gdn

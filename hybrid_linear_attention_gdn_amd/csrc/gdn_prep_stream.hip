@@ -10,7 +10,7 @@ hipError_t launch_prep_stream(const uint16_t* q, const uint16_t* k, const uint16
                               const int32_t* cu, int n_seqs, int h_qk, int h_v, const ChunkWorkspace& ws, int n_slots,
                               hipStream_t stream)
 {
-    hipLaunchKernelGGL(gdn_chunk_prep<true>, dim3(n_slots, h_v), dim3(256), 0, stream,
+    hipLaunchKernelGGL(gdn_chunk_prep<true>, dim3(slots_x8(n_slots), h_v), dim3(256), 0, stream,
                        q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws);
     return hipGetLastError();
 }
