@@ -344,20 +344,32 @@ enum : int {
     kModeSegment = 2,        // one segment per workgroup, from its incoming state, with the output
     kModeMap = 3,            // the affine map (Phi, R) of one segment, no output
     kModeWholePair = 4,      // whole sequences, two column tiles per workgroup, with the output
+    kModeSegmentPair = 5,    // segments, two column tiles per workgroup, with the output
+    kModeMapPair = 6,        // segment maps, two column tiles (of Phi or of R) per workgroup
 };
+
+__host__ __device__ constexpr bool mode_pair(int mode) {
+    return mode == kModeWholePair || mode == kModeSegmentPair || mode == kModeMapPair;
+}
+
+// The mode a tile-pair mode runs per tile.
+__host__ __device__ constexpr int mode_base(int mode) {
+    return mode == kModeWholePair ? kModeWhole : mode == kModeSegmentPair ? kModeSegment
+                                               : mode == kModeMapPair ? kModeMap : mode;
+}
 
 // Threads of a state workgroup: chain, output and copy waves; an affine map
 // has no output wave; a tile pair has two chain waves.
 __host__ __device__ constexpr int state_threads(int mode) {
-    return mode == kModeMap ? 128 : mode == kModeWholePair ? 256 : 192;
+    return 64 * ((mode_pair(mode) ? 2 : 1) + (mode_base(mode) == kModeMap ? 0 : 1) + 1);
 }
 
 // Workgroups of a state launch over `units` units of kTiles tiles each.
 constexpr unsigned state_grid(int units, int tiles) { return 8u * tiles * 2u * (unsigned)((units + 15) / 16); }
 
 // Grid: state_grid(U, kTiles) workgroups; U = n_seqs * h_v for whole
-// sequences, n_segslots * h_v for segments; kTiles = 8 column tiles, 4 tile
-// pairs, or 16 for a map (8 of Phi, 8 of R).  Workgroup b runs on XCD x = b % 8
+// sequences, n_segslots * h_v for segments; kTiles = 8 column tiles or 4
+// tile pairs, for a map 16 (8 of Phi, 8 of R) or 8 pairs.  Workgroup b runs on XCD x = b % 8
 // (round-robin dispatch); with m = b / 8 it takes tile m % kTiles of unit
 // 16 (g / 2) + 2 x + g % 2, g = m / kTiles.  All tiles of a unit share an
 // XCD, and so do units 2i and 2i + 1, the two value heads of a q/k head at
@@ -369,12 +381,13 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
     const float* s0, float* s_final, float* __restrict__ out, float* __restrict__ chunk_states,
     ChunkWorkspace ws, SegArgs sa)
 {
-    constexpr bool kOut = kMode != kModeMap;
-    constexpr bool kSnap = kMode == kModeWholeSnap;
-    constexpr bool kPair = kMode == kModeWholePair;
+    constexpr int kBase = mode_base(kMode);
+    constexpr bool kOut = kBase != kModeMap;
+    constexpr bool kSnap = kBase == kModeWholeSnap;
+    constexpr bool kPair = mode_pair(kMode);
     constexpr int kChains = kPair ? 2 : 1;                   // chain waves: roles 0 .. kChains - 1
-    constexpr int kTiles = kMode == kModeMap ? 16 : kPair ? 4 : 8;
-    constexpr bool kSeg = kMode == kModeSegment || kMode == kModeMap;
+    constexpr int kTiles = (kBase == kModeMap ? 16 : 8) / kChains;
+    constexpr bool kSeg = kBase == kModeSegment || kBase == kModeMap;
     constexpr int kCopyRole = state_threads(kMode) / 64 - 1;
     const int b = blockIdx.x;
     const int m = b >> 3;
@@ -391,7 +404,7 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
         gs = unit / h_v;
         h = unit % h_v;
         if (!resolve_segslot(cu, n_seqs, gs, sa.seg_chunks, seq, sg, nseg)) return;
-        if (kMode == kModeMap && sg >= nseg - 1) return;    // the last segment needs no map
+        if (kBase == kModeMap && sg >= nseg - 1) return;    // the last segment needs no map
     }
     const int j = h / ws.group;
 
@@ -401,8 +414,10 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
     const int role = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int gq = lane >> 4;
     const int ln = lane & 15;
-    // column tile of chain wave r (the output wave takes all of them)
-    auto tile_of = [&](int r) { return kPair ? 2 * tile + r : (tile & 7); };
+    // tile of chain wave r among the unit's tiles (a map's 0-7 are Phi's,
+    // 8-15 R's), and its column tile (the output wave takes all of them)
+    auto gtile_of = [&](int r) { return kPair ? 2 * tile + r : tile; };
+    auto tile_of = [&](int r) { return kBase == kModeMap ? gtile_of(r) & 7 : kPair ? 2 * tile + r : (tile & 7); };
 
     __shared__ __attribute__((aligned(16))) StateStage stage[kStages];
     __shared__ __attribute__((aligned(16))) f16 hbuf[kChains][2][kHbElems];  // chain -> output: fp16 state
@@ -422,15 +437,16 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
 
     if (role < kChains) {
         const int ct = tile_of(role);
+        const bool phi = gtile_of(role) < 8;                 // a map's Phi tile
         const int col = 16 * ct + ln;
         f32x4 H[8];
-        if (kMode == kModeMap) {
+        if (kBase == kModeMap) {
             // Phi starts at the identity (tiles 0-7), R at zero (tiles 8-15)
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    H[i][e] = (tile < 8 && 16 * i + 4 * gq + e == col) ? 1.f : 0.f;
+                    H[i][e] = (phi && 16 * i + 4 * gq + e == col) ? 1.f : 0.f;
         } else if (kSeg && sg > 0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -451,7 +467,7 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
         f16x8 hb[4];
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) hb[qq] = cat_to_f16(H[2 * qq], H[2 * qq + 1]);
-        const bool use_u = !(kMode == kModeMap && tile < 8);   // Phi: the homogeneous part
+        const bool use_u = !(kBase == kModeMap && phi);      // Phi: the homogeneous part
         if (c_end > c_begin) {
             if constexpr (kOut) {
 #pragma unroll
@@ -472,8 +488,8 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
                 lds_barrier();                               // B_{c+1}
             }
         }
-        if (kMode == kModeMap) {
-            float* dst = sa.maps + (gbase * 2 + (tile < 8 ? 0 : (size_t)kDim * kDim));
+        if (kBase == kModeMap) {
+            float* dst = sa.maps + (gbase * 2 + (phi ? 0 : (size_t)kDim * kDim));
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -678,12 +694,32 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
             sa.hstart = seg->hstart;
             sa.maps = seg->maps;
             const int units = seg->n_segslots * h_v;
-            hipLaunchKernelGGL(gdn_chunk_state<kModeMap>, dim3(state_grid(units, 16)), dim3(state_threads(kModeMap)), 0, stream,
-                               cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+            // Tile pairs once the active tiles outnumber the CUs, as for
+            // whole sequences.  The segment slots overcount the segments, so
+            // the choice uses an estimate that is exact for one sequence:
+            // its ceil(T / 64) chunks make ceil(chunks / sc) segments, each
+            // further sequence at most one more.
+            const long long chunks = (total_tokens + kChunk - 1) / kChunk;
+            const long long segs = (n_seqs - 1) + (chunks + seg->seg_chunks - 1) / seg->seg_chunks;
+            const long long cus = state_cus();
+            if (16 * (segs - n_seqs) * h_v > cus)
+                hipLaunchKernelGGL(gdn_chunk_state<kModeMapPair>, dim3(state_grid(units, 8)),
+                                   dim3(state_threads(kModeMapPair)), 0, stream,
+                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+            else
+                hipLaunchKernelGGL(gdn_chunk_state<kModeMap>, dim3(state_grid(units, 16)),
+                                   dim3(state_threads(kModeMap)), 0, stream,
+                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
             hipLaunchKernelGGL(gdn_chunk_seg_scan, dim3(8 * n_seqs * h_v), dim3(256), 0, stream,
                                cu, n_seqs, h_v, s0, sa);
-            hipLaunchKernelGGL(gdn_chunk_state<kModeSegment>, dim3(state_grid(units, 8)), dim3(state_threads(kModeSegment)), 0, stream,
-                               cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+            if (8 * segs * h_v > cus)
+                hipLaunchKernelGGL(gdn_chunk_state<kModeSegmentPair>, dim3(state_grid(units, 4)),
+                                   dim3(state_threads(kModeSegmentPair)), 0, stream,
+                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+            else
+                hipLaunchKernelGGL(gdn_chunk_state<kModeSegment>, dim3(state_grid(units, 8)),
+                                   dim3(state_threads(kModeSegment)), 0, stream,
+                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
         }
     }
     return hipGetLastError();

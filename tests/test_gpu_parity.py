@@ -433,3 +433,28 @@ def test_streaming_prep_matches_ordinary_prep_bitwise():
         a, b = int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1])
         assert torch.equal(o1.cpu(), out[a:b]), n
         assert torch.equal(f1.cpu()[0], fin[n]), n
+
+
+def test_segmented_tile_pairs_match_single_tiles_bitwise():
+    """At 32 value heads in segments of 8 chunks, the map and segment passes
+    have more tiles than CUs and run as tile pairs; one head alone runs them
+    one tile per workgroup.  Heads are independent and the arithmetic per tile
+    is the same: each head's output rows and final states in the batch equal
+    the one-head run's bit for bit."""
+    import dataclasses
+    lengths = [3000, 1700]
+    x = gi.make_inputs(lengths, 16, 32, 128, 128, seed=31, state_std=0.02)
+    _print_case("segmented sc=8, tile pairs", x)
+    out, fin = _segmented(x, DevInputs(x), 8)
+    out, fin = out.cpu(), fin.cpu()
+    assert torch.isfinite(out).all() and torch.isfinite(fin).all()
+    for h in (0, 1, 17, 31):
+        j = h // 2
+        xh = dataclasses.replace(
+            x, name=f"{x.name}_head{h}", q=x.q[:, j:j + 1].copy(), k=x.k[:, j:j + 1].copy(),
+            v=x.v[:, h:h + 1].copy(), g=x.g[:, h:h + 1].copy(), beta=x.beta[:, h:h + 1].copy(),
+            initial_state=x.initial_state[:, h:h + 1].copy())
+        _print_case(f"segmented sc=8, head {h} alone", xh)
+        oh, fh = _segmented(xh, DevInputs(xh), 8)
+        assert torch.equal(oh.cpu()[:, 0], out[:, h]), h
+        assert torch.equal(fh.cpu()[:, 0], fin[:, h]), h
