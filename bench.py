@@ -143,8 +143,14 @@ def cpu_baseline(x, budget_s: float):
         t = time.perf_counter() - t0
         if t >= budget_s or reps >= 100000:
             break
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": x.total_tokens * reps / t, "unit": "tokens/s per layer", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": f"fp32 token recurrence, {x.name}, all {x.h_v} value heads, {reps} run(s), "
                       f"{t:.1f} s wall, threads over (sequence, value head)"}
 
@@ -288,6 +294,10 @@ def main():
         "prep": sum(e[0].elapsed_time(e[1]) for e in ev) / 1e3 / args.steps,
         "state": sum(e[1].elapsed_time(e[2]) for e in ev) / 1e3 / args.steps,
     }
+    # spread of single steps (the evented pass: event to event, so each
+    # includes the gaps the events add)
+    per_step = sorted(e[0].elapsed_time(e[2]) * 1e3 for e in ev)
+    spread = {f"p{q}": per_step[min(len(per_step) - 1, int(q / 100 * len(per_step)))] for q in (10, 50, 90)}
     step()
     torch.cuda.synchronize()
 
@@ -343,6 +353,7 @@ def main():
         "ms_per_layer": t_step * 1e3,
         "ms_per_layer_with_events": t_step_evented * 1e3,
         "ms_per_layer_cold_median": t_cold * 1e3,
+        "us_per_step_evented_p10_p50_p90": [spread["p10"], spread["p50"], spread["p90"]],
         "pct_mfma_peak": 100 * f_layer * T / t_step / PEAK_MFMA_F16,
         "pct_hbm_peak": 100 * (b_layer * T + per_seq["layer"]) / t_step / PEAK_HBM,
         "algorithmic_flops": f_layer * T,
