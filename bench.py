@@ -81,7 +81,7 @@ def algorithmic_work():
 MEASURED_TRAFFIC = {
     "gdn_chunk_prep": {"bytes": 181932431, "source_sha256_prefix": "b52136c7a5260ad0",
                        "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_prep.h"},
-    "gdn_chunk_state": {"bytes": 180838592, "source_sha256_prefix": "d697c9616ff68114",
+    "gdn_chunk_state": {"bytes": 180838592, "source_sha256_prefix": "efb32dfe6c1d428a",
                         "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
 }
 

@@ -25,6 +25,9 @@
 //   dim a(gq, s)   = 32 qq + 16 (s / 4) + 4 gq + s % 4   for K-step qq over d_k
 //   pos p(gq, s)   = 32 qq + 16 (s / 4) + 4 gq + s % 4   for K-step qq over positions
 // which is exactly how two stacked 16x16 accumulator tiles sit in a lane.
+//
+// Stage 1 (prep) is in gdn_prep.h; this file holds the state recurrence with
+// the output, the segment scan and the host-side launch of the prefill.
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
