@@ -23,6 +23,13 @@ def _gpu_available():
 
 def pytest_collection_modifyitems(config, items):
     if _gpu_available():
+        # A kernel that never returns should end the run with a stack dump,
+        # not stall it: every GPU test gets a time limit (the whole GPU suite
+        # takes about a minute), unless it sets its own.
+        if config.pluginmanager.hasplugin("timeout"):
+            for item in items:
+                if "gpu" in item.keywords and item.get_closest_marker("timeout") is None:
+                    item.add_marker(pytest.mark.timeout(300, method="thread"))
         return
     skip = pytest.mark.skip(reason="no GPU visible")
     for item in items:
