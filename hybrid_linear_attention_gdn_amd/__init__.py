@@ -134,6 +134,12 @@ def _stream(stream, *tensors) -> Optional[int]:
     import torch
     for t in tensors:
         if isinstance(t, torch.Tensor) and t.is_cuda:
+            # the current stream's handle without building a Stream object
+            # (0.1 instead of 2 us per call; the same handle, also inside
+            # torch.cuda.stream(...) and graph capture)
+            raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+            if raw is not None:
+                return raw(t.get_device())
             return torch.cuda.current_stream(t.device).cuda_stream
     return None
 
@@ -142,7 +148,7 @@ def make_dims(n_seqs: int, total_tokens: int, h_qk: int, h_v: int, d_k: int = 12
     return gdn_dims(int(n_seqs), int(total_tokens), int(h_qk), int(h_v), int(d_k), int(d_v))
 
 
-def _check_arg(x, name: str, dtypes, shape=None) -> None:
+def _check_arg(x, what: str, name: str, dtypes, shape=None) -> None:
     """Refuse a tensor argument whose dtype, shape or layout the kernels would
     misread.  The C ABI sees bare addresses, so this is the only place where a
     short or strided buffer can be caught before a kernel reads past it.  None
@@ -151,27 +157,27 @@ def _check_arg(x, name: str, dtypes, shape=None) -> None:
         return
     import torch
     if not isinstance(x, torch.Tensor):
-        raise GDNError(GDN_ERR_INVALID_VALUE, f"{name} must be a tensor, a device address or None")
+        raise GDNError(GDN_ERR_INVALID_VALUE, f"{what}: {name} must be a tensor, a device address or None")
     if dtypes is not None and x.dtype not in dtypes:
-        raise GDNError(GDN_ERR_INVALID_VALUE, f"{name} has dtype {x.dtype}, expected one of {list(dtypes)}")
-    if shape is not None and tuple(x.shape) != tuple(shape):
-        raise GDNError(GDN_ERR_INVALID_VALUE, f"{name} has shape {tuple(x.shape)}, expected {tuple(shape)}")
+        raise GDNError(GDN_ERR_INVALID_VALUE, f"{what}: {name} has dtype {x.dtype}, expected one of {list(dtypes)}")
+    if shape is not None and x.shape != shape:
+        raise GDNError(GDN_ERR_INVALID_VALUE, f"{what}: {name} has shape {tuple(x.shape)}, expected {tuple(shape)}")
     if not x.is_contiguous():
-        raise GDNError(GDN_ERR_INVALID_VALUE, f"{name} is not contiguous")
+        raise GDNError(GDN_ERR_INVALID_VALUE, f"{what}: {name} is not contiguous")
     if not x.is_cuda:
-        raise GDNError(GDN_ERR_INVALID_VALUE, f"{name} is not a GPU tensor (there is no CPU path)")
+        raise GDNError(GDN_ERR_INVALID_VALUE, f"{what}: {name} is not a GPU tensor (there is no CPU path)")
 
 
 def _check_tokens(q, k, v, g, beta, out, dims: gdn_dims, what: str) -> None:
     import torch
     bf16, f32 = (torch.bfloat16,), (torch.float32,)
     T, hqk, hv, dk, dv = dims.total_tokens, dims.n_heads_qk, dims.n_heads_v, dims.d_k, dims.d_v
-    _check_arg(q, f"{what}: q", bf16, (T, hqk, dk))
-    _check_arg(k, f"{what}: k", bf16, (T, hqk, dk))
-    _check_arg(v, f"{what}: v", bf16, (T, hv, dv))
-    _check_arg(g, f"{what}: g", f32, (T, hv))
-    _check_arg(beta, f"{what}: beta", f32, (T, hv))
-    _check_arg(out, f"{what}: out", f32, (T, hv, dv))
+    _check_arg(q, what, "q", bf16, (T, hqk, dk))
+    _check_arg(k, what, "k", bf16, (T, hqk, dk))
+    _check_arg(v, what, "v", bf16, (T, hv, dv))
+    _check_arg(g, what, "g", f32, (T, hv))
+    _check_arg(beta, what, "beta", f32, (T, hv))
+    _check_arg(out, what, "out", f32, (T, hv, dv))
 
 
 def _check_prefill(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace,
@@ -179,10 +185,10 @@ def _check_prefill(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state
     import torch
     _check_tokens(q, k, v, g, beta, out, dims, what)
     state = (dims.n_seqs, dims.n_heads_v, dims.d_k, dims.d_v)
-    _check_arg(cu_seqlens, f"{what}: cu_seqlens", (torch.int32,), (dims.n_seqs + 1,))
-    _check_arg(initial_state, f"{what}: initial_state", (torch.float32,), state)
-    _check_arg(final_state, f"{what}: final_state", (torch.float32,), state)
-    _check_arg(workspace, f"{what}: workspace", None)
+    _check_arg(cu_seqlens, what, "cu_seqlens", (torch.int32,), (dims.n_seqs + 1,))
+    _check_arg(initial_state, what, "initial_state", (torch.float32,), state)
+    _check_arg(final_state, what, "final_state", (torch.float32,), state)
+    _check_arg(workspace, what, "workspace", None)
 
 
 def _nbytes(workspace, workspace_bytes: Optional[int]) -> int:
@@ -273,7 +279,7 @@ def gdn_chunk_fwd_snapshots(q, k, v, g, beta, cu_seqlens, initial_state, out, fi
         import torch
         slots = gdn_chunk_state_slots(dims.n_seqs, dims.total_tokens, dims.n_heads_qk, dims.n_heads_v,
                                       dims.d_k, dims.d_v)
-        _check_arg(chunk_states, "gdn_chunk_fwd_snapshots: chunk_states", (torch.float32,),
+        _check_arg(chunk_states, "gdn_chunk_fwd_snapshots", "chunk_states", (torch.float32,),
                    (slots, dims.n_heads_v, dims.d_k, dims.d_v))
     workspace_bytes = _nbytes(workspace, workspace_bytes)
     st = lib.gdn_chunk_fwd_snapshots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
@@ -320,9 +326,9 @@ def gdn_recurrent_step(q, k, v, g, beta, n_requests: int, tokens_per_request: in
     import torch
     _check_tokens(q, k, v, g, beta, out, dims, "gdn_recurrent_step")
     state = (dims.n_seqs, dims.n_heads_v, dims.d_k, dims.d_v)
-    _check_arg(state_in, "gdn_recurrent_step: state_in", (torch.float32,), state)
-    _check_arg(state_out, "gdn_recurrent_step: state_out", (torch.float32,), state)
-    _check_arg(intermediate_states, "gdn_recurrent_step: intermediate_states", (torch.float32,),
+    _check_arg(state_in, "gdn_recurrent_step", "state_in", (torch.float32,), state)
+    _check_arg(state_out, "gdn_recurrent_step", "state_out", (torch.float32,), state)
+    _check_arg(intermediate_states, "gdn_recurrent_step", "intermediate_states", (torch.float32,),
                (dims.n_seqs, tokens_per_request) + state[1:])
     st = lib.gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 int(n_requests), int(tokens_per_request),
@@ -360,12 +366,12 @@ def gdn_recurrent_step_slots(q, k, v, g, beta, cu_tokens, n_requests: int, max_t
     import torch
     _check_tokens(q, k, v, g, beta, out, dims, "gdn_recurrent_step_slots")
     i32 = (torch.int32,)
-    _check_arg(cu_tokens, "gdn_recurrent_step_slots: cu_tokens", i32, (dims.n_seqs + 1,))
-    _check_arg(state_pool, "gdn_recurrent_step_slots: state_pool",
+    _check_arg(cu_tokens, "gdn_recurrent_step_slots", "cu_tokens", i32, (dims.n_seqs + 1,))
+    _check_arg(state_pool, "gdn_recurrent_step_slots", "state_pool",
                (torch.float16,) if state_dtype == GDN_STATE_F16 else (torch.float32,),
                (pool_slots, dims.n_heads_v, dims.d_k, dims.d_v))
-    _check_arg(slot_table, "gdn_recurrent_step_slots: slot_table", i32, (dims.n_seqs, int(max_tokens) + 1))
-    _check_arg(num_accepted, "gdn_recurrent_step_slots: num_accepted", i32, (dims.n_seqs,))
+    _check_arg(slot_table, "gdn_recurrent_step_slots", "slot_table", i32, (dims.n_seqs, int(max_tokens) + 1))
+    _check_arg(num_accepted, "gdn_recurrent_step_slots", "num_accepted", i32, (dims.n_seqs,))
     st = lib.gdn_recurrent_step_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_tokens),
                                       int(n_requests), int(max_tokens), _ptr(state_pool), int(state_dtype),
                                       int(pool_slots), _ptr(slot_table), _ptr(num_accepted), _ptr(out),
