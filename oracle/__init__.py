@@ -29,7 +29,7 @@ _lib = None
 
 def build(verbose: bool = False) -> str:
     """Compile the C oracle with gcc (host only)."""
-    cmd = ["gcc", "-O3", "-march=native", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+    cmd = ["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
            "-Wall", "-Wextra", "-o", _LIB_PATH + ".tmp", _SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
