@@ -17,6 +17,9 @@ current stream.  The names mirror the C entry points:
   state_out, out, intermediate_states, save_intermediate_states)``
 * ``gdn_recurrent_step_slots(q, k, v, g, beta, cu_tokens, n_requests, max_tokens,
   state_pool, slot_table, num_accepted, out)`` (pool dtype float32 or float16)
+* ``gdn_check_chunk_inputs_host(...)`` / ``gdn_check_step_inputs_host(...)``: the
+  device-content preconditions on host (numpy) arrays, the checks that
+  ``GDN_DEBUG_CHECKS=1`` runs inside every entry point
 
 There is no fallback: if ``libgdn.so`` is missing or a call fails, a
 ``GDNError`` is raised.  Build the library with
@@ -52,6 +55,8 @@ EXPORTED_SYMBOLS = (
     "gdn_chunk_fwd_segmented",
     "gdn_recurrent_step",
     "gdn_recurrent_step_slots",
+    "gdn_check_chunk_inputs_host",
+    "gdn_check_step_inputs_host",
     "gdn_status_string",
     "gdn_get_last_error",
 )
@@ -104,6 +109,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_recurrent_step_slots.argtypes = [vp, vp, vp, vp, vp, vp, c32, c32, vp, c32, c64, vp, vp, vp,
                                              dims_p, vp]
     lib.gdn_recurrent_step_slots.restype = ctypes.c_int
+    lib.gdn_check_chunk_inputs_host.argtypes = [vp, vp, vp, vp, vp, vp, vp, dims_p]
+    lib.gdn_check_chunk_inputs_host.restype = ctypes.c_int
+    lib.gdn_check_step_inputs_host.argtypes = [vp, vp, vp, vp, vp, vp, c64, dims_p]
+    lib.gdn_check_step_inputs_host.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_get_last_error.argtypes = []
@@ -377,3 +386,60 @@ def gdn_recurrent_step_slots(q, k, v, g, beta, cu_tokens, n_requests: int, max_t
                                       int(pool_slots), _ptr(slot_table), _ptr(num_accepted), _ptr(out),
                                       ctypes.byref(dims), _stream(stream, q, state_pool, out))
     _check(lib, st, "gdn_recurrent_step_slots")
+
+
+def _host_ptr(a):
+    """Address of a C-contiguous numpy array (None stays NULL)."""
+    if a is None:
+        return None
+    import numpy as np
+    if not isinstance(a, np.ndarray) or not a.flags.c_contiguous:
+        raise GDNError(GDN_ERR_INVALID_VALUE, "host checks take C-contiguous numpy arrays")
+    return a.ctypes.data
+
+
+def _host_bits(x):
+    """bf16 operands as their uint16 bit patterns (numpy uint16, or float32 holding bf16 values)."""
+    import numpy as np
+    if x is None:
+        return None
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return x
+    if x.dtype == np.float32:
+        return np.ascontiguousarray((x.view(np.uint32) >> 16).astype(np.uint16))
+    raise GDNError(GDN_ERR_INVALID_VALUE, f"bf16 operand dtype {x.dtype} is neither uint16 bits nor float32")
+
+
+def gdn_check_chunk_inputs_host(q, k, v, g, beta, cu_seqlens, initial_state, *, h_qk: int, h_v: int,
+                                d_k: int = 128, d_v: int = 128) -> None:
+    """Device-content preconditions of the prefill on host arrays (raises GDNError).
+    q, k, v: uint16 bf16 bits or float32 bf16 values; g, beta float32; cu_seqlens int32."""
+    import numpy as np
+    lib = load_library()
+    cu = np.ascontiguousarray(cu_seqlens, np.int32)
+    dims = make_dims(cu.shape[0] - 1, int(cu[-1]) if cu.size else 0, h_qk, h_v, d_k, d_v)
+    bq, bk, bv = _host_bits(q), _host_bits(k), _host_bits(v)
+    g = None if g is None else np.ascontiguousarray(g, np.float32)
+    beta = None if beta is None else np.ascontiguousarray(beta, np.float32)
+    s0 = None if initial_state is None else np.ascontiguousarray(initial_state, np.float32)
+    st = lib.gdn_check_chunk_inputs_host(_host_ptr(bq), _host_ptr(bk), _host_ptr(bv), _host_ptr(g),
+                                         _host_ptr(beta), _host_ptr(cu), _host_ptr(s0), ctypes.byref(dims))
+    _check(lib, st, "gdn_check_chunk_inputs_host")
+
+
+def gdn_check_step_inputs_host(q, k, v, g, beta, state_in, *, n_requests: int, h_qk: int, h_v: int,
+                               d_k: int = 128, d_v: int = 128) -> None:
+    """Device-content preconditions of the recurrent steps on host arrays (raises GDNError)."""
+    import numpy as np
+    lib = load_library()
+    bq, bk, bv = _host_bits(q), _host_bits(k), _host_bits(v)
+    T = 0 if bq is None else bq.shape[0]
+    dims = make_dims(n_requests, T, h_qk, h_v, d_k, d_v)
+    g = None if g is None else np.ascontiguousarray(g, np.float32)
+    beta = None if beta is None else np.ascontiguousarray(beta, np.float32)
+    s = None if state_in is None else np.ascontiguousarray(state_in, np.float32)
+    n_states = 0 if s is None else s.shape[0]
+    st = lib.gdn_check_step_inputs_host(_host_ptr(bq), _host_ptr(bk), _host_ptr(bv), _host_ptr(g),
+                                        _host_ptr(beta), _host_ptr(s), int(n_states), ctypes.byref(dims))
+    _check(lib, st, "gdn_check_step_inputs_host")

@@ -1,111 +1,79 @@
 // C ABI of libgdn.so: host-side validation, workspace carving and launches.
 // Validation reads only host values; nothing here touches device memory or
-// synchronises.  See include/gdn.h for the contract.
+// synchronises, except the checks GDN_DEBUG_CHECKS turns on.  See
+// include/gdn.h for the contract.
 
 #include "gdn.h"
 
 #include <hip/hip_runtime.h>
 
-#include <cstdarg>
-#include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "gdn_launch.h"
+#include "gdn_validate.h"
+
+using gdn::aligned16;
+using gdn::fail;
+using gdn::kAlign;
+using gdn::Layout;
+using gdn::ok;
 
 namespace {
 
-thread_local char g_last_error[512] = "";
-
-gdn_status fail(gdn_status s, const char* fmt, ...) {
-    va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
-    va_end(ap);
-    return s;
+// GDN_DEBUG_CHECKS (any value but "" or "0") makes every entry point copy its
+// inputs to the host and check the device-content preconditions before any
+// launch: a debugging aid that synchronises the stream and allocates host
+// memory, never meant for a timed or captured call.
+bool debug_checks() {
+    const char* e = getenv("GDN_DEBUG_CHECKS");
+    return e && *e && strcmp(e, "0") != 0;
 }
 
-gdn_status ok() {
-    g_last_error[0] = '\0';
-    return GDN_SUCCESS;
+template <typename T>
+hipError_t to_host(std::vector<T>& dst, const void* src, size_t n) {
+    dst.resize(n);
+    if (n == 0 || !src) return hipSuccess;
+    return hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost);
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-constexpr size_t kAlign = 256;
-size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
-// Launch-size limits.  A dispatch holds at most 2^32 work-items per grid
-// dimension: the state launch runs 8 column tiles of 192 threads (an affine
-// map 16 of 128, the segment scan 8 of 256) per (sequence or segment, value
-// head) pair, prep 256 threads per chunk slot with the value heads as the
-// second grid dimension (at most 65535 workgroups there).
-constexpr long long kMaxHeadUnits = 1LL << 21;
-constexpr long long kMaxChunkSlots = 1LL << 24;
-constexpr int kMaxValueHeads = 65535;
-
-int64_t n_chunk_slots(const gdn_dims* d) {
-    return (int64_t)d->n_seqs + d->total_tokens / gdn::kChunk + 1;
+gdn_status debug_check_chunk(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             const int32_t* cu, const float* s0, const gdn_dims* d, void* stream) {
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    const size_t T = (size_t)d->total_tokens, N = (size_t)d->n_seqs;
+    const size_t nqk = T * d->n_heads_qk * d->d_k, nv = T * d->n_heads_v * d->d_v, ng = T * d->n_heads_v;
+    std::vector<uint16_t> hq, hk, hv;
+    std::vector<float> hg, hb, hs;
+    std::vector<int32_t> hc;
+    if (e == hipSuccess) e = to_host(hc, cu, N + 1);
+    if (e == hipSuccess) e = to_host(hq, q, nqk);
+    if (e == hipSuccess) e = to_host(hk, k, nqk);
+    if (e == hipSuccess) e = to_host(hv, v, nv);
+    if (e == hipSuccess) e = to_host(hg, g, ng);
+    if (e == hipSuccess) e = to_host(hb, beta, ng);
+    if (e == hipSuccess && s0) e = to_host(hs, s0, N * d->n_heads_v * d->d_k * d->d_v);
+    if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "GDN_DEBUG_CHECKS copy: %s", hipGetErrorString(e));
+    return gdn_check_chunk_inputs_host(hq.data(), hk.data(), hv.data(), hg.data(), hb.data(), hc.data(),
+                                       s0 ? hs.data() : nullptr, d);
 }
 
-gdn_status check_dims(const gdn_dims* d) {
-    if (!d) return fail(GDN_ERR_INVALID_VALUE, "dims is NULL");
-    if (d->n_seqs < 0) return fail(GDN_ERR_INVALID_VALUE, "n_seqs = %d is negative", d->n_seqs);
-    if (d->total_tokens < 0)
-        return fail(GDN_ERR_INVALID_VALUE, "total_tokens = %lld is negative", (long long)d->total_tokens);
-    if (d->total_tokens > 0x7fffffffLL)
-        return fail(GDN_ERR_INVALID_VALUE, "total_tokens = %lld exceeds int32 cu_seqlens", (long long)d->total_tokens);
-    if (d->n_seqs == 0 && d->total_tokens != 0)
-        return fail(GDN_ERR_INVALID_VALUE, "total_tokens = %lld with no sequences", (long long)d->total_tokens);
-    if (d->n_heads_qk <= 0 || d->n_heads_v <= 0)
-        return fail(GDN_ERR_INVALID_VALUE, "head counts must be positive (H_qk = %d, H_v = %d)",
-                    d->n_heads_qk, d->n_heads_v);
-    if (d->n_heads_v % d->n_heads_qk != 0)
-        return fail(GDN_ERR_INVALID_VALUE, "H_v = %d is not a multiple of H_qk = %d",
-                    d->n_heads_v, d->n_heads_qk);
-    if (d->d_k <= 0 || d->d_v <= 0)
-        return fail(GDN_ERR_INVALID_VALUE, "head dims must be positive (d_k = %d, d_v = %d)", d->d_k, d->d_v);
-    if (d->d_k != gdn::kDim || d->d_v != gdn::kDim)
-        return fail(GDN_ERR_NOT_SUPPORTED, "only d_k = d_v = 128 is supported (got %d, %d)", d->d_k, d->d_v);
-    if (d->n_heads_v > kMaxValueHeads)
-        return fail(GDN_ERR_INVALID_VALUE, "H_v = %d exceeds %d", d->n_heads_v, kMaxValueHeads);
-    const long long nh = (long long)d->n_seqs * d->n_heads_v;
-    if (nh > kMaxHeadUnits)
-        return fail(GDN_ERR_INVALID_VALUE, "n_seqs * H_v = %lld exceeds %lld", nh, kMaxHeadUnits);
-    if (n_chunk_slots(d) > kMaxChunkSlots)
-        return fail(GDN_ERR_INVALID_VALUE, "%lld chunk slots (N + T/64 + 1) exceed %lld",
-                    (long long)n_chunk_slots(d), kMaxChunkSlots);
-    return GDN_SUCCESS;
-}
-
-struct Layout {
-    size_t w, u, p, dg, kt, qf, junk, maps, hstart, total;
-};
-
-// Segment slots of the segment-parallel recurrence (see gdn_chunk.hip).
-int64_t n_seg_slots(const gdn_dims* d, int32_t seg_chunks) {
-    return (int64_t)d->n_seqs + n_chunk_slots(d) / seg_chunks + 1;
-}
-
-Layout workspace_layout(const gdn_dims* d, int32_t seg_chunks = 0) {
-    const size_t units = (size_t)n_chunk_slots(d) * (size_t)d->n_heads_v;
-    Layout L;
-    size_t off = 0;
-    const size_t qk_units = (size_t)n_chunk_slots(d) * (size_t)d->n_heads_qk;
-    L.w = off;  off += round_up(units * gdn::kWElems * sizeof(gdn::f16));
-    L.u = off;  off += round_up(units * gdn::kUElems * sizeof(gdn::f16));
-    L.p = off;  off += round_up(units * gdn::kPElems * sizeof(gdn::f16));
-    L.dg = off; off += round_up(units * gdn::kGElems * sizeof(float));
-    L.kt = off; off += round_up(qk_units * gdn::kKtElems * sizeof(gdn::f16));
-    L.qf = off; off += round_up(qk_units * gdn::kQfElems * sizeof(gdn::f16));
-    L.junk = off; off += round_up(gdn::kJunkBytes);
-    L.maps = L.hstart = off;
-    if (seg_chunks > 0) {
-        const size_t per = (size_t)n_seg_slots(d, seg_chunks) * (size_t)d->n_heads_v * gdn::kDim * gdn::kDim * sizeof(float);
-        L.maps = off;   off += round_up(2 * per);
-        L.hstart = off; off += round_up(per);
-    }
-    L.total = off;
-    return L;
+gdn_status debug_check_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                            const float* state_in, int64_t n_states, const gdn_dims* d, void* stream) {
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    const size_t T = (size_t)d->total_tokens;
+    const size_t nqk = T * d->n_heads_qk * d->d_k, nv = T * d->n_heads_v * d->d_v, ng = T * d->n_heads_v;
+    std::vector<uint16_t> hq, hk, hv;
+    std::vector<float> hg, hb, hs;
+    if (e == hipSuccess) e = to_host(hq, q, nqk);
+    if (e == hipSuccess) e = to_host(hk, k, nqk);
+    if (e == hipSuccess) e = to_host(hv, v, nv);
+    if (e == hipSuccess) e = to_host(hg, g, ng);
+    if (e == hipSuccess) e = to_host(hb, beta, ng);
+    if (e == hipSuccess && state_in) e = to_host(hs, state_in, (size_t)n_states * d->n_heads_v * d->d_k * d->d_v);
+    if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "GDN_DEBUG_CHECKS copy: %s", hipGetErrorString(e));
+    return gdn_check_step_inputs_host(hq.data(), hk.data(), hv.data(), hg.data(), hb.data(),
+                                      state_in ? hs.data() : nullptr, n_states, d);
 }
 
 #define GDN_REQUIRE_PTR(p)                                                              \
@@ -123,36 +91,6 @@ Layout workspace_layout(const gdn_dims* d, int32_t seg_chunks = 0) {
 
 extern "C" {
 
-const char* gdn_status_string(gdn_status s) {
-    switch (s) {
-        case GDN_SUCCESS: return "success";
-        case GDN_ERR_INVALID_VALUE: return "invalid value";
-        case GDN_ERR_NOT_SUPPORTED: return "not supported";
-        case GDN_ERR_MISALIGNED: return "misaligned pointer";
-        case GDN_ERR_WORKSPACE: return "workspace too small";
-        case GDN_ERR_LAUNCH: return "kernel launch failed";
-    }
-    return "unknown status";
-}
-
-const char* gdn_get_last_error(void) { return g_last_error; }
-
-gdn_status gdn_chunk_fwd_workspace_size(const gdn_dims* dims, size_t* bytes) {
-    if (!bytes) return fail(GDN_ERR_INVALID_VALUE, "bytes is NULL");
-    const gdn_status s = check_dims(dims);
-    if (s != GDN_SUCCESS) return s;
-    *bytes = workspace_layout(dims).total;
-    return ok();
-}
-
-gdn_status gdn_chunk_state_slots(const gdn_dims* dims, int64_t* n_slots) {
-    if (!n_slots) return fail(GDN_ERR_INVALID_VALUE, "n_slots is NULL");
-    const gdn_status s = check_dims(dims);
-    if (s != GDN_SUCCESS) return s;
-    *n_slots = n_chunk_slots(dims);
-    return ok();
-}
-
 namespace {
 
 gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -162,7 +100,7 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
                           const char* what, int32_t seg_chunks = 0) {
     if (stage_mask < 1 || stage_mask > 3)
         return fail(GDN_ERR_INVALID_VALUE, "stage_mask = %d is outside 1..3", stage_mask);
-    gdn_status s = check_dims(dims);
+    gdn_status s = gdn::check_dims(dims);
     if (s != GDN_SUCCESS) return s;
     if (dims->n_seqs == 0) return ok();   // nothing to do, nothing to write
     GDN_REQUIRE_PTR(cu_seqlens);
@@ -177,13 +115,17 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
         GDN_REQUIRE_PTR(beta);
         GDN_REQUIRE_PTR(out);
     }
-    const Layout L = workspace_layout(dims, seg_chunks);
+    const Layout L = gdn::workspace_layout(dims, seg_chunks);
     if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes required)", L.total);
     if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
         return fail(GDN_ERR_MISALIGNED, "workspace is not 256-byte aligned");
     if (workspace_bytes < L.total)
         return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, L.total);
-    const int64_t slots = n_chunk_slots(dims);
+    const int64_t slots = gdn::n_chunk_slots(dims);
+    if (debug_checks() && (stage_mask & 1)) {
+        s = debug_check_chunk(q, k, v, g, beta, cu_seqlens, initial_state, dims, stream);
+        if (s != GDN_SUCCESS) return s;
+    }
 
     char* base = static_cast<char*>(workspace);
     gdn::ChunkWorkspace ws;
@@ -201,10 +143,10 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
 
     gdn::SegLaunch seg;
     if (seg_chunks > 0) {
-        const int64_t segslots = n_seg_slots(dims, seg_chunks);
-        if (segslots * dims->n_heads_v > kMaxHeadUnits)
+        const int64_t segslots = gdn::n_seg_slots(dims, seg_chunks);
+        if (segslots * dims->n_heads_v > gdn::kMaxHeadUnits)
             return fail(GDN_ERR_INVALID_VALUE, "%lld segments x H_v exceed %lld (segment_chunks too small)",
-                        (long long)segslots, kMaxHeadUnits);
+                        (long long)segslots, gdn::kMaxHeadUnits);
         seg.seg_chunks = seg_chunks;
         seg.n_segslots = (int)segslots;
         seg.maps = reinterpret_cast<float*>(base + L.maps);
@@ -250,14 +192,6 @@ gdn_status gdn_chunk_fwd_snapshots(const void* q, const void* k, const void* v,
                           dims, workspace, workspace_bytes, 3, stream, "gdn_chunk_fwd_snapshots");
 }
 
-gdn_status gdn_chunk_fwd_segmented_workspace_size(const gdn_dims* dims, int32_t segment_chunks, size_t* bytes) {
-    if (!bytes) return fail(GDN_ERR_INVALID_VALUE, "bytes is NULL");
-    if (segment_chunks < 1) return fail(GDN_ERR_INVALID_VALUE, "segment_chunks = %d must be positive", segment_chunks);
-    const gdn_status s = check_dims(dims);
-    if (s != GDN_SUCCESS) return s;
-    *bytes = workspace_layout(dims, segment_chunks).total;
-    return ok();
-}
 
 gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
                                    const float* g, const float* beta,
@@ -298,7 +232,7 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v,
                               int save_intermediate_states,
                               const gdn_dims* dims,
                               void* stream) {
-    gdn_status s = check_dims(dims);
+    gdn_status s = gdn::check_dims(dims);
     if (s != GDN_SUCCESS) return s;
     if (n_requests < 0 || tokens_per_request < 0)
         return fail(GDN_ERR_INVALID_VALUE, "negative n_requests (%d) or tokens_per_request (%d)",
@@ -327,6 +261,10 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v,
         GDN_REQUIRE_PTR(beta);
         GDN_REQUIRE_PTR(out);
     }
+    if (debug_checks()) {
+        s = debug_check_step(q, k, v, g, beta, state_in, n_requests, dims, stream);
+        if (s != GDN_SUCCESS) return s;
+    }
     const hipError_t e = gdn::launch_recurrent_step(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
         g, beta, n_requests, tokens_per_request, dims->n_heads_qk, dims->n_heads_v,
@@ -346,7 +284,7 @@ gdn_status gdn_recurrent_step_slots(const void* q, const void* k, const void* v,
                                     float* out,
                                     const gdn_dims* dims,
                                     void* stream) {
-    gdn_status s = check_dims(dims);
+    gdn_status s = gdn::check_dims(dims);
     if (s != GDN_SUCCESS) return s;
     if (n_requests < 0 || max_tokens < 0)
         return fail(GDN_ERR_INVALID_VALUE, "negative n_requests (%d) or max_tokens (%d)", n_requests, max_tokens);
@@ -370,6 +308,10 @@ gdn_status gdn_recurrent_step_slots(const void* q, const void* k, const void* v,
         GDN_REQUIRE_PTR(g);
         GDN_REQUIRE_PTR(beta);
         GDN_REQUIRE_PTR(out);
+    }
+    if (debug_checks()) {
+        s = debug_check_step(q, k, v, g, beta, nullptr, 0, dims, stream);
+        if (s != GDN_SUCCESS) return s;
     }
     const hipError_t e = gdn::launch_recurrent_step_slots(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),

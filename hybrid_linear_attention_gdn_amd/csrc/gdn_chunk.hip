@@ -314,7 +314,8 @@ __device__ __forceinline__ void out_end(f32x4 (&oacc)[4], const PFrag& pf, const
 struct SegArgs {
     int seg_chunks;          // sc
     int n_segslots;
-    const float* hstart;     // [segslot][h_v][128][128]: incoming state of segment s >= 1
+    const float* hstart;     // [segslot][h_v][128][128]: incoming state of every segment of a
+                             // sequence with two or more (segment 0's copied from s0 by the scan)
     float* maps;             // [segslot][h_v][2][128][128]: Phi, R of segments s < nseg - 1
 };
 
@@ -450,7 +451,11 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     H[i][e] = (phi && 16 * i + 4 * gq + e == col) ? 1.f : 0.f;
-        } else if (kSeg && sg > 0) {
+        } else if (kSeg && nseg > 1) {
+            // every segment of a split sequence starts from its copy in
+            // hstart, segment 0 included: the last segment's workgroups may
+            // write final_state while segment 0's still run, and final_state
+            // may alias initial_state
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -601,10 +606,13 @@ __global__ __launch_bounds__(256) void gdn_chunk_seg_scan(
     __shared__ float Phi[kDim * kPS];
     __shared__ float Ht[kDim * 16];
     const size_t sbase = ((size_t)seq * h_v + h) * kDim * kDim;
+    float* hs0 = const_cast<float*>(sa.hstart) + ((size_t)g0 * h_v + h) * kDim * kDim;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = r0 + 16 * i;
-        Ht[r * 16 + c] = s0 ? s0[sbase + (size_t)r * kDim + 16 * ct + c] : 0.f;
+        const float x = s0 ? s0[sbase + (size_t)r * kDim + 16 * ct + c] : 0.f;
+        Ht[r * 16 + c] = x;
+        hs0[(size_t)r * kDim + 16 * ct + c] = x;      // segment 0's incoming state
     }
     for (int sg = 0; sg + 1 < nseg; ++sg) {
         const size_t mbase = ((size_t)(g0 + sg) * h_v + h) * 2 * kDim * kDim;

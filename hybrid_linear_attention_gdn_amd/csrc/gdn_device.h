@@ -21,10 +21,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace gdn {
+#include "gdn_sizes.h"
 
-constexpr int kChunk = 64;  // tokens per chunk
-constexpr int kDim = 128;   // d_k = d_v
+namespace gdn {
 
 typedef _Float16 f16;
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
@@ -34,22 +33,6 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-// Per (chunk slot, value head) element counts of the workspace regions, all
-// in matrix-core fragment order.
-constexpr size_t kWElems = 16 * 64 * 8;    // -W, A fragments [p][qq][lane][8]
-constexpr size_t kUElems = 8 * 4 * 64 * 4;  // U, accumulator fragments [ct][p][lane][4]
-// P = M o (Q K^T), A fragments over positions of its six nonzero (row tile,
-// K-step) blocks (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-constexpr size_t kPElems = 6 * 64 * 8;
-// decay vectors: e^{G_C - G_r} for r < 63 (the factor of row 63 is 1) with
-// e^{G_C} in entry 63, then e^{G_r} for r = 0..63
-constexpr size_t kGElems = 128;
-// Per (chunk slot, q/k head): K^T as A fragments of the state update
-// [d_k tile][pos step][lane][8], and Q as A fragments over d_k [p][qq][lane][8]
-constexpr size_t kKtElems = 8 * 2 * 64 * 8;
-constexpr size_t kQfElems = 4 * 4 * 64 * 8;
-constexpr size_t kJunkBytes = 1024;         // sink for the lanes of masked-off stores
 
 // Workspace regions are chunk-slot-major: unit (slot, head) sits at slot *
 // heads + head, so the units of all heads for one chunk are contiguous (a

@@ -1,9 +1,9 @@
 /*
  * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet layer library, libgdn.so.
  *
- * The layer is the gated delta rule (Yang, Kautz, Hatamizadeh, "Gated Delta
- * Networks: Improving Mamba2 with Delta Rule", ICLR 2025).  For every
- * sequence and value head, with state S (d_v x d_k), alpha_t = exp(g_t):
+ * The layer is the gated delta rule.  No page prints the recurrence; the
+ * definition in force is the layer's specification: for every sequence and
+ * value head, with state S (d_v x d_k), alpha_t = exp(g_t),
  *
  *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t.
  *
@@ -37,7 +37,8 @@
  *  - Supported sizes: d_k = d_v = 128; H_v a positive multiple of H_qk.
  *    Other head dims return GDN_ERR_NOT_SUPPORTED.
  *  - Validation reads only host values (no device reads, no synchronisation).
- *    Device-content preconditions are documented, not checked: cu_seqlens is
+ *    Device-content preconditions are documented, and checked only under
+ *    GDN_DEBUG_CHECKS (see gdn_check_chunk_inputs_host): cu_seqlens is
  *    nondecreasing with cu_seqlens[0] = 0 and cu_seqlens[N] = T; g <= 0; all
  *    inputs finite and, since matrix-core operands are fp16, |q|, |k|, |v|
  *    below 65504 and states and outputs well inside fp16 range.
@@ -290,6 +291,37 @@ gdn_status gdn_recurrent_step_slots(const void* q, const void* k, const void* v,
                                     float* out,
                                     const gdn_dims* dims,
                                     void* stream);
+
+/*
+ * Device-content preconditions, checked on HOST copies of the inputs: a
+ * debugging aid, and what every entry point runs on copies of its device
+ * inputs when the environment variable GDN_DEBUG_CHECKS is set (to anything
+ * but "" or "0"; the call then synchronises its stream, allocates host
+ * memory and is not fit for timing or graph capture).  No page states these
+ * conditions; they are what the arithmetic above needs: the decay
+ * alpha = exp(g) must lie in (0, 1], the chunk boundaries must be ordered,
+ * and fp16 matrix-core operands cannot hold magnitudes above 65504.
+ *
+ * gdn_check_chunk_inputs_host (the prefill entry points): cu_seqlens
+ * nondecreasing with cu_seqlens[0] = 0 and cu_seqlens[N] = total_tokens;
+ * g finite and <= 0; beta finite; q, k, v (bf16 bits) finite with
+ * |x| <= 65504; initial_state (NULL allowed) finite with |x| <= 65504.
+ * gdn_check_step_inputs_host (the recurrent steps): the same token checks,
+ * and state_in ([n_states, H_v, d_k, d_v], NULL allowed) finite.
+ * Every pointer is a host pointer with the layout of the corresponding
+ * device argument.  The first violation returns GDN_ERR_INVALID_VALUE and
+ * names the offending element in gdn_get_last_error(); invalid dims return
+ * what the entry points return for them.
+ */
+gdn_status gdn_check_chunk_inputs_host(const void* q, const void* k, const void* v,
+                                       const float* g, const float* beta,
+                                       const int32_t* cu_seqlens,
+                                       const float* initial_state,
+                                       const gdn_dims* dims);
+gdn_status gdn_check_step_inputs_host(const void* q, const void* k, const void* v,
+                                      const float* g, const float* beta,
+                                      const float* state_in, int64_t n_states,
+                                      const gdn_dims* dims);
 
 /* Static text for a status code. */
 const char* gdn_status_string(gdn_status s);

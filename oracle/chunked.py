@@ -36,7 +36,7 @@ import numpy as np
 def chunk_step(Q, K, V, g, beta, H0):
     """One chunk.  Q, K: [C, d_k]; V: [C, d_v]; g, beta: [C]; H0: [d_k, d_v].
 
-    Returns dict with G, A, Tm, W, U, Up (U'), O and H (outgoing state).
+    Returns dict with G, A, Tm, W, U, Up (U'), P (M o Q K^T), O and H (outgoing state).
     """
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
@@ -55,9 +55,10 @@ def chunk_step(Q, K, V, g, beta, H0):
     W = (Tm * (beta * np.exp(G))[None, :]) @ K
     U = (Tm * beta[None, :]) @ V
     Up = U - W @ H0
-    O = np.exp(G)[:, None] * (Q @ H0) + (decay * (Q @ K.T)) @ Up
+    P = decay * (Q @ K.T)
+    O = np.exp(G)[:, None] * (Q @ H0) + P @ Up
     H = np.exp(G[-1]) * H0 + K.T @ (np.exp(G[-1] - G)[:, None] * Up)
-    return {"G": G, "A": A, "Tm": Tm, "W": W, "U": U, "Up": Up, "O": O, "H": H}
+    return {"G": G, "A": A, "Tm": Tm, "W": W, "U": U, "Up": Up, "P": P, "O": O, "H": H}
 
 
 def chunked_forward(q, k, v, g, beta, cu_seqlens, initial_state=None, chunk: int = 64):

@@ -5,10 +5,11 @@
  * load this library.  The product path never calls it; it shares no code,
  * header or constant with the HIP library.
  *
- * What it computes: the gated delta rule (Yang, Kautz, Hatamizadeh, "Gated
- * Delta Networks: Improving Mamba2 with Delta Rule", ICLR 2025), one token at
- * a time, in the plain definition's order.  For each sequence and value head,
- * with state S (d_v x d_k), decay alpha_t = exp(g_t) and write strength beta_t:
+ * What it computes: the gated delta rule, one token at a time, in the plain
+ * definition's order.  No page prints the recurrence; the definition in force
+ * is the layer's specification, restated here.  For each sequence and value
+ * head, with state S (d_v x d_k), decay alpha_t = exp(g_t) and write strength
+ * beta_t:
  *
  *     S_t = alpha_t * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
  *     o_t = S_t q_t
