@@ -7,6 +7,8 @@ current stream.  The names mirror the C entry points:
 * ``gdn_chunk_fwd_workspace_size(n_seqs, total_tokens, h_qk, h_v)``
 * ``gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace)``
 * ``gdn_chunk_fwd_stages(..., stage_mask)`` (prep = 1, state with output = 2)
+* ``gdn_chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state)``
+  (the library's fixed per-GPU scratch as workspace, for callers that cannot allocate)
 * ``gdn_chunk_state_slots(n_seqs, total_tokens, h_qk, h_v)``
 * ``gdn_chunk_fwd_segmented_workspace_size(n_seqs, total_tokens, h_qk, h_v, segment_chunks)``
 * ``gdn_chunk_fwd_segmented(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
@@ -42,6 +44,8 @@ GDN_ERR_MISALIGNED = 3
 GDN_ERR_WORKSPACE = 4
 GDN_ERR_LAUNCH = 5
 
+GDN_NOALLOC_SCRATCH_BYTES = 128 << 20   # fixed workspace of gdn_chunk_fwd_noalloc, per GPU
+
 GDN_STATE_F32 = 0
 GDN_STATE_F16 = 1
 
@@ -55,6 +59,7 @@ EXPORTED_SYMBOLS = (
     "gdn_chunk_fwd_segmented",
     "gdn_recurrent_step",
     "gdn_recurrent_step_slots",
+    "gdn_chunk_fwd_noalloc",
     "gdn_check_chunk_inputs_host",
     "gdn_check_step_inputs_host",
     "gdn_status_string",
@@ -109,6 +114,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_recurrent_step_slots.argtypes = [vp, vp, vp, vp, vp, vp, c32, c32, vp, c32, c64, vp, vp, vp,
                                              dims_p, vp]
     lib.gdn_recurrent_step_slots.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, dims_p, vp]
+    lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.gdn_check_chunk_inputs_host.argtypes = [vp, vp, vp, vp, vp, vp, vp, dims_p]
     lib.gdn_check_chunk_inputs_host.restype = ctypes.c_int
     lib.gdn_check_step_inputs_host.argtypes = [vp, vp, vp, vp, vp, vp, c64, dims_p]
@@ -249,6 +256,22 @@ def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
                            _ptr(workspace), int(workspace_bytes),
                            _stream(stream, q, out, cu_seqlens))
     _check(lib, st, "gdn_chunk_fwd")
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
+                          *, dims: Optional[gdn_dims] = None, stream=None) -> None:
+    """Chunked prefill with the library's fixed per-GPU scratch as its workspace
+    (allocates nothing; batches up to GDN_NOALLOC_SCRATCH_BYTES of workspace;
+    overlapping calls on one GPU race).  See include/gdn.h."""
+    lib = load_library()
+    if dims is None:
+        dims = _prefill_dims(q, v, cu_seqlens)
+    _check_prefill(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, None, dims,
+                   "gdn_chunk_fwd_noalloc")
+    st = lib.gdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                   _ptr(initial_state), _ptr(out), _ptr(final_state), ctypes.byref(dims),
+                                   _stream(stream, q, out, cu_seqlens))
+    _check(lib, st, "gdn_chunk_fwd_noalloc")
 
 
 def gdn_chunk_fwd_stages(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace,

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libgdn.so")
 
-SOURCES = ["gdn_api.cpp", "gdn_validate.cpp", "gdn_chunk.hip", "gdn_prep.hip", "gdn_prep_stream.hip", "gdn_recurrent.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_validate.cpp", "gdn_chunk.hip", "gdn_prep.hip", "gdn_prep_stream.hip", "gdn_recurrent.hip", "gdn_noalloc.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

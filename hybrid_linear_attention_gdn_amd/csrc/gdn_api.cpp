@@ -89,15 +89,13 @@ gdn_status debug_check_step(const void* q, const void* k, const void* v, const f
 
 }  // namespace
 
-extern "C" {
-
-namespace {
-
-gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+// The prefill entry points' common body (also behind the no-allocation
+// variant in gdn_noalloc.hip, which passes its own scratch as the workspace).
+gdn_status gdn::chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
                           const int32_t* cu_seqlens, const float* initial_state, float* out,
                           float* final_state, float* chunk_states, const gdn_dims* dims,
                           void* workspace, size_t workspace_bytes, int stage_mask, void* stream,
-                          const char* what, int32_t seg_chunks = 0) {
+                          const char* what, int32_t seg_chunks) {
     if (stage_mask < 1 || stage_mask > 3)
         return fail(GDN_ERR_INVALID_VALUE, "stage_mask = %d is outside 1..3", stage_mask);
     gdn_status s = gdn::check_dims(dims);
@@ -161,7 +159,9 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
     return ok();
 }
 
-}  // namespace
+using gdn::chunk_fwd_impl;
+
+extern "C" {
 
 gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
                          const float* g, const float* beta,

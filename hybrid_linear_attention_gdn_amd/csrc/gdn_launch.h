@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdn.h"
 #include "gdn_device.h"
 
 namespace gdn {
@@ -36,6 +37,14 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
                             const float* s0, float* out, float* s_final, float* chunk_states,
                             const ChunkWorkspace& ws, int n_slots, int stage_mask,
                             const SegLaunch* seg, hipStream_t stream);
+
+// Body of the prefill entry points: host validation, workspace carving into
+// the regions above, and the launches (seg_chunks > 0: segment-parallel).
+gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const int32_t* cu_seqlens, const float* initial_state, float* out,
+                          float* final_state, float* chunk_states, const gdn_dims* dims,
+                          void* workspace, size_t workspace_bytes, int stage_mask, void* stream,
+                          const char* what, int32_t seg_chunks = 0);
 
 // Enqueues the per-token recurrent update on `stream`.
 hipError_t launch_recurrent_step(const uint16_t* q, const uint16_t* k, const uint16_t* v,

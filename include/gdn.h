@@ -293,6 +293,30 @@ gdn_status gdn_recurrent_step_slots(const void* q, const void* k, const void* v,
                                     void* stream);
 
 /*
+ * gdn_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The workspace is a fixed array of GDN_NOALLOC_SCRATCH_BYTES in the
+ * library's device code, one per GPU, held until the process ends; the call
+ * itself allocates nothing (no hipMalloc or hipFree, no allocating library
+ * routine).  Batches whose gdn_chunk_fwd_workspace_size exceeds it return
+ * GDN_ERR_WORKSPACE (128 MiB: up to about 4,700 tokens at 32 value / 16 q-k
+ * heads; 4000 tokens use 109 MiB).  The first call on a device looks up the
+ * array's address there.  Every call on one GPU uses that GPU's single copy:
+ * calls that overlap on one GPU (two streams, two threads) race and give
+ * undefined results; serialise them.  Arguments, results and other errors as
+ * gdn_chunk_fwd.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (128u << 20)
+gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta,
+                                 const int32_t* cu_seqlens,
+                                 const float* initial_state,
+                                 float* out,
+                                 float* final_state,
+                                 const gdn_dims* dims,
+                                 void* stream);
+
+/*
  * Device-content preconditions, checked on HOST copies of the inputs: a
  * debugging aid, and what every entry point runs on copies of its device
  * inputs when the environment variable GDN_DEBUG_CHECKS is set (to anything

@@ -309,3 +309,29 @@ def test_segmented_workspace_and_arguments(lib):
     assert call(4, need.value - 1) == gdn.GDN_ERR_WORKSPACE
     assert call(4, need.value, q=None) == gdn.GDN_ERR_INVALID_VALUE
     assert call(4, need.value, q=MIS) == gdn.GDN_ERR_MISALIGNED
+
+
+def test_noalloc_rejects_batches_beyond_its_scratch(lib):
+    """The fixed scratch holds GDN_NOALLOC_SCRATCH_BYTES; a batch that needs more
+    is refused on the host, before any device call, with the sizes named."""
+    import ctypes as ct
+    d = dims(1, 4800, 16, 32)
+    need = ct.c_size_t(0)
+    assert lib.gdn_chunk_fwd_workspace_size(ct.byref(d), ct.byref(need)) == 0
+    assert need.value > gdn.GDN_NOALLOC_SCRATCH_BYTES
+    st = lib.gdn_chunk_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, ct.byref(d), None)
+    assert st == gdn.GDN_ERR_WORKSPACE
+    msg = lib.gdn_get_last_error().decode()
+    assert str(need.value) in msg and str(gdn.GDN_NOALLOC_SCRATCH_BYTES) in msg
+    bad = dims(1, 64, 3, 4)
+    assert lib.gdn_chunk_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                     ct.byref(bad), None) == gdn.GDN_ERR_INVALID_VALUE
+    zero = dims(0, 0, 16, 32)
+    assert lib.gdn_chunk_fwd_noalloc(None, None, None, None, None, None, None, None, None,
+                                     ct.byref(zero), None) == gdn.GDN_SUCCESS
+
+
+def test_noalloc_header_size_matches_binding():
+    text = open(HEADER).read()
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == gdn.GDN_NOALLOC_SCRATCH_BYTES
