@@ -1,29 +1,42 @@
 #!/usr/bin/env python3
 """Benchmark of the Gated DeltaNet layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--leg all|prefill|varlen|long|verify]
 
-One step = one chunked prefill (gdn_chunk_fwd: prep, state, out) of one GDN
-layer over T = 4000 tokens, 32 value heads / 16 q-k heads, d = 128, bf16
-inputs, fp32 state and output, zero initial state -- the one-layer,
-4000-token workload of the "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page,
-section 2.  Inputs are synthetic, seeded and resident in HBM before timing.
+One step = one chunked prefill (gdn_chunk_fwd: intra-chunk preparation,
+inter-chunk state recurrence, output) of one GDN layer over T = 4000 tokens,
+32 value heads / 16 q-k heads, d = 128, bf16 inputs, fp32 state and output,
+zero initial state -- the one-layer, 4000-token workload of the "2080 Ti runs
+Qwen3.8-27B: a vLLM plugin" page, section 2.  Inputs are synthetic, seeded
+and resident in HBM before timing.
+
+The headline is the COLD step: before each of the K timed steps a 1 GiB fill
+(outside the step's event pair) evicts the 256 MB last-level cache and L2, so
+every step reads its inputs from HBM; ms_per_step is the mean over the K
+steps.  The warm figure (K steps back to back) is reported beside it.
+
+Algorithmic work is the layer's own (per token at these dims): 4,237,995
+flop (triangular products at half, the K K^T / Q K^T Grams once per q/k
+head) and 33,024 bytes of input and output (q, k, v bf16; g, beta, out fp32),
+plus 2 MiB per state read or written.  A kernel's share is the terms it
+evaluates and the layer I/O it reads or writes; its intermediates are not
+algorithmic bytes (they are reported as measured `traffic`).
 
 Printed as one JSON line:
-  value      prefill tokens/s per layer over the K timed steps (warm, back to back)
-  roofline   the dominant prefill kernel: algorithmic work per launch / its
-             mean launch time (HIP events on the launch stream), vs MI355X peak
-  verify     the speculative-verify leg (8 requests x 6 tokens, per-token state
-             snapshots kept) timed the same way, as a fraction of HBM bandwidth
-  verify_fp16_slots  the same verify over an fp16 state pool addressed through
-             a slot table (gdn_recurrent_step_slots)
-  decode     the same 8 requests, one token each, state advanced in place
-             (verify and decode also replayed from a HIP graph of 20 calls:
-             *_graph, the launch cost a serving loop does not pay per step)
-  prefill_snapshots  the prefill that also writes the fp32 state after every
-             64-token chunk (gdn_chunk_fwd_snapshots, for a prefix cache), as
-             a fraction of HBM bandwidth on its bytes
-  cpu_baseline  the CPU oracle (fp32 token recurrence) on host cores
+  value      prefill tokens/s per layer over the K cold steps
+  roofline   the dominant prefill kernel: its algorithmic bytes or flops
+             (the binding one) per launch / its mean launch time (HIP events
+             on the launch stream), vs MI355X peak; traffic = measured HBM
+             bytes per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a
+             plain copy) while the kernel source matches the profiled one
+  prefill    cold and warm step times, %MFMA and %HBM of the layer, stages
+  varlen     the 8-sequence packed batch (lengths U{512..4096}, random states)
+  long       one 131072-token sequence (slow decay)
+  verify     the speculative-verify step (8 requests x 6 tokens, per-token
+             state snapshots kept), as a fraction of HBM bandwidth; also over
+             an fp16 state pool (verify_fp16_slots) and one-token decode
+  prefill_snapshots  the prefill that also writes the state after every chunk
+  cpu_baseline  the CPU oracle (fp32 token recurrence) on the host's cores
 """
 
 from __future__ import annotations
@@ -41,49 +54,52 @@ if ROOT not in sys.path:
 PEAK_MFMA_F16 = 2.5e15      # dense fp16/bf16 matrix-core FLOP/s (MI355X)
 PEAK_HBM = 8.0e12           # HBM3E bytes/s (MI355X)
 PAGES_MS_T4000 = 1.35       # pages' hand-written CUDA kernel, 2x RTX 2080 Ti (context only)
+BOX_CPU_SHARE = 16          # host cores a one-GPU machine allots to the GPU's process
 
 H_V, H_QK, D, C = 32, 16, 128, 64
+STATE_BYTES = H_V * D * D * 4          # one fp32 state of one sequence (all value heads)
 
 
-def algorithmic_work():
-    """Per-token algorithmic flops and bytes of each prefill kernel (config dims).
+def layer_terms(h_v=H_V, h_qk=H_QK, d=D, c=C):
+    """Per-token flops of the layer's terms and per-token bytes of its I/O.
 
-    Flops count each causal (triangular) product at half and the K K^T / Q K^T
-    Grams once per q/k head; they are the layer's terms, each assigned to the
-    kernel that evaluates it: prep takes the decay, Grams, UT transform, W and
-    U; the state kernel the recurrence (W H, K^T U') and the output (Q S and
-    P U').  Bytes count each tensor of a kernel's interface read or written
-    once: bf16 inputs, fp32 g / beta / decay vectors / output, fp16
-    intermediates (-W, U and the six nonzero 16x32 blocks of P per value head,
-    K^T and Q fragments per q/k head)."""
-    prep_f = H_V * (C * (D + D) + C * C / 3) + H_QK * (C * D) + H_QK * (C * D)
-    state_f = H_V * (4 * D * D) + H_V * (2 * D * D) + H_V * (C * D)
-    qk_b = H_QK * D * 2          # one of q or k, bf16
-    v_b = H_V * D * 2
-    gb_b = H_V * 4               # one of g, beta, or one fp32 value per token and value head
-    f16_row = H_V * D * 2        # one of -W, U per token (per value head)
-    p_row = H_V * 6 * 16 * 32 * 2 // C   # P's six nonzero blocks per token (per value head)
-    qk_row = H_QK * D * 2        # K^T or Q fragments per token (per q/k head)
-    out_b = H_V * D * 4
-    work = 2 * f16_row + p_row + 2 * qk_row + 2 * gb_b   # the intermediates, each way
-    prep_b = 2 * qk_b + v_b + 2 * gb_b + work
-    state_b = work + out_b
+    Flops: the recurrence W H0 and K^T U' (4 d^2 per value head), the output
+    Q H0 (2 d^2) and P U' (C d, causal half), W and U (C d each, causal
+    half), the triangular solve (C^2 / 3), and per q/k head the Grams K K^T
+    and Q K^T (C d each, causal half)."""
+    f = {
+        "recurrence": h_v * 4 * d * d,
+        "out_qh": h_v * 2 * d * d,
+        "out_pu": h_v * c * d,
+        "w_u": h_v * 2 * c * d,
+        "solve": h_v * c * c / 3,
+        "gram_kk": h_qk * c * d,
+        "gram_qk": h_qk * c * d,
+    }
+    b = {"q": h_qk * d * 2, "k": h_qk * d * 2, "v": h_v * d * 2, "g": h_v * 4, "beta": h_v * 4,
+         "out": h_v * d * 4}
+    return f, b
+
+
+def kernel_work():
+    """Which layer terms and which layer I/O each prefill kernel evaluates.
+
+    gdn_chunk_prep: the decay, Grams, UT transform, W and U, and the output's
+    intra-chunk matrix; reads q, k, v, g, beta.  gdn_chunk_state: the
+    recurrence and the output; writes the output and the final states."""
+    f, b = layer_terms()
     return {
-        "prep": (prep_f, prep_b),
-        "state": (state_f, state_b),
-        "layer": (prep_f + state_f, 2 * qk_b + v_b + 2 * gb_b + out_b),
+        "gdn_chunk_prep": (f["solve"] + f["gram_kk"] + f["gram_qk"] + f["w_u"],
+                           b["q"] + b["k"] + b["v"] + b["g"] + b["beta"]),
+        "gdn_chunk_state": (f["recurrence"] + f["out_qh"] + f["out_pu"], b["out"]),
+        "layer": (sum(f.values()), sum(b.values())),
     }
 
 
 # HBM bytes per launch of the prefill kernels at T = 4000, from rocprofv3
-# FETCH_SIZE / WRITE_SIZE runs scaled by a plain 1 GiB copy (fetch x 2.0,
-# write x 1.0); valid only for the kernel source they were taken with.
-MEASURED_TRAFFIC = {
-    "gdn_chunk_prep": {"bytes": 181932334, "source_sha256_prefix": "b52136c7a5260ad0",
-                       "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_prep.h"},
-    "gdn_chunk_state": {"bytes": 180855143, "source_sha256_prefix": "efb32dfe6c1d428a",
-                        "source": "hybrid_linear_attention_gdn_amd/csrc/gdn_chunk.hip"},
-}
+# FETCH_SIZE / WRITE_SIZE runs of `bench.py --leg prefill` scaled by a plain
+# 1 GiB copy; valid only for the kernel sources they were taken with.
+MEASURED_TRAFFIC = {}
 
 
 def measured_traffic(kernel: str):
@@ -91,9 +107,12 @@ def measured_traffic(kernel: str):
     rec = MEASURED_TRAFFIC.get(kernel)
     if rec is None:
         return None
-    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != rec["source_sha256_prefix"]:
-            return None      # kernel changed since the counters were taken
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest()[:16] != rec["sources_sha256_prefix"]:
+        return None      # kernel changed since the counters were taken
     return rec["bytes"]
 
 
@@ -109,6 +128,21 @@ def time_launches(fn, n, torch):
     e1.record(s)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / 1e3 / n
+
+
+def time_cold(fn, n, flush, torch):
+    """Per-step times of n steps, each after a fill of `flush` that evicts the
+    last-level cache and L2 (outside its event pair).  Returns a sorted list (s)."""
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        flush.fill_(float(i))
+        ev[i][0].record(s)
+        fn()
+        ev[i][1].record(s)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) / 1e3 for a, b in ev)
 
 
 def time_graph(fn, n_inner, reps, torch):
@@ -132,9 +166,18 @@ def time_graph(fn, n_inner, reps, torch):
     return t
 
 
+def host_cores() -> int:
+    """Cores this process may run on, up to the box's share for one GPU."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, BOX_CPU_SHARE))
+
+
 def cpu_baseline(x, budget_s: float):
     import oracle
-    cores = min(16, os.cpu_count() or 1)
+    cores = host_cores()
     reps, t = 0, 0.0
     t0 = time.perf_counter()
     while True:
@@ -163,6 +206,251 @@ def cpu_baseline(x, budget_s: float):
                       f"{t:.1f} s wall, threads over (sequence, value head)"}
 
 
+class Prefill:
+    """Device copies of one prefill workload with its outputs and workspace."""
+
+    def __init__(self, x, torch, gdn, dev):
+        bf = torch.bfloat16
+        self.x = x
+        self.gdn = gdn
+        self.q = torch.from_numpy(x.q).to(dev, bf)
+        self.k = torch.from_numpy(x.k).to(dev, bf)
+        self.v = torch.from_numpy(x.v).to(dev, bf)
+        self.g = torch.from_numpy(x.g).to(dev)
+        self.beta = torch.from_numpy(x.beta).to(dev)
+        self.cu = torch.from_numpy(x.cu_seqlens).to(dev)
+        self.s0 = None if x.initial_state is None else torch.from_numpy(x.initial_state).to(dev)
+        self.out = torch.empty((x.total_tokens, x.h_v, x.d_v), device=dev)
+        self.fin = torch.empty((x.n_seqs, x.h_v, x.d_k, x.d_v), device=dev)
+        n = gdn.gdn_chunk_fwd_workspace_size(x.n_seqs, x.total_tokens, x.h_qk, x.h_v)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=dev)
+
+    def step(self):
+        self.gdn.gdn_chunk_fwd(self.q, self.k, self.v, self.g, self.beta, self.cu, self.s0,
+                               self.out, self.fin, self.ws)
+
+    def stage(self, mask):
+        self.gdn.gdn_chunk_fwd_stages(self.q, self.k, self.v, self.g, self.beta, self.cu, self.s0,
+                                      self.out, self.fin, self.ws, mask)
+
+    def algorithmic(self):
+        """Layer flops and bytes of this batch (states read if given, final states written)."""
+        f, b = kernel_work()["layer"]
+        T, N = self.x.total_tokens, self.x.n_seqs
+        states = N * (2 if self.x.initial_state is not None else 1)
+        return f * T, b * T + states * STATE_BYTES
+
+
+def layer_fractions(flops, nbytes, t):
+    return {"pct_mfma_peak": 100 * flops / t / PEAK_MFMA_F16, "pct_hbm_peak": 100 * nbytes / t / PEAK_HBM}
+
+
+def roofline_of(kernel, flops, nbytes, t):
+    """Roofline of one kernel from its algorithmic work and mean launch time:
+    the binding roof is the one with the longer ideal time."""
+    t_mfma, t_hbm = flops / PEAK_MFMA_F16, nbytes / PEAK_HBM
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_MFMA_F16 / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    traffic = measured_traffic(kernel)
+    roof.update({
+        "traffic": traffic,
+        "kernel": kernel,
+        "mean_launch_us": t * 1e6,
+        "algorithmic_flops_per_launch": flops,
+        "algorithmic_bytes_per_launch": nbytes,
+        "frac_mfma": t_mfma / t,
+        "frac_hbm": t_hbm / t,
+        "traffic_over_algorithmic_bytes": None if traffic is None else traffic / nbytes,
+    })
+    return roof
+
+
+def prefill_leg(args, torch, gi, gdn, dev, flush):
+    p = Prefill(gi.prefill_4000(), torch, gdn, dev)
+    T = p.x.total_tokens
+    for _ in range(args.warmup):
+        p.step()
+    torch.cuda.synchronize()
+
+    # Timed region: K cold steps (the headline), then K warm steps back to back.
+    cold = time_cold(p.step, args.steps, flush, torch)
+    t_cold = sum(cold) / len(cold)
+    t_warm = time_launches(p.step, args.steps, torch)
+
+    # Per-kernel durations: K warm steps launched stage by stage with HIP
+    # events between the kernels, on the launch stream (upper bounds: the
+    # events add a few microseconds of gap per kernel).
+    s = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev[i][0].record(s)
+        p.stage(1)
+        ev[i][1].record(s)
+        p.stage(2)
+        ev[i][2].record(s)
+    torch.cuda.synchronize()
+    stage_t = {
+        "gdn_chunk_prep": sum(e[0].elapsed_time(e[1]) for e in ev) / 1e3 / args.steps,
+        "gdn_chunk_state": sum(e[1].elapsed_time(e[2]) for e in ev) / 1e3 / args.steps,
+    }
+    p.step()
+    torch.cuda.synchronize()
+
+    work = kernel_work()
+    per_launch = {
+        "gdn_chunk_prep": (work["gdn_chunk_prep"][0] * T, work["gdn_chunk_prep"][1] * T),
+        "gdn_chunk_state": (work["gdn_chunk_state"][0] * T, work["gdn_chunk_state"][1] * T + STATE_BYTES),
+    }
+    dom = max(stage_t, key=stage_t.get)
+    roof = roofline_of(dom, *per_launch[dom], stage_t[dom])
+    flops, nbytes = p.algorithmic()
+    prefill = {
+        "workload": p.x.name,
+        "ms_per_layer_cold": t_cold * 1e3,
+        "ms_per_layer_cold_p10_p50_p90": [cold[min(len(cold) - 1, int(q * len(cold)))] * 1e3 for q in (0.1, 0.5, 0.9)],
+        "ms_per_layer_warm": t_warm * 1e3,
+        "tokens_per_s_warm": T / t_warm,
+        "algorithmic_flops": flops,
+        "algorithmic_bytes": nbytes,
+        "cold": layer_fractions(flops, nbytes, t_cold),
+        "warm": layer_fractions(flops, nbytes, t_warm),
+        "stage_us_warm": {n: t * 1e6 for n, t in stage_t.items()},
+        "stage_roofline": {n: {k: v for k, v in roofline_of(n, *per_launch[n], stage_t[n]).items()
+                               if k in ("bound", "frac", "frac_mfma", "frac_hbm", "traffic")}
+                           for n in stage_t},
+    }
+
+    # The same prefill writing the state after every chunk (a prefix cache's
+    # snapshots): 63 chunk states of 32 heads x 64 KB at T = 4000.
+    n_snap = gdn.gdn_chunk_state_slots(1, T, H_QK, H_V)
+    chunk_states = torch.empty((n_snap, H_V, D, D), dtype=torch.float32, device=dev)
+
+    def snap_step():
+        gdn.gdn_chunk_fwd_snapshots(p.q, p.k, p.v, p.g, p.beta, p.cu, None, p.out, p.fin, chunk_states, p.ws)
+
+    for _ in range(min(args.warmup, 100)):
+        snap_step()
+    t_snap = time_launches(snap_step, args.steps, torch)
+    del chunk_states
+    snap_bytes = ((T + C - 1) // C) * STATE_BYTES
+    snapshots = {
+        "workload": p.x.name + "_chunk_snapshots",
+        "us_per_step_warm": t_snap * 1e6,
+        "tokens_per_s": T / t_snap,
+        "snapshot_bytes": snap_bytes,
+        "pct_hbm_peak": 100 * (nbytes + snap_bytes) / t_snap / PEAK_HBM,
+        "us_over_prefill_warm": (t_snap - t_warm) * 1e6,
+    }
+    return p, t_cold, roof, prefill, snapshots
+
+
+def batch_leg(x, runs, torch, gdn, dev, flush):
+    """A bigger prefill batch, timed cold (median of `runs` steps after a cache flush)."""
+    p = Prefill(x, torch, gdn, dev)
+    p.step()
+    torch.cuda.synchronize()
+    cold = time_cold(p.step, runs, flush, torch)
+    t = cold[len(cold) // 2]
+    flops, nbytes = p.algorithmic()
+    res = {"workload": x.name, "n_seqs": x.n_seqs, "tokens": x.total_tokens,
+           "lengths": [int(n) for n in x.lengths][:16], "ms_cold_median": t * 1e3,
+           "tokens_per_s": x.total_tokens / t, **layer_fractions(flops, nbytes, t),
+           "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
+    del p
+    torch.cuda.empty_cache()
+    return res
+
+
+def verify_legs(args, torch, gi, gdn, dev):
+    y = gi.verify_8x6()
+    bf = torch.bfloat16
+    R, n_tok = 8, 6
+    vq = torch.from_numpy(y.q).to(dev, bf)
+    vk = torch.from_numpy(y.k).to(dev, bf)
+    vv = torch.from_numpy(y.v).to(dev, bf)
+    vg = torch.from_numpy(y.g).to(dev)
+    vb = torch.from_numpy(y.beta).to(dev)
+    s_in = torch.from_numpy(y.initial_state).to(dev)
+    vout = torch.empty((R * n_tok, H_V, D), device=dev)
+    inter = torch.empty((R, n_tok, H_V, D, D), device=dev)
+    tok_b = 2 * H_QK * D * 2 + H_V * D * 2 + 2 * H_V * 4 + H_V * D * 4
+
+    def vstep():
+        gdn.gdn_recurrent_step(vq, vk, vv, vg, vb, R, n_tok, s_in, None, vout, inter, True)
+
+    for _ in range(args.warmup):
+        vstep()
+    t_verify = time_launches(vstep, args.steps, torch)
+    t_verify_graph = time_graph(vstep, 20, max(1, args.steps // 20), torch)
+    v_bytes = R * STATE_BYTES + R * n_tok * STATE_BYTES + R * n_tok * tok_b
+    verify = {
+        "workload": y.name,
+        "us_per_step": t_verify * 1e6,
+        "tokens_per_s": R * n_tok / t_verify,
+        "algorithmic_bytes": v_bytes,
+        "achieved_GBps": v_bytes / t_verify / 1e9,
+        "pct_hbm_peak": 100 * v_bytes / t_verify / PEAK_HBM,
+        "us_per_step_graph": t_verify_graph * 1e6,
+        "pct_hbm_peak_graph": 100 * v_bytes / t_verify_graph / PEAK_HBM,
+    }
+    if args.leg == "verify":
+        return verify, None, None
+
+    # the same verify over an fp16 slot pool (state slots picked by a
+    # device-side table, as a serving loop with rollback runs it)
+    pool16 = torch.from_numpy(gi.state_pool(y, R * n_tok, f16=True)).to(dev)
+    table = torch.from_numpy(gi.slot_table_contiguous(R, n_tok, R)).to(dev)
+    cu_tok = torch.from_numpy(y.cu_seqlens).to(dev)
+
+    def sstep():
+        gdn.gdn_recurrent_step_slots(vq, vk, vv, vg, vb, cu_tok, R, n_tok, pool16, table, None, vout)
+
+    for _ in range(args.warmup):
+        sstep()
+    t_slots = time_launches(sstep, args.steps, torch)
+    half = STATE_BYTES // 2
+    s_bytes = R * half + R * n_tok * half + R * n_tok * tok_b
+    verify_f16 = {
+        "workload": y.name + "_fp16_slot_pool",
+        "us_per_step": t_slots * 1e6,
+        "tokens_per_s": R * n_tok / t_slots,
+        "algorithmic_bytes": s_bytes,
+        "achieved_GBps": s_bytes / t_slots / 1e9,
+        "pct_hbm_peak": 100 * s_bytes / t_slots / PEAK_HBM,
+    }
+
+    # decode: the same 8 requests, one token each (the first of each
+    # request's verify tokens), state advanced in place
+    dq, dk, dv = (t[::n_tok].contiguous() for t in (vq, vk, vv))
+    dg, db = vg[::n_tok].contiguous(), vb[::n_tok].contiguous()
+    d_state = s_in.clone()
+    dout = torch.empty((R, H_V, D), device=dev)
+
+    def dstep():
+        gdn.gdn_recurrent_step(dq, dk, dv, dg, db, R, 1, d_state, d_state, dout, None, False)
+
+    for _ in range(args.warmup):
+        dstep()
+    t_decode = time_launches(dstep, args.steps, torch)
+    t_decode_graph = time_graph(dstep, 20, max(1, args.steps // 20), torch)
+    d_bytes = 2 * R * STATE_BYTES + R * tok_b
+    decode = {
+        "workload": "decode_8req_1tok_hv32_hqk16_d128",
+        "us_per_step": t_decode * 1e6,
+        "tokens_per_s": R / t_decode,
+        "algorithmic_bytes": d_bytes,
+        "achieved_GBps": d_bytes / t_decode / 1e9,
+        "pct_hbm_peak": 100 * d_bytes / t_decode / PEAK_HBM,
+        "us_per_step_graph": t_decode_graph * 1e6,
+        "pct_hbm_peak_graph": 100 * d_bytes / t_decode_graph / PEAK_HBM,
+    }
+    return verify, verify_f16, decode
+
+
 def long_context(args):
     """The long-context workload (one sequence of 131072 tokens, g = -softplus(N(-2, 1))):
     gdn_chunk_fwd against gdn_chunk_fwd_segmented at a few segment lengths, at the
@@ -172,39 +460,31 @@ def long_context(args):
     import gdn_inputs as gi
     import hybrid_linear_attention_gdn_amd as gdn
 
-    dev, bf, T = torch.device("cuda:0"), torch.bfloat16, 131072
+    dev, T = torch.device("cuda:0"), 131072
     reps = max(1, min(args.steps, 5))
     res = {"metric": "long-context prefill ms per layer (T=131072)", "unit": "ms", "shapes": []}
     for hqk, hv in ((16, 32), (8, 16)):
         x = gi.make_inputs([T], hqk, hv, D, D, seed=0, g_mean=-2.0, name=f"long_{T}_hv{hv}_hqk{hqk}")
-        q = torch.from_numpy(x.q).to(dev, bf)
-        k = torch.from_numpy(x.k).to(dev, bf)
-        v = torch.from_numpy(x.v).to(dev, bf)
-        g = torch.from_numpy(x.g).to(dev)
-        beta = torch.from_numpy(x.beta).to(dev)
-        cu = torch.from_numpy(x.cu_seqlens).to(dev)
-        out = torch.empty((T, hv, D), device=dev)
-        fin = torch.empty((1, hv, D, D), device=dev)
-        ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(1, T, hqk, hv), dtype=torch.uint8, device=dev)
+        p = Prefill(x, torch, gdn, dev)
         row = {"workload": x.name}
 
         def timed(fn):
             fn()
             return time_launches(fn, reps, torch) * 1e3
 
-        row["serial_ms"] = timed(lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, cu, None, out, fin, ws))
-        row["serial_prep_ms"] = timed(lambda: gdn.gdn_chunk_fwd_stages(q, k, v, g, beta, cu, None, out, fin, ws, 1))
-        row["serial_state_ms"] = timed(lambda: gdn.gdn_chunk_fwd_stages(q, k, v, g, beta, cu, None, out, fin, ws, 2))
-        del ws
+        row["serial_ms"] = timed(p.step)
+        row["serial_prep_ms"] = timed(lambda: p.stage(1))
+        row["serial_state_ms"] = timed(lambda: p.stage(2))
+        del p.ws
         for sc in (1024, 512, 256):
             wss = torch.empty(gdn.gdn_chunk_fwd_segmented_workspace_size(1, T, hqk, hv, sc),
                               dtype=torch.uint8, device=dev)
             row[f"segmented_sc{sc}_ms"] = timed(
-                lambda: gdn.gdn_chunk_fwd_segmented(q, k, v, g, beta, cu, None, out, fin, sc, wss))
+                lambda: gdn.gdn_chunk_fwd_segmented(p.q, p.k, p.v, p.g, p.beta, p.cu, None, p.out, p.fin, sc, wss))
             del wss
         row["tokens_per_s_serial"] = T / (row["serial_ms"] * 1e-3)
         res["shapes"].append(row)
-        del q, k, v, out
+        del p
         torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 
@@ -212,10 +492,12 @@ def long_context(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the CPU-oracle baseline (0 skips it)")
+    ap.add_argument("--leg", choices=("all", "prefill", "varlen", "long", "verify"), default="all",
+                    help="run one leg only (for counter runs); the JSON line then holds that leg")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 5 plain device-to-device copies of BYTES bytes (reference for "
                          "the HBM byte counters) and exit")
@@ -223,6 +505,11 @@ def main():
                     help="only time the long-context prefill (T=131072) serially and segment-parallel "
                          "(gdn_chunk_fwd_segmented) at 32/16 and 16/8 heads, print one JSON line and exit")
     args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the layer on a single MI355X "
+              "(heads or sequences would shard across GPUs with no exchange); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
     if args.long:
         long_context(args)
         return
@@ -237,13 +524,6 @@ def main():
         print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 5}), flush=True)
         return
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this layer's path runs on a single MI355X "
-              "(heads or sequences would shard across GPUs with no exchange); run with --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
     import torch
 
     import gdn_inputs as gi
@@ -254,248 +534,56 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    bf = torch.bfloat16
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)     # 1 GiB
 
-    # ---------------- prefill workload (resident in HBM)
-    x = gi.prefill_4000()
-    T = x.total_tokens
-    q = torch.from_numpy(x.q).to(dev, bf)
-    k = torch.from_numpy(x.k).to(dev, bf)
-    v = torch.from_numpy(x.v).to(dev, bf)
-    g = torch.from_numpy(x.g).to(dev)
-    beta = torch.from_numpy(x.beta).to(dev)
-    cu = torch.from_numpy(x.cu_seqlens).to(dev)
-    out = torch.empty((T, H_V, D), device=dev)
-    fin = torch.empty((1, H_V, D, D), device=dev)
-    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(1, T, H_QK, H_V), dtype=torch.uint8, device=dev)
-
-    def step():
-        gdn.gdn_chunk_fwd(q, k, v, g, beta, cu, None, out, fin, ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Timed region: K steps back to back on the current stream.
-    t_step = time_launches(step, args.steps, torch)
-
-    # The same K steps again with HIP events between the two kernels of each
-    # step (launched stage by stage), for each kernel's mean duration.  The
-    # events add a few microseconds of gap per kernel, so these durations are
-    # upper bounds of the kernel times.
-    s = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    e_start = torch.cuda.Event(enable_timing=True)
-    e_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e_start.record(s)
-    for i in range(args.steps):
-        ev[i][0].record(s)
-        gdn.gdn_chunk_fwd_stages(q, k, v, g, beta, cu, None, out, fin, ws, 1)
-        ev[i][1].record(s)
-        gdn.gdn_chunk_fwd_stages(q, k, v, g, beta, cu, None, out, fin, ws, 2)
-        ev[i][2].record(s)
-    e_end.record(s)
-    torch.cuda.synchronize()
-    t_step_evented = e_start.elapsed_time(e_end) / 1e3 / args.steps
-    stage_t = {
-        "prep": sum(e[0].elapsed_time(e[1]) for e in ev) / 1e3 / args.steps,
-        "state": sum(e[1].elapsed_time(e[2]) for e in ev) / 1e3 / args.steps,
-    }
-    # spread of single steps (the evented pass: event to event, so each
-    # includes the gaps the events add)
-    per_step = sorted(e[0].elapsed_time(e[2]) * 1e3 for e in ev)
-    spread = {f"p{q}": per_step[min(len(per_step) - 1, int(q / 100 * len(per_step)))] for q in (10, 50, 90)}
-    step()
-    torch.cuda.synchronize()
-
-    # Cold steps: a 1 GiB fill between steps (outside the timed interval)
-    # evicts the 256 MB last-level cache and L2, so each timed step reads its
-    # inputs and intermediates from HBM.  Reported beside the warm figure.
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    n_cold = min(args.steps, 20)
-    cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_cold)]
-    for i in range(n_cold):
-        flush.fill_(float(i))
-        cold_ev[i][0].record(s)
-        step()
-        cold_ev[i][1].record(s)
-    torch.cuda.synchronize()
-    t_cold = sorted(e[0].elapsed_time(e[1]) for e in cold_ev)[n_cold // 2] / 1e3
-    del flush
-
-    # The same prefill writing the state after every chunk (a prefix cache's
-    # snapshots): 63 chunk states of 32 heads x 64 KB at T = 4000.
-    n_snap = gdn.gdn_chunk_state_slots(1, T, H_QK, H_V)
-    chunk_states = torch.empty((n_snap, H_V, D, D), dtype=torch.float32, device=dev)
-
-    def snap_step():
-        gdn.gdn_chunk_fwd_snapshots(q, k, v, g, beta, cu, None, out, fin, chunk_states, ws)
-
-    for _ in range(args.warmup):
-        snap_step()
-    t_snap = time_launches(snap_step, args.steps, torch)
-    del chunk_states
-
-    work = algorithmic_work()
-    state_bytes = H_V * D * D * 4          # one fp32 state per sequence (final state written)
-    per_seq = {"prep": 0, "state": state_bytes, "layer": state_bytes}
-    dom = max(stage_t, key=stage_t.get)
-    f_tok, b_tok = work[dom]
-    flops, nbytes = f_tok * T, b_tok * T + per_seq[dom]
-    t_dom = stage_t[dom]
-    if flops / PEAK_MFMA_F16 >= nbytes / PEAK_HBM:
-        roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": PEAK_MFMA_F16 / 1e12,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": nbytes / t_dom / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = f"gdn_chunk_{dom}"
-    roof["traffic"] = measured_traffic(roof["kernel"])
-    roof["mean_launch_us"] = t_dom * 1e6
-    roof["algorithmic_flops_per_launch"] = flops
-    roof["algorithmic_bytes_per_launch"] = nbytes
-
-    f_layer, b_layer = work["layer"]
-    prefill = {
-        "ms_per_layer": t_step * 1e3,
-        "ms_per_layer_with_events": t_step_evented * 1e3,
-        "ms_per_layer_cold_median": t_cold * 1e3,
-        "us_per_step_evented_p10_p50_p90": [spread["p10"], spread["p50"], spread["p90"]],
-        "pct_mfma_peak": 100 * f_layer * T / t_step / PEAK_MFMA_F16,
-        "pct_hbm_peak": 100 * (b_layer * T + per_seq["layer"]) / t_step / PEAK_HBM,
-        "algorithmic_flops": f_layer * T,
-        "algorithmic_bytes": b_layer * T + per_seq["layer"],
-        "stage_us": {n: t * 1e6 for n, t in stage_t.items()},
-        "stage_pct_of_roofline": {
-            n: 100 * max(work[n][0] * T / PEAK_MFMA_F16, (work[n][1] * T + per_seq[n]) / PEAK_HBM) / stage_t[n]
-            for n in stage_t},
-    }
-
-    snap_bytes = ((T + C - 1) // C) * state_bytes
-    snap_total = work["layer"][1] * T + per_seq["layer"] + snap_bytes
-    prefill_snapshots = {
-        "workload": x.name + "_chunk_snapshots",
-        "us_per_step": t_snap * 1e6,
-        "tokens_per_s": T / t_snap,
-        "snapshot_bytes": snap_bytes,
-        "algorithmic_bytes": snap_total,
-        "pct_hbm_peak": 100 * snap_total / t_snap / PEAK_HBM,
-        "us_over_prefill": (t_snap - t_step) * 1e6,
-    }
-
-    # ---------------- verify workload: 8 requests x (1 + 5) tokens, snapshots kept
-    y = gi.verify_8x6()
-    R, n_tok = 8, 6
-    vq = torch.from_numpy(y.q).to(dev, bf)
-    vk = torch.from_numpy(y.k).to(dev, bf)
-    vv = torch.from_numpy(y.v).to(dev, bf)
-    vg = torch.from_numpy(y.g).to(dev)
-    vb = torch.from_numpy(y.beta).to(dev)
-    s_in = torch.from_numpy(y.initial_state).to(dev)
-    vout = torch.empty((R * n_tok, H_V, D), device=dev)
-    inter = torch.empty((R, n_tok, H_V, D, D), device=dev)
-
-    def vstep():
-        gdn.gdn_recurrent_step(vq, vk, vv, vg, vb, R, n_tok, s_in, None, vout, inter, True)
-
-    for _ in range(args.warmup):
-        vstep()
-    t_verify = time_launches(vstep, args.steps, torch)
-    t_verify_graph = time_graph(vstep, 20, max(1, args.steps // 20), torch)
-    state_b = H_V * D * D * 4
-    v_bytes = R * state_b + R * n_tok * state_b + R * n_tok * (2 * H_QK * D * 2 + H_V * D * 2 + 2 * H_V * 4 + H_V * D * 4)
-    verify = {
-        "workload": y.name,
-        "us_per_step": t_verify * 1e6,
-        "tokens_per_s": R * n_tok / t_verify,
-        "algorithmic_bytes": v_bytes,
-        "achieved_GBps": v_bytes / t_verify / 1e9,
-        "pct_hbm_peak": 100 * v_bytes / t_verify / PEAK_HBM,
-        "us_per_step_graph": t_verify_graph * 1e6,
-        "pct_hbm_peak_graph": 100 * v_bytes / t_verify_graph / PEAK_HBM,
-    }
-
-    # ---------------- the same verify over an fp16 slot pool (state slots picked by
-    #                  a device-side table, as a serving loop with rollback runs it)
-    pool16 = torch.from_numpy(gi.state_pool(y, R * n_tok, f16=True)).to(dev)
-    table = torch.from_numpy(gi.slot_table_contiguous(R, n_tok, R)).to(dev)
-    cu_tok = torch.from_numpy(y.cu_seqlens).to(dev)
-
-    def sstep():
-        gdn.gdn_recurrent_step_slots(vq, vk, vv, vg, vb, cu_tok, R, n_tok, pool16, table, None, vout)
-
-    for _ in range(args.warmup):
-        sstep()
-    t_slots = time_launches(sstep, args.steps, torch)
-    state_h = H_V * D * D * 2
-    s_bytes = R * state_h + R * n_tok * state_h + R * n_tok * (2 * H_QK * D * 2 + H_V * D * 2 + 2 * H_V * 4 + H_V * D * 4)
-    verify_f16 = {
-        "workload": y.name + "_fp16_slot_pool",
-        "us_per_step": t_slots * 1e6,
-        "tokens_per_s": R * n_tok / t_slots,
-        "algorithmic_bytes": s_bytes,
-        "achieved_GBps": s_bytes / t_slots / 1e9,
-        "pct_hbm_peak": 100 * s_bytes / t_slots / PEAK_HBM,
-    }
-
-    # ---------------- decode: the same 8 requests, one token each (the first of
-    #                  each request's verify tokens), state advanced in place
-    dq, dk, dv = (t[::n_tok].contiguous() for t in (vq, vk, vv))
-    dg, db = vg[::n_tok].contiguous(), vb[::n_tok].contiguous()
-    d_state = s_in.clone()
-    dout = torch.empty((R, H_V, D), device=dev)
-
-    def dstep():
-        gdn.gdn_recurrent_step(dq, dk, dv, dg, db, R, 1, d_state, d_state, dout, None, False)
-
-    for _ in range(args.warmup):
-        dstep()
-    t_decode = time_launches(dstep, args.steps, torch)
-    t_decode_graph = time_graph(dstep, 20, max(1, args.steps // 20), torch)
-    d_bytes = 2 * R * state_b + R * (2 * H_QK * D * 2 + H_V * D * 2 + 2 * H_V * 4 + H_V * D * 4)
-    decode = {
-        "workload": "decode_8req_1tok_hv32_hqk16_d128",
-        "us_per_step": t_decode * 1e6,
-        "tokens_per_s": R / t_decode,
-        "algorithmic_bytes": d_bytes,
-        "achieved_GBps": d_bytes / t_decode / 1e9,
-        "pct_hbm_peak": 100 * d_bytes / t_decode / PEAK_HBM,
-        "us_per_step_graph": t_decode_graph * 1e6,
-        "pct_hbm_peak_graph": 100 * d_bytes / t_decode_graph / PEAK_HBM,
-    }
-
-    cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(x, args.cpu_seconds)
-
-    value = T / t_step
     line = {
         "metric": "GDN prefill tokens/s per layer (T=4000) & %MFMA peak; verify %HBM BW",
-        "value": value,
         "unit": "tokens/s per layer",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": t_step * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": value / (4000 / (PAGES_MS_T4000 * 1e-3)),
-        "vs_baseline_note": "pages' 1.35 ms per 4000-token layer on 2x RTX 2080 Ti (TP=2); context, not a target",
         "dtype": "f16",
         "dtype_note": "bf16 inputs widened to fp16 matrix-core operands, fp32 accumulation, state and output",
         "data": "synthetic",
-        "config": {"workload": x.name, "global_batch": 1, "seq_len": T, "n_heads_v": H_V,
-                   "n_heads_qk": H_QK, "d_k": D, "d_v": D, "chunk": C, "initial_state": "zeros (NULL)",
-                   "parallelism": "single GPU"},
-        "prefill": prefill,
-        "roofline": roof,
-        "verify": verify,
-        "verify_fp16_slots": verify_f16,
-        "decode": decode,
-        "prefill_snapshots": prefill_snapshots,
-        "cpu_baseline": cpu,
     }
+    if args.leg in ("all", "prefill"):
+        p, t_cold, roof, prefill, snapshots = prefill_leg(args, torch, gi, gdn, dev, flush)
+        T = p.x.total_tokens
+        line.update({
+            "value": T / t_cold,
+            "ms_per_step": t_cold * 1e3,
+            "vs_baseline": (T / t_cold) / (4000 / (PAGES_MS_T4000 * 1e-3)),
+            "vs_baseline_note": "against the pages' 1.35 ms per 4000-token layer on 2x RTX 2080 Ti "
+                                "(TP=2): another machine's figure, context only",
+            "config": {"workload": p.x.name, "global_batch": 1, "seq_len": T, "n_heads_v": H_V,
+                       "n_heads_qk": H_QK, "d_k": D, "d_v": D, "chunk": C, "initial_state": "zeros (NULL)",
+                       "timing": "cold: 1 GiB cache flush before each timed step", "parallelism": "single GPU"},
+            "roofline": roof,
+            "prefill": prefill,
+            "prefill_snapshots": snapshots,
+        })
+        del p
+        torch.cuda.empty_cache()
+    if args.leg in ("all", "varlen"):
+        line["varlen"] = batch_leg(gi.varlen_8(), max(3, min(args.steps, 20)), torch, gdn, dev, flush)
+    if args.leg in ("all", "long"):
+        line["long"] = batch_leg(gi.long_131072(), 3, torch, gdn, dev, flush)
+    if args.leg in ("all", "verify"):
+        verify, verify_f16, decode = verify_legs(args, torch, gi, gdn, dev)
+        line["verify"] = verify
+        if verify_f16 is not None:
+            line["verify_fp16_slots"] = verify_f16
+            line["decode"] = decode
+    if args.leg == "all" and args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(gi.prefill_4000(), args.cpu_seconds)
+    if "value" not in line:      # a single non-prefill leg: its own figure
+        leg = next(k for k in ("varlen", "long", "verify") if k in line)
+        line["value"] = line[leg]["tokens_per_s"]
+        line["ms_per_step"] = line[leg].get("ms_cold_median", line[leg].get("us_per_step", 0) / 1e3)
+        line["config"] = {"workload": line[leg]["workload"]}
+        line["vs_baseline"] = None
     print(json.dumps(line), flush=True)
 
 
