@@ -127,8 +127,7 @@ gdn_status gdn::chunk_fwd_impl(const void* q, const void* k, const void* v, cons
 
     char* base = static_cast<char*>(workspace);
     gdn::ChunkWorkspace ws;
-    ws.w = reinterpret_cast<gdn::f16*>(base + L.w);
-    ws.u = reinterpret_cast<gdn::f16*>(base + L.u);
+    ws.tu = reinterpret_cast<gdn::f16*>(base + L.tu);
     ws.p = reinterpret_cast<gdn::f16*>(base + L.p);
     ws.dg = reinterpret_cast<float*>(base + L.dg);
     ws.kt = reinterpret_cast<gdn::f16*>(base + L.kt);

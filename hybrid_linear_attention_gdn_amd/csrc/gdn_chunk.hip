@@ -37,48 +37,60 @@ namespace gdn {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Stage 2: inter-chunk state recurrence with the output.  One workgroup of
-// three waves per (sequence, value head, 16-column tile), specialised:
+// Stage 2: inter-chunk state recurrence with the output.  One workgroup per
+// (sequence, value head, 16-column tile), its waves specialised:
 //   * the chain wave keeps the tile's 128 x 16 slice of the state in
 //     accumulator registers (8 tiles of 16 d_k rows) for the whole sequence.
 //     Per chunk it runs the 32 matrix-core products of U' = U - W H0 and
-//     H_C = e^{G_C} H0 + K^T D U', the dependency from chunk to chunk (-W,
-//     K^T and the decay vector from LDS, its U fragments by register loads
-//     one chunk ahead), and hands U' and the new state, rounded to fp16 as B
-//     operands, to the output wave through double-buffered LDS slots;
+//     H_C = e^{G_C} H0 + K^T D U', the dependency from chunk to chunk (-W and
+//     U from the W wave, K^T and the decay vector from the copy ring, all in
+//     LDS), and hands U' and the new state, rounded to fp16 as B operands, to
+//     the output wave through double-buffered LDS slots;
 //   * the output wave forms O = diag(e^G) (Q H0) + P U' on its own SIMD:
 //     the Q H0 half in the interval of the chunk (Q fragments by register
-//     loads one interval ahead, e^G from the stage), the P U' half one
+//     loads one interval ahead, e^G from the ring), the P U' half one
 //     interval later, when U' has been handed over (P by register loads in
-//     the chunk's interval); it stores O to global memory.  Taking Q
-//     straight to its registers keeps 16 KB per chunk off the copy wave and
-//     out of LDS;
-//   * the copy wave issues direct global-to-LDS copies of -W, K^T and the
-//     decay vectors into a ring of three stages, two chunks ahead, and
-//     touches the operands of the chunk two beyond those (Q, U and P
-//     included) into L2.
+//     the chunk's interval); it stores O to global memory;
+//   * two W waves (one for a tile pair) form, one chunk ahead of the chain,
+//     -W = -TU diag(e^G) K (48 products: -W^T = K^T (TU diag(-e^G))^T from
+//     the K^T and TU fragments in the ring) and the tile's U = TU V (six
+//     products from the tile's value rows in the ring, read transposed),
+//     each wave about half of both, so that W and U, 32 KB per chunk and
+//     value head, never go through memory: prep stores only the 6 KB of TU;
+//   * the copy wave issues direct global-to-LDS copies of K^T, TU, the decay
+//     vectors and the tile's value rows into a ring of kStages stages, and
+//     touches the operands of a chunk two beyond those (Q and P included)
+//     into L2.
 // The waves meet at one barrier per chunk.  The copy wave issues a fixed
 // number of copies per chunk, so one memory-counter wait makes a stage ready
 // before that barrier.  The eight tiles of a head run on one XCD so that its
 // L2 serves the shared fragments.  An affine map has no output: its
-// workgroups have a chain and a copy wave only.  When a batch has more tiles
+// workgroups have chain, W and copy waves.  When a batch has more tiles
 // than the GPU has CUs, so that the workgroups run in rounds, a workgroup
 // takes a pair of adjacent tiles: two chain waves on two SIMDs share the
-// copy ring (-W, K^T and the decay vectors are the same for both) and one
-// output wave forms both tiles' output from one set of Q and P fragments,
-// which halves the operand traffic per tile and the number of rounds.
+// ring and the W wave's -W (the W wave forms both tiles' U), and one output
+// wave forms both tiles' output from one set of Q and P fragments, which
+// halves the operand traffic per tile and the number of rounds.
 // ---------------------------------------------------------------------------
-constexpr int kStages = 3;
-constexpr int kUTile = 4 * 64 * 4;                           // halves of U fragments per column tile
+constexpr int kVRowElems = 16;                               // halves of one tile's row of V
 constexpr int kHbElems = 4 * 64 * 8;                         // halves of the state's four B fragments
 constexpr int kUbElems = 2 * 64 * 8;                         // halves of U''s two B fragments
-constexpr int kCopiesPerChunk = 16 + 16 + 2;                 // -W, K^T, decay vectors
+constexpr int kUaccElems = 4 * 64 * 4;                       // floats of a tile's U accumulators
 
+template <int kChains>
 struct StateStage {
-    f16 w[kWElems];
-    f16 k[kKtElems];
+    static constexpr int kTiles = kChains;
+    f16 k[kKtElems];                                         // K^T A fragments
+    f16 tu[kTuElems];                                        // TU fragments
     float dg[kGElems];        // e^{G_C - G_r} (r < 63) and e^{G_C} in entry 63; then e^{G_r}
+    uint16_t v[kChains][kChunk * kVRowElems];                // the tiles' value rows, bf16 [pos][16]
 };
+
+// Copies per chunk: 1 KB pieces (16 B per lane) of K^T (16) and TU (6), the
+// two 256 B decay vectors (4 B per lane), and per tile the 64 value rows of
+// 32 B (two 16-byte halves per row, 32 rows per copy).
+template <int kChains>
+constexpr int copies_per_chunk() { return 16 + 6 + 2 + 2 * kChains; }
 
 // s_waitcnt with vmcnt = N and the other counters left alone (gfx9 encoding).
 template <int N>
@@ -97,62 +109,98 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// One chunk's copies: 1 KB pieces (16 B per lane) of -W and K^T, and the
-// two 256 B decay vectors (4 B per lane).
-__device__ __forceinline__ void state_copy(StateStage& st, const ChunkWorkspace& ws, size_t vu, size_t ku,
-                                           int lane) {
-    const f16* wsrc = ws.w + vu * kWElems;
-    const f16* ksrc = ws.kt + ku * kKtElems;
-    const float* gsrc = ws.dg + vu * kGElems;
+// Where one chunk's operands come from.  vu / ku: workspace units of the
+// value head and of its q/k head; vrow: the chunk's first token row of v
+// (value head h, column 0); len: its valid rows.
+struct ChunkSrc {
+    size_t vu, ku;
+    const uint16_t* vrow;
+    int len;
+};
+
+// One chunk's copies into a stage.  Value rows past the chunk's end read its
+// last valid row instead: TU's columns for those positions are zero, so they
+// contribute nothing, and no read leaves the sequence.
+template <typename Stage>
+__device__ __forceinline__ void state_copy(Stage& st, const ChunkWorkspace& ws, const ChunkSrc& s,
+                                           const int* ct, size_t row_stride, int lane) {
+    // (the operands go through void pointers: typed ones make the host pass
+    //  of this template reject the builtin, and typed 4-byte copies tripped a
+    //  code-generation fault of the ROCm 7.2 compiler in this kernel)
+    constexpr int kChains = Stage::kTiles;
+    const f16* ksrc = ws.kt + s.ku * kKtElems;
+    const f16* tsrc = ws.tu + s.vu * kTuElems;
+    const float* gsrc = ws.dg + s.vu * kGElems;
 #pragma unroll
-    for (int piece = 0; piece < 16; ++piece) {
-        __builtin_amdgcn_global_load_lds(wsrc + (piece * 64 + lane) * 8, st.w + piece * 512, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(ksrc + (piece * 64 + lane) * 8, st.k + piece * 512, 16, 0, 0);
-    }
-    // (the casts keep these 4-byte copies from tripping a code-generation
-    //  fault of the ROCm 7.2 compiler in this kernel)
+    for (int piece = 0; piece < 16; ++piece)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ksrc + (piece * 64 + lane) * 8),
+                                         reinterpret_cast<void*>(st.k + piece * 512), 16, 0, 0);
+#pragma unroll
+    for (int piece = 0; piece < 6; ++piece)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tsrc + (piece * 64 + lane) * 8),
+                                         reinterpret_cast<void*>(st.tu + piece * 512), 16, 0, 0);
 #pragma unroll
     for (int half = 0; half < 2; ++half)
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gsrc + kChunk * half + lane),
                                          reinterpret_cast<void*>(st.dg + kChunk * half), 4, 0, 0);
-}
-
-// Touch one chunk's operands into L2 two chunks before their copies, with
-// 4-byte direct-to-LDS copies into a sink nobody reads (one cache line per
-// lane).  First copy: the 384 lines of -W, K^T and Q, split over the 8
-// column tiles of a head (lanes 0-47), and the 16 lines of the tile's own U
-// (lanes 48-63).  Second copy: the 48 lines of P, 6 per tile (lanes past 6
-// repeat a line).  A direct copy, unlike a register load, is invisible to the
-// compiler's counter waits, so the copy wave's own single wait still covers
-// it.  It pays where the operands come from HBM (long sequences).
-constexpr int kTouchesPerChunk = 2;
-
-__device__ __forceinline__ void state_touch(const ChunkWorkspace& ws, size_t vu, size_t ku, int ct, int lane,
-                                            float* sink) {
-    const f16* base;
-    if (lane < 48) {
-        const int line = ct * 48 + lane;
-        const int arr = line >> 7, off = (line & 127) * 64;      // halves
-        base = (arr == 0 ? ws.w + vu * kWElems : arr == 1 ? ws.kt + ku * kKtElems : ws.qf + ku * kQfElems) + off;
-    } else {
-        base = ws.u + vu * kUElems + (size_t)ct * kUTile + (lane - 48) * 64;
-    }
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base), reinterpret_cast<void*>(sink), 4, 0, 0);
-    const f16* pl = ws.p + vu * kPElems + (ct * 6 + min(lane, 5)) * 64;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(pl), reinterpret_cast<void*>(sink), 4, 0, 0);
-}
-
-// The tile's U fragments of one chunk, as four 8-byte register loads.
-struct UFrag {
-    f16x4 f[4];
-};
-
-__device__ __forceinline__ UFrag load_u(const ChunkWorkspace& ws, size_t vu, int ct, int lane) {
-    const f16* src = ws.u + vu * kUElems + (size_t)ct * kUTile;
-    UFrag u;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) u.f[p] = *reinterpret_cast<const f16x4*>(src + (p * 64 + lane) * 4);
-    return u;
+    for (int r = 0; r < kChains; ++r)
+#pragma unroll
+        for (int piece = 0; piece < 2; ++piece) {
+            const int row = min(32 * piece + (lane >> 1), s.len - 1);
+            const uint16_t* src = s.vrow + (size_t)row * row_stride + kVRowElems * ct[r] + 8 * (lane & 1);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                             reinterpret_cast<void*>(st.v[r] + piece * 512), 16, 0, 0);
+        }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// The tile's value rows of one chunk (bf16 [pos][16] in the stage) as the B
+// fragment of U = TU V over the position slots of K-step qq, column ln,
+// widened to fp16: two LDS transpose reads (ds_read_b64_tr_b16).  In each
+// group of 16 lanes that instruction hands lane l element l % 4 of the
+// 8-byte granules addressed by lanes l / 4 + 4 e, e = 0..3.  Lane l of group
+// gq addresses row 32 qq + 16 h + 4 gq + l / 4 at granule l % 4, so it
+// receives rows 32 qq + 16 h + 4 gq + e of column l: position slots 4 h + e.
+__device__ __forceinline__ f16x8 v_frag(const uint16_t* vrows, int qq, int gq, int ln) {
+    f16x8 f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = 32 * qq + 16 * h + 4 * gq + (ln >> 2);
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vrows + row * kVRowElems + 4 * (ln & 3)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            f[4 * h + e] = static_cast<f16>(__uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(x[e])) << 16));
+    }
+    return f;
+}
+
+// Touch one chunk's operands into L2 ahead of their copies and loads, with
+// 4-byte direct-to-LDS copies into a sink nobody reads (one cache line per
+// lane), two per tile: the 352 shared lines of K^T, Q, TU and P split over
+// the 8 column tiles of a head (44 per tile; lanes past 44 repeat a line),
+// and the tile's 64 value-row lines.  A direct copy, unlike a register load,
+// is invisible to the compiler's counter waits, so the copy wave's own
+// single wait still covers it.  (Issued from a W wave, which never waits for
+// its memory counter, the value touches were slower: a touch that waits on
+// HBM holds one of the CU's outstanding-request slots the copies need.)
+__device__ __forceinline__ void touch_shared(const ChunkWorkspace& ws, const ChunkSrc& s, int ct, int lane,
+                                             float* sink) {
+    const int line = ct * 44 + min(lane, 43);
+    const int off = (line & 127) * 64;                       // halves
+    const f16* base = line < 128 ? ws.kt + s.ku * kKtElems + off
+                    : line < 256 ? ws.qf + s.ku * kQfElems + off
+                    : line < 304 ? ws.tu + s.vu * kTuElems + (line - 256) * 64
+                                 : ws.p + s.vu * kPElems + (line - 304) * 64;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base), reinterpret_cast<void*>(sink), 4, 0, 0);
+}
+
+__device__ __forceinline__ void touch_values(const ChunkSrc& s, int ct, size_t row_stride, int lane, float* sink) {
+    const uint16_t* vl = s.vrow + (size_t)min(lane, s.len - 1) * row_stride + kVRowElems * ct;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vl), reinterpret_cast<void*>(sink), 4, 0, 0);
 }
 
 // Q's 16 fragments of one chunk, as sixteen 16-byte register loads.
@@ -181,24 +229,98 @@ __device__ __forceinline__ PFrag load_p(const ChunkWorkspace& ws, size_t vu, int
     return pf;
 }
 
+// The (row tile, K-step) blocks of TU's six nonzero fragments, in storage order.
+__device__ __forceinline__ constexpr int tu_pt(int f) { return f < 2 ? f : 2 + ((f - 2) >> 1); }
+__device__ __forceinline__ constexpr int tu_qq(int f) { return f < 2 ? 0 : (f - 2) & 1; }
+
+// A W wave's step for one chunk (stage st): the chain's A fragments of -W
+// over d_k K-steps kQd0 .. kQd1 - 1 into wdst.
+//   -W^T[d][r] = sum_s K^T[d][s] (-e^{G_s} TU[r][s]): A = the K^T fragment
+//   (d_k tile i, K-step qq), B = TU's fragment (row tile pt, K-step qq) with
+//   each position slot scaled by -e^{G_s} (an A and a B fragment share one
+//   lane layout); the accumulators of d_k tiles 2 qq', 2 qq' + 1 stacked are
+//   the chain's A fragment (p, qq') of -W.  The scaling is a packed fp16
+//   product: TU is fp16 already and the product is rounded to fp16 as the
+//   operand anyway; e^{G_s} below fp16's normal range (G_s < -9.7) loses
+//   relative precision there, where the entries' share of W is as small.
+template <int kQd0, int kQd1, typename Stage>
+__device__ __forceinline__ void w_chunk(const Stage& st, f16* wdst, int lane, int gq) {
+    f16x8 ng[2];                                             // -e^{G_s} over the slots of K-step qq
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(&st.dg[kChunk + 32 * qq + 4 * gq]);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(&st.dg[kChunk + 32 * qq + 16 + 4 * gq]);
+        ng[qq] = cat_to_f16(-g0, -g1);
+    }
+    f16x8 twb[6];
+#pragma unroll
+    for (int f = 0; f < 6; ++f) twb[f] = *reinterpret_cast<const f16x8*>(&st.tu[(f * 64 + lane) * 8]) * ng[tu_qq(f)];
+#pragma unroll
+    for (int qd = kQd0; qd < kQd1; ++qd) {
+        f16x8 ka[2][2];                                      // K^T fragments (i = 2 qd + a, K-step qq)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq)
+                ka[a][qq] = *reinterpret_cast<const f16x8*>(&st.k[(((2 * qd + a) * 2 + qq) * 64 + lane) * 8]);
+        f32x4 acc[2][4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) acc[a][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < 6; ++f)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) acc[a][tu_pt(f)] = mfma_f16(ka[a][tu_qq(f)], twb[f], acc[a][tu_pt(f)]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            *reinterpret_cast<f16x8*>(&wdst[((p * 4 + qd) * 64 + lane) * 8]) = cat_to_f16(acc[0][p], acc[1][p]);
+    }
+}
+
+// Row tiles kPt0 .. kPt1 - 1 of a tile's U = TU V for one chunk into udst
+// as fp32 accumulator fragments (rows 16 p + 4 gq + e, column ln of the
+// tile): A = TU's fragment, B = the tile's values over the same position
+// slots (v_frag).  Row tiles 0-1 need only K-step 0.
+template <int kPt0, int kPt1, typename Stage>
+__device__ __forceinline__ void u_part(const Stage& st, int r, float* udst, int lane, int gq, int ln) {
+    constexpr int kQq = kPt1 > 2 ? 2 : 1;
+    f16x8 vb[2];
+#pragma unroll
+    for (int qq = 0; qq < kQq; ++qq) vb[qq] = v_frag(st.v[r], qq, gq, ln);
+    f32x4 u[4];
+#pragma unroll
+    for (int p = kPt0; p < kPt1; ++p) u[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int f = 0; f < 6; ++f) {
+        if (tu_pt(f) < kPt0 || tu_pt(f) >= kPt1) continue;
+        u[tu_pt(f)] = mfma_f16(*reinterpret_cast<const f16x8*>(&st.tu[(f * 64 + lane) * 8]), vb[tu_qq(f)],
+                               u[tu_pt(f)]);
+    }
+#pragma unroll
+    for (int p = kPt0; p < kPt1; ++p) *reinterpret_cast<f32x4*>(&udst[(p * 64 + lane) * 4]) = u[p];
+}
+
 // The chain wave's step for one chunk: H0 (fp32 accumulators H, its fp16 B
-// fragments hb) -> H_C, and hb <- fp16 B fragments of H_C.  With the output,
-// U' goes to ub and H_C's fragments to hd for the output wave.
-template <bool kOut, bool kSnap>
-__device__ __forceinline__ void chain_chunk(f32x4 (&H)[8], f16x8 (&hb)[4], const StateStage& st, const UFrag& u,
-                                            f16* ub, f16* hd, float* snap, bool use_u, int lane, int gq, int ln) {
+// fragments hb) -> H_C, and hb <- fp16 B fragments of H_C.  -W comes from
+// wsrc, U (fp32 accumulator fragments) from usrc, K^T and the decay vector
+// from the stage.  With the output, U' goes to ub and H_C's fragments to hd
+// for the output wave.
+template <bool kOut, bool kSnap, typename Stage>
+__device__ __forceinline__ void chain_chunk(f32x4 (&H)[8], f16x8 (&hb)[4], const Stage& st,
+                                            const f16* wsrc, const float* usrc, f16* ub, f16* hd, float* snap,
+                                            bool use_u, int lane, int gq, int ln) {
     // U' = U + (-W) H0: the fragments are read before the burst, whose 4
     // accumulator chains interleave
     f32x4 acc[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[p][e] = use_u ? static_cast<float>(u.f[p][e]) : 0.f;
+        acc[p] = use_u ? *reinterpret_cast<const f32x4*>(&usrc[(p * 64 + lane) * 4]) : f32x4{0.f, 0.f, 0.f, 0.f};
     f16x8 wa[4][4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) wa[qq][p] = *reinterpret_cast<const f16x8*>(&st.w[((p * 4 + qq) * 64 + lane) * 8]);
+        for (int p = 0; p < 4; ++p) wa[qq][p] = *reinterpret_cast<const f16x8*>(&wsrc[((p * 4 + qq) * 64 + lane) * 8]);
     f16x8 ka[2][8];
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
@@ -259,7 +381,7 @@ __device__ __forceinline__ void chain_chunk(f32x4 (&H)[8], f16x8 (&hb)[4], const
 // of the tile.
 
 // The output wave's first half of a chunk: diag(e^G) (Q H0) into oacc.
-__device__ __forceinline__ void out_begin(f32x4 (&oacc)[4], const StateStage& st, const QFrag& qf, const f16* hsrc,
+__device__ __forceinline__ void out_begin(f32x4 (&oacc)[4], const float* dg, const QFrag& qf, const f16* hsrc,
                                           int lane, int ln) {
     f16x8 hb[4];
 #pragma unroll
@@ -276,7 +398,7 @@ __device__ __forceinline__ void out_begin(f32x4 (&oacc)[4], const StateStage& st
 #pragma unroll
         for (int p = 0; p < 4; ++p) oacc[p] = mfma_f16(hb[qq], qa[qq][p], oacc[p]);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) oacc[p] *= st.dg[kChunk + 16 * p + ln];
+    for (int p = 0; p < 4; ++p) oacc[p] *= dg[kChunk + 16 * p + ln];
 }
 
 // The output wave's second half: + P U', then the stores of the output rows
@@ -362,11 +484,23 @@ __host__ __device__ constexpr int mode_base(int mode) {
                                                : mode == kModeMapPair ? kModeMap : mode;
 }
 
-// Threads of a state workgroup: chain, output and copy waves; an affine map
-// has no output wave; a tile pair has two chain waves.
+// W waves of a state workgroup: two (about half of -W and U each) for one
+// tile, whose interval is short; one for a tile pair, whose longer interval
+// it fits.
+__host__ __device__ constexpr int w_waves(int mode) { return mode_pair(mode) ? 1 : 2; }
+
+// Threads of a state workgroup: chain, output, W and copy waves; an affine
+// map has no output wave; a tile pair has two chain waves.
 __host__ __device__ constexpr int state_threads(int mode) {
-    return 64 * ((mode_pair(mode) ? 2 : 1) + (mode_base(mode) == kModeMap ? 0 : 1) + 1);
+    return 64 * ((mode_pair(mode) ? 2 : 1) + (mode_base(mode) == kModeMap ? 0 : 1) + w_waves(mode) + 1);
 }
+
+// Stages of the copy ring.  The W wave uses a chunk's stage one interval
+// before the chain, so a chunk must have landed two intervals ahead: with
+// four stages its copies are issued three intervals ahead (one interval to
+// land); a tile pair's larger stages leave room for three, issued two ahead
+// and waited for in the same interval.
+__host__ __device__ constexpr int ring_stages(int mode) { return mode_pair(mode) ? 3 : 4; }
 
 // Workgroups of a state launch over `units` units of kTiles tiles each.
 constexpr unsigned state_grid(int units, int tiles) { return 8u * tiles * 2u * (unsigned)((units + 15) / 16); }
@@ -381,7 +515,7 @@ constexpr unsigned state_grid(int units, int tiles) { return 8u * tiles * 2u * (
 // serves; consecutive unit pairs go to different XCDs.
 template <int kMode>
 __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
-    const int32_t* __restrict__ cu, int n_seqs, int h_v,
+    const int32_t* __restrict__ cu, int n_seqs, int h_v, const uint16_t* __restrict__ v,
     const float* s0, float* s_final, float* __restrict__ out, float* __restrict__ chunk_states,
     ChunkWorkspace ws, SegArgs sa)
 {
@@ -392,7 +526,16 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
     constexpr int kChains = kPair ? 2 : 1;                   // chain waves: roles 0 .. kChains - 1
     constexpr int kTiles = (kBase == kModeMap ? 16 : 8) / kChains;
     constexpr bool kSeg = kBase == kModeSegment || kBase == kModeMap;
-    constexpr int kCopyRole = state_threads(kMode) / 64 - 1;
+    constexpr int kStages = ring_stages(kMode);
+    constexpr int kAhead = kStages - 1;                      // copies issued this many chunks ahead
+    constexpr int kCopies = copies_per_chunk<kChains>();
+    constexpr int kTouches = 2 * kChains;                    // the copy wave's touches per chunk
+    constexpr int kTouchAhead = kAhead + 2;                  // chunks ahead of use that the touches reach
+    constexpr int kOutRole = kChains;                        // when kOut
+    constexpr int kWRole = kChains + (kOut ? 1 : 0);         // first W wave
+    constexpr int kWWaves = w_waves(kMode);
+    constexpr int kCopyRole = kWRole + kWWaves;
+    static_assert(state_threads(kMode) == 64 * (kCopyRole + 1), "one wave per role");
     const int b = blockIdx.x;
     const int m = b >> 3;
     const int gu = m / kTiles;
@@ -414,7 +557,7 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
 
     const int lane = threadIdx.x & 63;
     // roles: chain waves first (one per column tile), then the output wave,
-    // then the copy wave
+    // the W wave and the copy wave
     const int role = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int gq = lane >> 4;
     const int ln = lane & 15;
@@ -422,10 +565,13 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
     // 8-15 R's), and its column tile (the output wave takes all of them)
     auto gtile_of = [&](int r) { return kPair ? 2 * tile + r : tile; };
     auto tile_of = [&](int r) { return kBase == kModeMap ? gtile_of(r) & 7 : kPair ? 2 * tile + r : (tile & 7); };
+    auto phi_of = [&](int r) { return kBase == kModeMap && gtile_of(r) < 8; };   // a map's Phi tile: no U
 
-    __shared__ __attribute__((aligned(16))) StateStage stage[kStages];
-    __shared__ __attribute__((aligned(16))) f16 hbuf[kChains][2][kHbElems];  // chain -> output: fp16 state
-    __shared__ __attribute__((aligned(16))) f16 ubuf[kChains][2][kUbElems];  // chain -> output: fp16 U'
+    __shared__ __attribute__((aligned(16))) StateStage<kChains> stage[kStages];
+    __shared__ __attribute__((aligned(16))) f16 wbuf[2][kWElems];                  // W wave -> chain: -W
+    __shared__ __attribute__((aligned(16))) float uin[kChains][2][kUaccElems];      // W wave -> chain: U
+    __shared__ __attribute__((aligned(16))) f16 hbuf[kOut ? kChains : 1][2][kOut ? kHbElems : 8];  // chain -> output
+    __shared__ __attribute__((aligned(16))) f16 ubuf[kOut ? kChains : 1][2][kOut ? kUbElems : 8];  // chain -> output
     __shared__ __attribute__((aligned(16))) float touch_sink[64];   // target of the L2 touches, never read
 
     const int start = cu[seq];
@@ -436,12 +582,29 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
     const int slot0 = slot_base(cu, seq);
     auto vidx = [&](int c) { return ws.vunit(slot0 + min(c, c_end - 1), h); };
     auto kidx = [&](int c) { return ws.kunit(slot0 + min(c, c_end - 1), j); };
+    const size_t vstride = (size_t)h_v * kDim;                // elements between token rows of v
+    // chunk c's operands; chunks past the last one are clamped to it
+    auto src_of = [&](int c) {
+        const int cc = min(c, c_end - 1);
+        const int t0 = start + kChunk * cc;
+        ChunkSrc s;
+        s.vu = ws.vunit(slot0 + cc, h);
+        s.ku = ws.kunit(slot0 + cc, j);
+        s.vrow = v + (size_t)t0 * vstride + (size_t)h * kDim;
+        s.len = min(kChunk, end - t0);
+        return s;
+    };
+    auto stage_of = [&](int c) -> StateStage<kChains>& { return stage[(c - c_begin) % kStages]; };
     const size_t sbase = ((size_t)seq * h_v + h) * kDim * kDim;
     const size_t gbase = ((size_t)gs * h_v + h) * kDim * kDim;
 
+    // Barriers: P (the first chunk has landed), then B_0 .. B_n for n chunks;
+    // in the interval between B_i and B_{i+1} the chain and the output work on
+    // chunk i, the W wave forms chunk i + 1's -W and U (chunk c_begin's
+    // between P and B_0) and the copy wave fills the stage of chunk i + kAhead.
     if (role < kChains) {
         const int ct = tile_of(role);
-        const bool phi = gtile_of(role) < 8;                 // a map's Phi tile
+        const bool phi = phi_of(role);
         const int col = 16 * ct + ln;
         f32x4 H[8];
         if (kBase == kModeMap) {
@@ -475,25 +638,24 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
         f16x8 hb[4];
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) hb[qq] = cat_to_f16(H[2 * qq], H[2 * qq + 1]);
-        const bool use_u = !(kBase == kModeMap && phi);      // Phi: the homogeneous part
         if (c_end > c_begin) {
             if constexpr (kOut) {
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<f16x8*>(&hbuf[role][0][(qq * 64 + lane) * 8]) = hb[qq];
             }
-            UFrag un = load_u(ws, vidx(c_begin), ct, lane);
-            lds_barrier();                                   // B_0: the first chunk has landed
+            lds_barrier();                                   // P
+            lds_barrier();                                   // B_0
             for (int c = c_begin; c < c_end; ++c) {
-                const UFrag uc = un;
-                un = load_u(ws, vidx(c + 1), ct, lane);       // clamped past the end
+                const int i = c - c_begin;
                 // tile base (column 16 ct); each lane adds its column ln
                 float* snap = kSnap ? chunk_states + ((size_t)(slot0 + c) * h_v + h) * kDim * kDim + 16 * ct
                                     : nullptr;
                 // U'(c) and H0(c + 1) for the output wave; the buffers it
                 // reads in this interval are the other ones
-                chain_chunk<kOut, kSnap>(H, hb, stage[(c - c_begin) % kStages], uc, ubuf[role][(c - c_begin) & 1],
-                                         hbuf[role][(c - c_begin + 1) & 1], snap, use_u, lane, gq, ln);
-                lds_barrier();                               // B_{c+1}
+                chain_chunk<kOut, kSnap>(H, hb, stage_of(c), wbuf[i & 1], uin[role][i & 1],
+                                                  ubuf[kOut ? role : 0][i & 1], hbuf[kOut ? role : 0][(i + 1) & 1],
+                                                  snap, !phi, lane, gq, ln);
+                lds_barrier();                               // B_{i+1}
             }
         }
         if (kBase == kModeMap) {
@@ -509,7 +671,7 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
                 for (int e = 0; e < 4; ++e)
                     s_final[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col] = H[i][e];
         }
-    } else if (role < kCopyRole) {
+    } else if (kOut && role == kOutRole) {
         // the output wave: Q H0 of chunk c between B_c and B_{c+1}, from the
         // state the chain wave handed over before B_c; P U' of chunk c one
         // interval later, from the U' handed over before B_{c+1}.  Q and P
@@ -532,8 +694,9 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
             auto begin_of = [&](int cc, const QFrag& qf) {
 #pragma unroll
                 for (int r = 0; r < kChains; ++r)
-                    out_begin(oacc[r], stage[(cc - c_begin) % kStages], qf, hbuf[r][(cc - c_begin) & 1], lane, ln);
+                    out_begin(oacc[r], stage_of(cc).dg, qf, hbuf[r][(cc - c_begin) & 1], lane, ln);
             };
+            lds_barrier();                                   // P
             lds_barrier();                                   // B_0
             for (int c = c_begin; c < c_end; c += 2) {
                 if (c > c_begin) end_of(c - 1, p1);
@@ -551,28 +714,73 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
             if (((c_end - 1 - c_begin) & 1) == 0) end_of(c_end - 1, p0);
             else end_of(c_end - 1, p1);
         }
+    } else if (role < kCopyRole) {
+        // the W waves: chunk c_begin's -W and U between P and B_0, chunk
+        // c + 1's between B_c and B_{c+1}.  With two W waves the first takes
+        // d_k K-steps 0-1 of -W and row tiles 0-1 of U, the second the rest.
+        if (c_end > c_begin) {
+            const bool first = role == kWRole;
+            lds_barrier();                                   // P
+            for (int c = c_begin; c <= c_end; ++c) {
+                const int i = c - c_begin;
+                if (c < c_end) {
+                    const StateStage<kChains>& st = stage_of(c);
+                    if (kWWaves == 1) {
+                        w_chunk<0, 4>(st, wbuf[i & 1], lane, gq);
+#pragma unroll
+                        for (int r = 0; r < kChains; ++r)
+                            if (!phi_of(r)) u_part<0, 4>(st, r, uin[r][i & 1], lane, gq, ln);
+                    } else if (first) {
+                        w_chunk<0, 2>(st, wbuf[i & 1], lane, gq);
+#pragma unroll
+                        for (int r = 0; r < kChains; ++r)
+                            if (!phi_of(r)) u_part<0, 2>(st, r, uin[r][i & 1], lane, gq, ln);
+                    } else {
+                        w_chunk<2, 4>(st, wbuf[i & 1], lane, gq);
+#pragma unroll
+                        for (int r = 0; r < kChains; ++r)
+                            if (!phi_of(r)) u_part<2, 4>(st, r, uin[r][i & 1], lane, gq, ln);
+                    }
+                }
+                lds_barrier();                               // B_i
+            }
+        }
     } else if (c_end > c_begin) {
-        // copies for chunks past the last one are issued too (clamped, never
-        // used) so the number of copies per chunk never changes
-        constexpr int kCopies = kCopiesPerChunk;
-        state_copy(stage[0], ws, vidx(c_begin), kidx(c_begin), lane);
-        state_copy(stage[1], ws, vidx(c_begin + 1), kidx(c_begin + 1), lane);
-        wait_vmcnt<kCopies>();                               // the first chunk has landed
+        // the copy wave.  Copies for chunks past the last one are issued too
+        // (clamped, never used) so that the number of copies per chunk never
+        // changes.  The touches go out after the copies: loads complete in
+        // issue order, and the copies must not wait behind touches that go
+        // to HBM.
+        int cts[kChains];
+#pragma unroll
+        for (int r = 0; r < kChains; ++r) cts[r] = tile_of(r);
+#pragma unroll
+        for (int a = 0; a < kAhead; ++a) state_copy(stage_of(c_begin + a), ws, src_of(c_begin + a), cts, vstride, lane);
+        // the touches an interval before B_0 would have issued, so that every
+        // wait below counts the same operations after the chunk it waits for
+#pragma unroll
+        for (int r = 0; r < kChains; ++r) {
+            touch_shared(ws, src_of(c_begin + kTouchAhead - 1), cts[r], lane, touch_sink);
+            touch_values(src_of(c_begin + kTouchAhead - 1), cts[r], vstride, lane, touch_sink);
+        }
+        wait_vmcnt<(kAhead - 1) * kCopies + kTouches>();     // chunk c_begin has landed
+        lds_barrier();                                       // P
+        wait_vmcnt<(kAhead - 2) * kCopies + kTouches>();     // chunk c_begin + 1 has landed
         lds_barrier();                                       // B_0
         for (int c = c_begin; c < c_end; ++c) {
-            // between B_c and B_{c+1}: the chain and output waves work on chunk c
-            // the touches go out before the copies for one tile of whole
-            // sequences, after them for segments, maps and tile pairs (whose
-            // four touches would delay the copies): measured
-            constexpr bool kTouchFirst = kMode == kModeWhole || kMode == kModeWholeSnap;
-            if constexpr (kTouchFirst) state_touch(ws, vidx(c + 4), kidx(c + 4), tile_of(0), lane, touch_sink);
-            state_copy(stage[(c - c_begin + 2) % kStages], ws, vidx(c + 2), kidx(c + 2), lane);
-            if constexpr (!kTouchFirst) {
+            // between B_i and B_{i+1}: chunk c + 2 must land for the W waves
+            state_copy(stage_of(c + kAhead), ws, src_of(c + kAhead), cts, vstride, lane);
 #pragma unroll
-                for (int r = 0; r < kChains; ++r) state_touch(ws, vidx(c + 4), kidx(c + 4), tile_of(r), lane, touch_sink);
+            for (int r = 0; r < kChains; ++r) {
+                touch_shared(ws, src_of(c + kTouchAhead), cts[r], lane, touch_sink);
+                touch_values(src_of(c + kTouchAhead), cts[r], vstride, lane, touch_sink);
             }
-            wait_vmcnt<kCopies + kChains * kTouchesPerChunk>();  // chunk c + 1 has landed
-            lds_barrier();                                   // B_{c+1}
+            // outstanding after chunk c + 2's copies: the previous interval's
+            // touches (four ahead) when the copies run three ahead, then this
+            // interval's copies and touches
+            if constexpr (kAhead == 3) wait_vmcnt<2 * kTouches + kCopies>();
+            else wait_vmcnt<kTouches>();
+            lds_barrier();                                   // B_{i+1}
         }
         // drain the copies past the end before the workgroup's LDS goes away
         __builtin_amdgcn_s_waitcnt(0);
@@ -674,7 +882,7 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
         // last-level cache keeps for the state kernel.  Measured crossover
         // between 114 MB (T = 4000: ordinary stores 13 us faster per layer)
         // and 170 MB (T = 6000: streaming 2 us faster; 8-10% from 227 MB on).
-        const size_t inter = (size_t)n_slots * ((size_t)h_v * ((kWElems + kUElems + kPElems) * sizeof(f16) +
+        const size_t inter = (size_t)n_slots * ((size_t)h_v * ((kTuElems + kPElems) * sizeof(f16) +
                                                                kGElems * sizeof(float)) +
                                                 (size_t)h_qk * (kKtElems + kQfElems) * sizeof(f16));
         const hipError_t e = inter > kStreamWorkspaceBytes
@@ -689,16 +897,16 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
             const dim3 grid(state_grid(units, 8));
             if (chunk_states)
                 hipLaunchKernelGGL(gdn_chunk_state<kModeWholeSnap>, grid, dim3(state_threads(kModeWholeSnap)), 0, stream,
-                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+                                   cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
             else if (8 * units > state_cus())
                 // more tiles than CUs: the workgroups run in rounds, and a
                 // pair of tiles sharing one copy ring halves them
                 hipLaunchKernelGGL(gdn_chunk_state<kModeWholePair>, dim3(state_grid(units, 4)),
                                    dim3(state_threads(kModeWholePair)), 0, stream,
-                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+                                   cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
             else
                 hipLaunchKernelGGL(gdn_chunk_state<kModeWhole>, grid, dim3(state_threads(kModeWhole)), 0, stream,
-                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+                                   cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
         } else {
             sa.seg_chunks = seg->seg_chunks;
             sa.n_segslots = seg->n_segslots;
@@ -716,21 +924,21 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
             if (16 * (segs - n_seqs) * h_v > cus)
                 hipLaunchKernelGGL(gdn_chunk_state<kModeMapPair>, dim3(state_grid(units, 8)),
                                    dim3(state_threads(kModeMapPair)), 0, stream,
-                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+                                   cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
             else
                 hipLaunchKernelGGL(gdn_chunk_state<kModeMap>, dim3(state_grid(units, 16)),
                                    dim3(state_threads(kModeMap)), 0, stream,
-                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+                                   cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
             hipLaunchKernelGGL(gdn_chunk_seg_scan, dim3(8 * n_seqs * h_v), dim3(256), 0, stream,
                                cu, n_seqs, h_v, s0, sa);
             if (8 * segs * h_v > cus)
                 hipLaunchKernelGGL(gdn_chunk_state<kModeSegmentPair>, dim3(state_grid(units, 4)),
                                    dim3(state_threads(kModeSegmentPair)), 0, stream,
-                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+                                   cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
             else
                 hipLaunchKernelGGL(gdn_chunk_state<kModeSegment>, dim3(state_grid(units, 8)),
                                    dim3(state_threads(kModeSegment)), 0, stream,
-                                   cu, n_seqs, h_v, s0, s_final, out, chunk_states, ws, sa);
+                                   cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
         }
     }
     return hipGetLastError();

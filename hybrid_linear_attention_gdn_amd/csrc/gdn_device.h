@@ -39,8 +39,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // few large pages per chunk step for the state recurrence, whose 256 or more
 // workgroups walk the chunks in step).
 struct ChunkWorkspace {
-    f16* w;
-    f16* u;
+    f16* tu;
     f16* p;
     float* dg;
     f16* kt;

@@ -2,9 +2,12 @@
 // preparation (the "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page, section 2,
 // first of its three stages).  Per chunk of 64 positions and value head it
 // forms the decay cumsum, A = strictly-lower(beta_r e^{G_r-G_s} K K^T), the UT
-// transform Tm = (I + A)^{-1}, W = Tm diag(beta e^G) K, U = Tm diag(beta) V
-// and P = M o Q K^T, and writes them in the matrix-core fragment order the
-// state kernel reads (the algebra is restated in gdn_chunk.hip).
+// transform Tm = (I + A)^{-1}, TU = Tm diag(beta) and P = M o Q K^T, and
+// writes them, with the fp16 K^T and Q of each q/k head, in the matrix-core
+// fragment order the state kernel reads.  W = TU diag(e^G) K and U = TU V are
+// formed by the state kernel on chip (the algebra is restated in
+// gdn_chunk.hip): 6 KB of TU per chunk and value head instead of 32 KB of W
+// and U through memory, and prep no longer reads V.
 //
 // The kernel is a template over its store kind: ordinary stores, or
 // non-temporal ones for workspaces too large to stay cached until the state
@@ -20,11 +23,9 @@ namespace gdn {
 
 namespace {
 
-constexpr int kTS = 72;   // LDS row stride (halves) of 64-wide fp16 tiles
 // LDS row stride (floats) of the fp32 64 x 64 A / Tm: rows 4 apart (the rows
 // of one accumulator store) fall 16 banks apart
 constexpr int kTA = 68;
-constexpr int kQS = 136;  // LDS row stride (halves) of 128-wide tiles
 
 // Transposed [dim][pos] fp16 tiles, 64 positions per row, no padding.  Rows
 // are written one position per lane, four dims 8 apart at a time, and read as
@@ -146,8 +147,8 @@ __device__ __forceinline__ void store_a(float* Ab, const f32x4 (&av)[4], int gq,
 // Stage 1: intra-chunk preparation.  One workgroup per (chunk slot, value
 // head); 35 KB of LDS and at most 128 registers per lane so that four
 // workgroups share a CU.  The UT transform runs in place in the A buffer: A,
-// then Tm = (I + A)^{-1}, then the fp16 rows of Tm diag(beta e^G) and
-// Tm diag(beta).  kStream: the intermediates go out as non-temporal stores.
+// then Tm = (I + A)^{-1}, read out as the fp16 fragments of Tm diag(beta).
+// kStream: the intermediates go out as non-temporal stores.
 // ---------------------------------------------------------------------------
 template <bool kStream>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void gdn_chunk_prep(
@@ -161,13 +162,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     if (!resolve_slot(cu, n_seqs, slot, seq, t0, len)) return;
     const int j = h / (h_v / h_qk);
 
-    // K^T [dim][pos] (swizzled), then V^T, then Q rows: one buffer, so that
-    // four workgroups (35 KB of LDS each) share a CU
+    // K^T [dim][pos] (swizzled), then Q rows: one buffer, so that four
+    // workgroups (35 KB of LDS each) share a CU
     __shared__ __attribute__((aligned(16))) f16 KsT[kDim * kChunk];
-    __shared__ __attribute__((aligned(16))) float Ab[kChunk * kTS];  // A, then Tm, then TW | TU
+    __shared__ __attribute__((aligned(16))) float Ab[kChunk * kTA];  // K rows (16 KB), then A, then Tm
     __shared__ __attribute__((aligned(16))) float Bs[kChunk];  // beta
-    __shared__ __attribute__((aligned(16))) float Bw[kChunk];  // beta e^G
     __shared__ float Gs[kChunk];     // G
+    __shared__ __attribute__((aligned(16))) float vsink[64];   // target of the value-line touches, never read
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -176,14 +177,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const int ln = lane & 15;
     const size_t wsidx = ws.vunit(slot, h);
 
-    // ---- This wave's row tile of K, Q and V (rows 16 w + ln, dims 32 kk +
-    //      8 gq .. +7), the only global reads of the inputs: K and V go to LDS
-    //      transposed (fp16) for the products over positions; K also goes to
-    //      LDS row-major (bf16, in the A buffer, which is still free) so that
-    //      every wave can read the row tiles its Gram rows need.  Q stays in
-    //      registers.  V is loaded after the UT transform, into the K^T space
-    //      once W has been formed.  Pad rows are zero.
+    // ---- This wave's row tile of K and Q (rows 16 w + ln, dims 32 kk + 8 gq
+    //      .. +7), the only global reads of the inputs: K goes to LDS
+    //      row-major (bf16, in the A buffer, which is still free) so that every
+    //      wave can read the row tiles its Gram rows need, and, for the first
+    //      value head of a q/k head, which writes the K^T fragments,
+    //      transposed (fp16).  Q stays in registers.  Pad rows are zero.
     uint16_t* Kr = reinterpret_cast<uint16_t*>(Ab);   // [pos][dim] bf16, chunk-swizzled
+    // ---- Touch this chunk's value rows of head h (two 128-byte lines per
+    //      row) into the last-level cache with 4-byte direct-to-LDS copies
+    //      into a sink nobody reads, drained at the end: the state kernel
+    //      gathers them on its serial path, where HBM misses stall the
+    //      recurrence (measured: 79 -> 60 us for the recurrence after a cold
+    //      4000-token prep).  Not with streaming stores: a workspace that
+    //      large outgrows the cache before the state kernel gets there.
+    if (!kStream && wave == 3) {
+        const int row = min(lane, len - 1);
+        const uint16_t* vl = v + ((size_t)(t0 + row) * h_v + h) * kDim;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vl), reinterpret_cast<void*>(vsink), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vl + 64), reinterpret_cast<void*>(vsink), 4, 0, 0);
+    }
     bf16x8 kown[4], qf[4];
     {
         const int r = 16 * wave + ln;
@@ -199,9 +212,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             kown[kk] = __builtin_bit_cast(bf16x8, kb);
             qf[kk] = __builtin_bit_cast(bf16x8, qb);
             *reinterpret_cast<u16x8*>(Kr + rsw(r, 4 * kk + gq)) = kb;
-            const f16x8 kt8 = bf16x8_to_f16x8(kb);
+            if (h % ws.group == 0) {
+                const f16x8 kt8 = bf16x8_to_f16x8(kb);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) KsT[tsw(32 * kk + 8 * gq + e, r)] = kt8[e];
+                for (int e = 0; e < 8; ++e) KsT[tsw(32 * kk + 8 * gq + e, r)] = kt8[e];
+            }
         }
     }
     // ---- decay cumsum (wave 0, one lane per position) and the decay vectors
@@ -219,7 +234,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         const float dc = exp_f(gc - x);
         Gs[lane] = x;
         Bs[lane] = bt;
-        Bw[lane] = bt * eg;
         put<kStream>(&ws.dg[wsidx * kGElems + lane], lane == kChunk - 1 ? eg : dc);
         put<kStream>(&ws.dg[wsidx * kGElems + kChunk + lane], eg);
     }
@@ -340,134 +354,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
     __syncthreads();
 
-    // ---- TW = Tm diag(beta e^G), TU = Tm diag(beta) as fp16, in place; blocks
-    //      above the diagonal are zero.
-    f16* TWs = reinterpret_cast<f16*>(Ab);          // [pos][t]
-    f16* TUs = TWs + kChunk * kTS;                  // [pos][t]
+    // ---- TU = Tm diag(beta) as A fragments over positions of its six nonzero
+    //      (row tile, K-step) blocks, in the order of P's: wave w writes row
+    //      tile w.  Entry (r, s) = Tm[r][s] beta_s for s <= r; blocks above the
+    //      diagonal block are zero (the A buffer holds leftovers there), and
+    //      inside a diagonal block the solve left exact zeros above the
+    //      diagonal.  The state kernel forms W = TU diag(e^G) K and U = TU V on
+    //      chip from these 6 KB, the K^T fragments and the value rows.
     {
-        // thread: row r = idx / 16, columns t .. t + 3 (one 16-block)
-        f32x4 tv[4];
+        const int pt = wave;
+        const int r = 16 * pt + ln;
+        f16* tdst = ws.tu + wsidx * kTuElems;
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int idx = tid + 256 * it;
-            const int r = idx >> 4, t = (idx & 15) * 4;
-            tv[it] = ((t >> 4) > (r >> 4)) ? f32x4{0.f, 0.f, 0.f, 0.f}
-                                            : *reinterpret_cast<const f32x4*>(Ab + r * kTA + t);
-        }
-        __syncthreads();
+        for (int qq = 0; qq < 2; ++qq) {
+            if (qq == 1 && pt < 2) continue;          // blocks (0, 1) and (1, 1) are zero
+            const int f = pt < 2 ? pt : 2 + 2 * (pt - 2) + qq;
+            f16x8 fr;
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int idx = tid + 256 * it;
-            const int r = idx >> 4, t = (idx & 15) * 4;
-            const f32x4 bw = *reinterpret_cast<const f32x4*>(Bw + t);
-            const f32x4 bs = *reinterpret_cast<const f32x4*>(Bs + t);
-            f16x4 tw, tu;
+            for (int half = 0; half < 2; ++half) {
+                const int s0 = 32 * qq + 16 * half + 4 * gq;      // slots 4 half .. 4 half + 3
+                const bool live = (s0 >> 4) <= pt;
+                const f32x4 t = live ? *reinterpret_cast<const f32x4*>(Ab + r * kTA + s0) : f32x4{0.f, 0.f, 0.f, 0.f};
+                const f32x4 b = *reinterpret_cast<const f32x4*>(Bs + s0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                tw[e] = static_cast<f16>(tv[it][e] * bw[e]);
-                tu[e] = static_cast<f16>(tv[it][e] * bs[e]);
+                for (int e = 0; e < 4; ++e) fr[4 * half + e] = static_cast<f16>(t[e] * b[e]);
             }
-            *reinterpret_cast<f16x4*>(TWs + r * kTS + t) = tw;
-            *reinterpret_cast<f16x4*>(TUs + r * kTS + t) = tu;
-        }
-    }
-    __syncthreads();
-
-    // ---- W = TW K (positions on lanes), then U = TU V (d_v on lanes), with V^T
-    //      in the K^T space in between.  Wave w owns d_k tiles 2w, 2w+1 and
-    //      d_v tiles 2w, 2w+1.
-    {
-        f32x4 wacc[2][4];   // W^T[d_k tile 2w + a][pos tile p]: positions on lanes
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) wacc[a][p] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            f16x8 kfr[2];
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-                kfr[a] = *reinterpret_cast<const f16x8*>(KsT + tsw(16 * (2 * wave + a) + ln, 32 * kt + 8 * gq));
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const f16x8 tw = *reinterpret_cast<const f16x8*>(TWs + (16 * p + ln) * kTS + 32 * kt + 8 * gq);
-#pragma unroll
-                for (int a = 0; a < 2; ++a) wacc[a][p] = mfma_f16(kfr[a], tw, wacc[a][p]);
-            }
-        }
-        // -W fragments (p, qq = wave): stacked d_k tiles 2w, 2w+1 of W^T
-        f16* wdst = ws.w + wsidx * kWElems;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const f16x8 fr = cat_to_f16(-wacc[0][p], -wacc[1][p]);
-            put<kStream>(reinterpret_cast<f16x8*>(wdst + ((p * 4 + wave) * 64 + lane) * 8), fr);
-        }
-    }
-    // ---- This wave's row tile of V, loaded after W (out of the register peak
-    //      of the W products; the other workgroups on the CU cover the wait)
-    //      and written to LDS once every wave is done with K^T.
-    u16x8 vrow[4];
-    {
-        const int r = 16 * wave + ln;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            vrow[kk] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (r < len) vrow[kk] = *reinterpret_cast<const u16x8*>(v + ((size_t)(t0 + r) * h_v + h) * kDim + 32 * kk + 8 * gq);
-        }
-    }
-    __syncthreads();                                  // every read of K^T is done
-    f16* VsT = KsT;                                   // V^T [dim][pos], swizzled
-    {
-        const int r = 16 * wave + ln;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const f16x8 vt8 = bf16x8_to_f16x8(vrow[kk]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) VsT[tsw(32 * kk + 8 * gq + e, r)] = vt8[e];
-        }
-    }
-    __syncthreads();
-    {
-        f32x4 uacc[4][2];   // U[pos tile p][d_v tile 2w + a]: d_v on lanes
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) uacc[p][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            f16x8 vfr[2];
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-                vfr[a] = *reinterpret_cast<const f16x8*>(VsT + tsw(16 * (2 * wave + a) + ln, 32 * kt + 8 * gq));
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const f16x8 tu = *reinterpret_cast<const f16x8*>(TUs + (16 * p + ln) * kTS + 32 * kt + 8 * gq);
-#pragma unroll
-                for (int a = 0; a < 2; ++a) uacc[p][a] = mfma_f16(tu, vfr[a], uacc[p][a]);
-            }
-        }
-        // U accumulator fragments (ct, p)
-        f16* udst = ws.u + wsidx * kUElems;
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            const int ct = 2 * wave + a;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                f16x4 fr;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) fr[e] = static_cast<f16>(uacc[p][a][e]);
-                put<kStream>(reinterpret_cast<f16x4*>(udst + ((ct * 4 + p) * 64 + lane) * 4), fr);
-            }
+            put<kStream>(reinterpret_cast<f16x8*>(tdst + ((size_t)f * 64 + lane) * 8), fr);
         }
     }
 
     // ---- Q as A fragments over the chunk state's d_k slots, (p, qq = wave),
     //      for the output stage's Q H0; the value heads of a q/k head share
     //      them and the first one writes them.  The rows go through LDS (in
-    //      the K^T / V^T space, free once the products above have read it) because
+    //      the K^T space, free once the fragments above have been read) because
     //      a lane's slots span two 16-dim runs held by different lanes.
     if (h % ws.group == 0) {
-        __syncthreads();                              // every read of V^T is done
+        __syncthreads();                              // every read of K^T is done
         uint16_t* Qr = reinterpret_cast<uint16_t*>(KsT);   // [pos][dim] bf16, chunk-swizzled
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
@@ -490,6 +412,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             put<kStream>(reinterpret_cast<f16x8*>(qdst + ((p * 4 + wave) * 64 + lane) * 8), fr);
         }
     }
+    // drain the value-line touches before the workgroup's LDS goes away
+    if (!kStream && wave == 3) __builtin_amdgcn_s_waitcnt(0);
 }
 
 // Grid width of a prep launch: the chunk slots rounded up to a multiple of 8.

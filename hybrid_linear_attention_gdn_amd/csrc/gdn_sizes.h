@@ -11,10 +11,10 @@ constexpr int kDim = 128;   // d_k = d_v
 
 // Per (chunk slot, value head) element counts of the workspace regions, all
 // in matrix-core fragment order (two bytes per element except kGElems).
-constexpr size_t kWElems = 16 * 64 * 8;    // -W, A fragments [p][qq][lane][8]
-constexpr size_t kUElems = 8 * 4 * 64 * 4;  // U, accumulator fragments [ct][p][lane][4]
-// P = M o (Q K^T), A fragments over positions of its six nonzero (row tile,
-// K-step) blocks (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+// TU = Tm diag(beta), the UT transform's rows scaled by beta, and
+// P = M o (Q K^T): A fragments over positions of their six nonzero (row tile,
+// K-step) blocks (0,0) (1,0) (2,0) (2,1) (3,0) (3,1) (both lower triangular)
+constexpr size_t kTuElems = 6 * 64 * 8;
 constexpr size_t kPElems = 6 * 64 * 8;
 // decay vectors: e^{G_C - G_r} for r < 63 (the factor of row 63 is 1) with
 // e^{G_C} in entry 63, then e^{G_r} for r = 0..63 (fp32)
@@ -24,5 +24,9 @@ constexpr size_t kGElems = 128;
 constexpr size_t kKtElems = 8 * 2 * 64 * 8;
 constexpr size_t kQfElems = 4 * 4 * 64 * 8;
 constexpr size_t kJunkBytes = 1024;         // sink for the lanes of masked-off stores
+
+// -W as A fragments of W H0 [p][qq][lane][8]: formed on chip from K^T and TU
+// (LDS only, not a workspace region)
+constexpr size_t kWElems = 16 * 64 * 8;
 
 }  // namespace gdn

@@ -87,8 +87,7 @@ Layout workspace_layout(const gdn_dims* d, int32_t seg_chunks) {
     const size_t qk_units = (size_t)n_chunk_slots(d) * (size_t)d->n_heads_qk;
     Layout L;
     size_t off = 0;
-    L.w = off;  off += round_up(units * kWElems * kHalf);
-    L.u = off;  off += round_up(units * kUElems * kHalf);
+    L.tu = off; off += round_up(units * kTuElems * kHalf);
     L.p = off;  off += round_up(units * kPElems * kHalf);
     L.dg = off; off += round_up(units * kGElems * sizeof(float));
     L.kt = off; off += round_up(qk_units * kKtElems * kHalf);

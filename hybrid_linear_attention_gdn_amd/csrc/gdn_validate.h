@@ -32,7 +32,7 @@ int64_t n_seg_slots(const gdn_dims* d, int32_t seg_chunks);
 gdn_status check_dims(const gdn_dims* d);
 
 struct Layout {
-    size_t w, u, p, dg, kt, qf, junk, maps, hstart, total;
+    size_t tu, p, dg, kt, qf, junk, maps, hstart, total;
 };
 Layout workspace_layout(const gdn_dims* d, int32_t seg_chunks = 0);
 

@@ -83,10 +83,11 @@ typedef struct {
 /*
  * Workspace bytes gdn_chunk_fwd needs for `dims` (device memory the caller
  * allocates; contents undefined before and after a call).  It holds the
- * intra-chunk products of the chunkwise form (W, U, corrected U', the
- * per-chunk incoming states and the decay cumsums), one 64-token chunk slot
- * per chunk: at most N + T/64 + 1 slots, about 55 KB per slot and value head
- * at two value heads per q/k head.
+ * intra-chunk products of the chunkwise form that the preparation kernel
+ * hands to the recurrence (Tm diag(beta), the output's intra-chunk matrix,
+ * the decay vectors, and fp16 K^T and Q per q/k head), one 64-token chunk
+ * slot per chunk: at most N + T/64 + 1 slots, about 28.5 KB per slot and
+ * value head at two value heads per q/k head.
  */
 gdn_status gdn_chunk_fwd_workspace_size(const gdn_dims* dims, size_t* bytes);
 
@@ -95,9 +96,11 @@ gdn_status gdn_chunk_fwd_workspace_size(const gdn_dims* dims, size_t* bytes);
  * (tokens cu_seqlens[n] .. cu_seqlens[n+1]-1).  Follows the three steps
  * of the "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page, section 2, in two
  * kernels:
- *   gdn_chunk_prep  -- decay cumsum, masked K K^T, (I + A)^{-1}, W and U, and
- *                      the output's intra-chunk matrix P = M o Q K^T;
- *   gdn_chunk_state -- inter-chunk recurrence with the state held in
+ *   gdn_chunk_prep  -- decay cumsum, masked K K^T, Tm = (I + A)^{-1} (stored
+ *                      as Tm diag(beta)), and the output's intra-chunk matrix
+ *                      P = M o Q K^T;
+ *   gdn_chunk_state -- W and U formed on chip from Tm diag(beta), the
+ *                      inter-chunk recurrence with the state held in
  *                      matrix-core accumulators and the next chunks
  *                      prefetched, and the output
  *                      O = diag(e^G) Q S_chunk + P U'.
@@ -299,8 +302,8 @@ gdn_status gdn_recurrent_step_slots(const void* q, const void* k, const void* v,
  * library's device code, one per GPU, held until the process ends; the call
  * itself allocates nothing (no hipMalloc or hipFree, no allocating library
  * routine).  Batches whose gdn_chunk_fwd_workspace_size exceeds it return
- * GDN_ERR_WORKSPACE (128 MiB: up to about 4,700 tokens at 32 value / 16 q-k
- * heads; 4000 tokens use 109 MiB).  The first call on a device looks up the
+ * GDN_ERR_WORKSPACE (128 MiB: up to about 9,100 tokens at 32 value / 16 q-k
+ * heads; 4000 tokens use 57 MiB).  The first call on a device looks up the
  * array's address there.  Every call on one GPU uses that GPU's single copy:
  * calls that overlap on one GPU (two streams, two threads) race and give
  * undefined results; serialise them.  Arguments, results and other errors as

@@ -71,7 +71,7 @@ def test_workspace_size_formula(lib):
     st, b = ws_size(lib, dims(n=1, T=4000, hqk=16, hv=32))
     assert st == 0
     slots = 1 + 4000 // 64 + 1
-    per_v = 8192 * 2 * 2 + 3072 * 2 + 128 * 4   # per value head: -W, U, P (fp16), decay vectors (fp32)
+    per_v = 3072 * 2 * 2 + 128 * 4             # per value head: TU, P (fp16), decay vectors (fp32)
     per_qk = 8192 * 2 * 2                        # per q/k head: K^T, Q (fp16)
     need = slots * (32 * per_v + 16 * per_qk) + 1024  # + the sink of masked-off stores
     assert need <= b < need + 7 * 256
@@ -315,7 +315,7 @@ def test_noalloc_rejects_batches_beyond_its_scratch(lib):
     """The fixed scratch holds GDN_NOALLOC_SCRATCH_BYTES; a batch that needs more
     is refused on the host, before any device call, with the sizes named."""
     import ctypes as ct
-    d = dims(1, 4800, 16, 32)
+    d = dims(1, 9400, 16, 32)
     need = ct.c_size_t(0)
     assert lib.gdn_chunk_fwd_workspace_size(ct.byref(d), ct.byref(need)) == 0
     assert need.value > gdn.GDN_NOALLOC_SCRATCH_BYTES

@@ -7,9 +7,10 @@
 * the intra-chunk preparation checked on its own, kernel by kernel as the
   "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page does in its section on
   precision (each kernel against an fp32-or-better reference): its
-  workspace intermediates (W, U, P = M o Q K^T, the decay vectors, the fp16
-  K^T and Q fragments) decoded from matrix-core fragment order and compared
-  with the chunkwise oracle's, chunk by chunk and head by head.
+  workspace intermediates (TU = Tm diag(beta), P = M o Q K^T, the decay
+  vectors, the fp16 K^T and Q fragments) decoded from matrix-core fragment
+  order and compared with the chunkwise oracle's, chunk by chunk and head by
+  head.
 
 Gates as elsewhere: relative L2 <= 2e-3 on outputs, <= 1e-3 on states.
 """
@@ -200,7 +201,7 @@ def _workspace_regions(n_seqs, T, h_qk, h_v):
     """Byte offsets of the prefill workspace's regions, in the order and
     256-byte rounding the library carves them (region, per-unit elements, item bytes)."""
     slots = n_seqs + T // 64 + 1
-    spec = [("w", h_v, 16 * 64 * 8, 2), ("u", h_v, 8 * 4 * 64 * 4, 2), ("p", h_v, 6 * 64 * 8, 2),
+    spec = [("tu", h_v, 6 * 64 * 8, 2), ("p", h_v, 6 * 64 * 8, 2),
             ("dg", h_v, 128, 4), ("kt", h_qk, 8 * 2 * 64 * 8, 2), ("qf", h_qk, 4 * 4 * 64 * 8, 2)]
     off, regions = 0, {}
     for name, heads, elems, isz in spec:
@@ -237,17 +238,6 @@ def _dec_rowfrag(frag, n_row_tiles, n_ksteps, order):
     return m
 
 
-def _dec_u(frag):
-    """U accumulator fragments [ct][p][lane][4] -> U[16 p + 4 gq + e][16 ct + ln]."""
-    f = frag.reshape(8, 4, 64, 4)
-    u = np.zeros((64, 128))
-    gq, ln, e = np.meshgrid(np.arange(4), np.arange(16), np.arange(4), indexing="ij")
-    for ct in range(8):
-        for p in range(4):
-            u[16 * p + 4 * gq + e, 16 * ct + ln] = f[ct, p][16 * gq + ln, e]
-    return u
-
-
 _P_BLOCKS = {(0, 0): 0, (1, 0): 1, (2, 0): 2, (2, 1): 3, (3, 0): 4, (3, 1): 5}
 
 
@@ -264,8 +254,8 @@ def test_prep_intermediates_against_chunkwise_oracle():
     w_np = ws.cpu().numpy()
     regions = _workspace_regions(x.n_seqs, x.total_tokens, x.h_qk, x.h_v)
     grp = x.h_v // x.h_qk
-    worst = {"W": 0.0, "U": 0.0, "P": 0.0, "dg": 0.0}
-    sq = {k: [0.0, 0.0] for k in ("W", "U", "P")}
+    worst = {"TU": 0.0, "P": 0.0, "dg": 0.0}
+    sq = {k: [0.0, 0.0] for k in ("TU", "P")}
     for s, L in enumerate(lengths):
         a = int(x.cu_seqlens[s])
         for ch in range((L + 63) // 64):
@@ -285,19 +275,23 @@ def test_prep_intermediates_against_chunkwise_oracle():
                 j = h // grp
                 r = chunk_step(x.q[t0:t0 + n, j], x.k[t0:t0 + n, j], x.v[t0:t0 + n, h],
                                x.g[t0:t0 + n, h], x.beta[t0:t0 + n, h], np.zeros((128, 128)))
-                wdec = -_dec_rowfrag(_unit(w_np, regions, "w", slot, h), 4, 4, lambda p, qq: 4 * p + qq)
-                udec = _dec_u(_unit(w_np, regions, "u", slot, h))
+                # TU = Tm diag(beta): what the state kernel forms W = TU diag(e^G) K
+                # and U = TU V from
+                tudec = _dec_rowfrag(_unit(w_np, regions, "tu", slot, h), 4, 2,
+                                     lambda p, qq: _P_BLOCKS.get((p, qq)))
                 pdec = _dec_rowfrag(_unit(w_np, regions, "p", slot, h), 4, 2,
                                     lambda p, qq: _P_BLOCKS.get((p, qq)))
-                for name, dec, ref in (("W", wdec, r["W"]), ("U", udec, r["U"]), ("P", pdec[:, :64], r["P"])):
-                    e = rel_l2(dec[:n, :ref.shape[1]], ref)
+                tu_ref = r["Tm"] * np.asarray(x.beta[t0:t0 + n, h], np.float64)[None, :]
+                for name, dec, ref in (("TU", tudec, tu_ref), ("P", pdec, r["P"])):
+                    e = rel_l2(dec[:n, :n], ref)
                     worst[name] = max(worst[name], e)
-                    sq[name][0] += float(((dec[:n, :ref.shape[1]] - ref) ** 2).sum())
+                    sq[name][0] += float(((dec[:n, :n] - ref) ** 2).sum())
                     sq[name][1] += float((ref ** 2).sum())
                     assert e <= OUT_TOL, (name, s, ch, h, e)
-                    # pad rows of a short chunk are exactly zero
-                    assert not np.any(dec[n:]), (name, s, ch, h)
-                assert not np.any(pdec[:n, n:64]), ("P past the chunk", s, ch, h)
+                    # pad rows and columns of a short chunk, and everything
+                    # above the diagonal, are exactly zero
+                    assert not np.any(dec[n:]) and not np.any(dec[:n, n:]), (name, s, ch, h)
+                    assert not np.any(np.triu(dec, 1)), (name, "upper triangle", s, ch, h)
                 # decay vectors: e^{G_C - G_r} (r < 63; entry 63 = e^{G_C}), then e^{G_r};
                 # pad positions carry G_C (their g reads as 0)
                 dg = _unit(w_np, regions, "dg", slot, h)

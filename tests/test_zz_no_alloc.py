@@ -53,9 +53,9 @@ def test_noalloc_in_place_state_and_rejects_oversized_batches():
     gdn.gdn_chunk_fwd_noalloc(d.q, d.k, d.v, d.g, d.beta, d.cu, s, out, s)
     torch.cuda.synchronize()
     assert torch.equal(out, ref_out) and torch.equal(s, ref_fin)
-    y = gi.make_inputs([4800], 16, 32, 128, 128, seed=1)
+    y = gi.make_inputs([9400], 16, 32, 128, 128, seed=1)
     dy = DevInputs(y)
-    yo = torch.full((4800, 32, 128), 7.0, device="cuda")
+    yo = torch.full((9400, 32, 128), 7.0, device="cuda")
     with pytest.raises(gdn.GDNError) as ei:
         gdn.gdn_chunk_fwd_noalloc(dy.q, dy.k, dy.v, dy.g, dy.beta, dy.cu, None, yo, None)
     assert ei.value.status == gdn.GDN_ERR_WORKSPACE
