@@ -84,14 +84,16 @@ def layer_terms(h_v=H_V, h_qk=H_QK, d=D, c=C):
 def kernel_work():
     """Which layer terms and which layer I/O each prefill kernel evaluates.
 
-    gdn_chunk_prep: the decay, Grams, UT transform, W and U, and the output's
-    intra-chunk matrix; reads q, k, v, g, beta.  gdn_chunk_state: the
-    recurrence and the output; writes the output and the final states."""
+    gdn_chunk_prep: the decay, the Grams K K^T and Q K^T and the UT
+    transform (Tm diag(beta)); reads q, k, g, beta.  gdn_chunk_state: W and U
+    from Tm diag(beta), the recurrence and the output; reads v, writes the
+    output and the final states.  (Prep also pulls v into the last-level
+    cache for the state kernel; that read is not counted twice.)"""
     f, b = layer_terms()
     return {
-        "gdn_chunk_prep": (f["solve"] + f["gram_kk"] + f["gram_qk"] + f["w_u"],
-                           b["q"] + b["k"] + b["v"] + b["g"] + b["beta"]),
-        "gdn_chunk_state": (f["recurrence"] + f["out_qh"] + f["out_pu"], b["out"]),
+        "gdn_chunk_prep": (f["solve"] + f["gram_kk"] + f["gram_qk"],
+                           b["q"] + b["k"] + b["g"] + b["beta"]),
+        "gdn_chunk_state": (f["w_u"] + f["recurrence"] + f["out_qh"] + f["out_pu"], b["v"] + b["out"]),
         "layer": (sum(f.values()), sum(b.values())),
     }
 
@@ -99,7 +101,21 @@ def kernel_work():
 # HBM bytes per launch of the prefill kernels at T = 4000, from rocprofv3
 # FETCH_SIZE / WRITE_SIZE runs of `bench.py --leg prefill` scaled by a plain
 # 1 GiB copy; valid only for the kernel sources they were taken with.
-MEASURED_TRAFFIC = {}
+CSRC = "hybrid_linear_attention_gdn_amd/csrc/"
+MEASURED_TRAFFIC = {
+    # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (KiB per launch, mean over the
+    # warm and cold launches of the counter run)
+    "gdn_chunk_state": {
+        "sources": [CSRC + "gdn_chunk.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
+        "sources_sha256_prefix": "19e0184f184ddf22",
+        "bytes": (44847 * 2 + 66056) * 1024,
+    },
+    "gdn_chunk_prep": {
+        "sources": [CSRC + "gdn_prep.h", CSRC + "gdn_prep.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
+        "sources_sha256_prefix": "5c39beab5282aeac",
+        "bytes": (33428 * 2 + 57456) * 1024,
+    },
+}
 
 
 def measured_traffic(kernel: str):

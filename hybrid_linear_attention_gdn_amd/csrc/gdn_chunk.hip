@@ -182,7 +182,12 @@ __device__ __forceinline__ f16x8 v_frag(const uint16_t* vrows, int qq, int gq, i
 // 4-byte direct-to-LDS copies into a sink nobody reads (one cache line per
 // lane), two per tile: the 352 shared lines of K^T, Q, TU and P split over
 // the 8 column tiles of a head (44 per tile; lanes past 44 repeat a line),
-// and the tile's 64 value-row lines.  A direct copy, unlike a register load,
+// and a quarter of the value-row lines that hold the tile's columns: a
+// 128-byte line of a value row holds the columns of four tiles, so tile ct
+// touches the rows r with r % 4 == ct % 4 (16 lines, four lanes a line) and
+// the four tiles together cover all 64 (measured against each tile touching
+// all 64: recurrence at T = 131072 2.19 -> 2.06 ms, varlen batch 281 -> 273
+// us, T = 4000 unchanged).  A direct copy, unlike a register load,
 // is invisible to the compiler's counter waits, so the copy wave's own
 // single wait still covers it.  (Issued from a W wave, which never waits for
 // its memory counter, the value touches were slower: a touch that waits on
@@ -199,7 +204,8 @@ __device__ __forceinline__ void touch_shared(const ChunkWorkspace& ws, const Chu
 }
 
 __device__ __forceinline__ void touch_values(const ChunkSrc& s, int ct, size_t row_stride, int lane, float* sink) {
-    const uint16_t* vl = s.vrow + (size_t)min(lane, s.len - 1) * row_stride + kVRowElems * ct;
+    const int row = min(4 * (lane >> 2) + (ct & 3), s.len - 1);
+    const uint16_t* vl = s.vrow + (size_t)row * row_stride + kVRowElems * ct;
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vl), reinterpret_cast<void*>(sink), 4, 0, 0);
 }
 
