@@ -7,7 +7,14 @@
 // fragment order the state kernel reads.  W = TU diag(e^G) K and U = TU V are
 // formed by the state kernel on chip (the algebra is restated in
 // gdn_chunk.hip): 6 KB of TU per chunk and value head instead of 32 KB of W
-// and U through memory, and prep no longer reads V.
+// and U through memory.
+//
+// One workgroup serves kH value heads of one q/k head (two when the heads per
+// q/k head are even): they share the chunk's K and Q rows and the raw Grams
+// K K^T and K Q^T, and differ only in beta and the decay.  At 32 value / 16
+// q/k heads that is 1008 workgroups for a 4000-token chunk batch, which four
+// workgroups per CU run in one round, where one workgroup per value head took
+// two, each paying the full latency of its input loads.
 //
 // The kernel is a template over its store kind: ordinary stores, or
 // non-temporal ones for workspaces too large to stay cached until the state
@@ -27,22 +34,38 @@ namespace {
 // of one accumulator store) fall 16 banks apart
 constexpr int kTA = 68;
 
-// Transposed [dim][pos] fp16 tiles, 64 positions per row, no padding.  Rows
-// are written one position per lane, four dims 8 apart at a time, and read as
-// 16-byte runs of 8 positions, 16 consecutive dims at a time.  XOR-ing the
-// position's 8-block index (bits 3-5) with (d & 7) ^ 2 ((d >> 3) & 3) keeps
-// every 8-aligned run contiguous, puts the four written rows on different
-// banks and gives eight consecutive read rows eight different 8-blocks.
-__device__ __forceinline__ int tsw(int d, int t) {
-    return d * kChunk + (t ^ ((((d & 7) ^ (((d >> 3) & 3) << 1)) & 7) << 3));
-}
-
 // Row-major [pos][dim] bf16 tiles, 128 dims per row, no padding: 16-byte
 // chunk c (dims 8 c .. 8 c + 7) of row r sits at chunk c ^ (r % 16), so the
 // 16 rows read at the same dims by a fragment load hit 16 different banks.
 // Returns the element offset of chunk c of row r.
 __device__ __forceinline__ int rsw(int r, int c) {
     return r * kDim + ((c ^ (r & 15)) << 3);
+}
+
+typedef short p16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) p16x4 lds_p16x4;
+
+// K^T as the A fragment (d_k tile i, position step qq) of the state update:
+// lane (gq, ln) holds K[p][16 i + ln] at the position slots p = 32 qq +
+// 16 (s / 4) + 4 gq + s % 4, widened to fp16.  Read from the bf16 K rows in
+// LDS with two transpose reads (ds_read_b64_tr_b16): in each group of 16
+// lanes that instruction hands lane l element l % 4 of the 8-byte granules
+// addressed by lanes l / 4 + 4 e, e = 0..3, so lane l addresses row
+// 32 qq + 16 h + 4 gq + l / 4 at dims 16 i + 4 (l % 4) .. + 3 and receives
+// rows 32 qq + 16 h + 4 gq + e of dim 16 i + l.
+__device__ __forceinline__ f16x8 kt_frag(const uint16_t* Kr, int i, int qq, int gq, int ln) {
+    f16x8 f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = 32 * qq + 16 * h + 4 * gq + (ln >> 2);
+        const int a = 4 * i + (ln & 3);                     // 8-byte granule of the row
+        const p16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_p16x4*)(Kr + rsw(row, a >> 1) + 4 * (a & 1)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            f[4 * h + e] = static_cast<f16>(bf16_to_f32(static_cast<uint16_t>(x[e])));
+    }
+    return f;
 }
 
 // ---------------------------------------------------------------------------
@@ -70,13 +93,42 @@ template <> struct GramBlocks<3> { static constexpr int n = 1, p[4] = {0, 0, 0, 
 __device__ __forceinline__ int diag_row_block(int i) { return i < 3 ? 0 : 1; }
 __device__ __forceinline__ int diag_col_block(int i) { return i < 3 ? 1 + i : 2; }
 
-// The products of wave W: the A values of its Gram blocks into av (A_rs for
-// rows r = 16 p + 4 gq + e, column s = 16 jt + ln; 0 for s >= r), and P's
-// row tile W, stored to pdst.  K row tiles come from Kr (row-major bf16,
+// One head's A values of a Gram block: A_rs for rows r = 16 p + 4 gq + e,
+// column s = 16 jt + ln (0 for s >= r), from the raw K K^T accumulator.
+__device__ __forceinline__ f32x4 a_values(const f32x4& acc, const float* Gs, const float* Bs, int p, int jt, int gq,
+                                          int ln) {
+    const int s = 16 * jt + ln;
+    const float gsv = Gs[s];
+    f32x4 av;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = 16 * p + 4 * gq + e;
+        av[e] = (s < r) ? Bs[r] * exp_f(Gs[r] - gsv) * acc[e] : 0.f;
+    }
+    return av;
+}
+
+// Store a block of A values into an A buffer (row stride kTA); a diagonal
+// block goes transposed to its place above the diagonal.
+__device__ __forceinline__ void put_a(float* Ab, const f32x4& av, int p, int jt, int gq, int ln) {
+    if (jt < p) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Ab[(16 * p + 4 * gq + e) * kTA + 16 * jt + ln] = av[e];
+    } else {
+        *reinterpret_cast<f32x4*>(Ab + (16 * diag_row_block(p) + ln) * kTA + 16 * diag_col_block(p) + 4 * gq) = av;
+    }
+}
+
+// The products of wave W for kH value heads: the raw Gram blocks once, with
+// each head's A values of them (head 0's into av, to be stored once every
+// wave has read its K tiles from head 0's A buffer; the other heads' straight
+// into their own, still unused, A buffers), and P's row tile W per head,
+// stored to pdst[hh].  K row tiles come from Kr (row-major bf16,
 // chunk-swizzled), the wave's own from kown.
-template <int W, bool kStream>
+template <int W, bool kStream, int kH>
 __device__ __forceinline__ void prep_products(f32x4 (&av)[4], const bf16x8 (&kown)[4], const bf16x8 (&qf)[4],
-                                              const uint16_t* Kr, const float* Gs, const float* Bs, f16* pdst,
+                                              const uint16_t* Kr, float* const (&Ab)[kH], const float* const (&Gs)[kH],
+                                              const float* const (&Bs)[kH], f16* const (&pdst)[kH],
                                               int lane, int gq, int ln) {
     bf16x8 kt[4][4];
 #pragma unroll
@@ -92,13 +144,9 @@ __device__ __forceinline__ void prep_products(f32x4 (&av)[4], const bf16x8 (&kow
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};   // exact bf16 inputs
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(kt[p][kk], kt[jt][kk], acc);
-        const int s = 16 * jt + ln;
-        const float gsv = Gs[s];
+        av[i] = a_values(acc, Gs[0], Bs[0], p, jt, gq, ln);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * p + 4 * gq + e;
-            av[i][e] = (s < r) ? Bs[r] * exp_f(Gs[r] - gsv) * acc[e] : 0.f;
-        }
+        for (int hh = 1; hh < kH; ++hh) put_a(Ab[hh], a_values(acc, Gs[hh], Bs[hh], p, jt, gq, ln), p, jt, gq, ln);
     }
     // P = M o (Q K^T) for row tile W, M_rs = e^{G_r - G_s} (s <= r), computed
     // as (K Q^T)[s][r] so that the accumulators of two position tiles stack
@@ -106,7 +154,6 @@ __device__ __forceinline__ void prep_products(f32x4 (&av)[4], const bf16x8 (&kow
     // stage reads it: block (p, qq) at 2 p (p < 2) or 2 + 2 (p - 2) + qq;
     // blocks (0, 1) and (1, 1) are zero and not stored.
     const int r = 16 * W + ln;
-    const float gr = Gs[r];
     f32x4 dt[4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
@@ -114,60 +161,93 @@ __device__ __forceinline__ void prep_products(f32x4 (&av)[4], const bf16x8 (&kow
         if (jt > W) continue;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) dt[jt] = mfma_bf16(kt[jt][kk], qf[kk], dt[jt]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int sp = 16 * jt + 4 * gq + e;
-            dt[jt][e] = (sp <= r) ? exp_f(gr - Gs[sp]) * dt[jt][e] : 0.f;
-        }
     }
     constexpr int f0 = W < 2 ? W : 2 * W - 2;
-    put<kStream>(reinterpret_cast<f16x8*>(pdst + ((size_t)f0 * 64 + lane) * 8), cat_to_f16(dt[0], dt[1]));
-    if constexpr (W >= 2)
-        put<kStream>(reinterpret_cast<f16x8*>(pdst + ((size_t)(f0 + 1) * 64 + lane) * 8), cat_to_f16(dt[2], dt[3]));
+#pragma unroll
+    for (int hh = 0; hh < kH; ++hh) {
+        const float gr = Gs[hh][r];
+        f32x4 m[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int sp = 16 * jt + 4 * gq + e;
+                m[jt][e] = (jt <= W && sp <= r) ? exp_f(gr - Gs[hh][sp]) * dt[jt][e] : 0.f;
+            }
+        put<kStream>(reinterpret_cast<f16x8*>(pdst[hh] + ((size_t)f0 * 64 + lane) * 8), cat_to_f16(m[0], m[1]));
+        if constexpr (W >= 2)
+            put<kStream>(reinterpret_cast<f16x8*>(pdst[hh] + ((size_t)(f0 + 1) * 64 + lane) * 8), cat_to_f16(m[2], m[3]));
+    }
 }
 
-// A values of wave W's Gram blocks into the A buffer (row stride kTA); a
-// diagonal block goes transposed to its place above the diagonal.
+// Head 0's A values of wave W's Gram blocks into its A buffer.
 template <int W>
 __device__ __forceinline__ void store_a(float* Ab, const f32x4 (&av)[4], int gq, int ln) {
     using B = GramBlocks<W>;
 #pragma unroll
-    for (int i = 0; i < B::n; ++i) {
-        const int p = B::p[i], jt = B::jt[i];
-        if (jt < p) {
+    for (int i = 0; i < B::n; ++i) put_a(Ab, av[i], B::p[i], B::jt[i], gq, ln);
+}
+
+// Tm_ii = (I + A_ii)^{-1} of diagonal block i of one head, in place in its A
+// buffer.  N = A_ii is strictly lower, so N^16 = 0 and (I + N)^{-1} =
+// sum_p (-N)^p = (I - N)(I + N^2)(I + N^4)(I + N^8): eight 16x16x16 products
+// in six dependent steps.  A product's accumulator Xc (lane (gq, ln) holds
+// X[4 gq + e][ln]) is X's B operand and X^T's A operand, so a power is also
+// formed transposed where the next product needs it as an A operand.  Split
+// fp16 operands (~2^-22 relative per product); for |N_rs| <= 1 every power
+// and partial product stays below 2^14, inside fp16 range.
+__device__ __forceinline__ void diag_inverse(float* Ab, int ib, int gq, int ln) {
+    const float* at = Ab + 16 * diag_row_block(ib) * kTA + 16 * diag_col_block(ib);   // at[t * kTA + r] = A_ii[r][t]
+    const f32x4 nb = *reinterpret_cast<const f32x4*>(at + ln * kTA + 4 * gq);           // N[4 gq + e][ln]
+    f32x4 na;                                                                           // N[ln][4 gq + e]
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Ab[(16 * p + 4 * gq + e) * kTA + 16 * jt + ln] = av[i][e];
-        } else {
-            *reinterpret_cast<f32x4*>(Ab + (16 * diag_row_block(p) + ln) * kTA + 16 * diag_col_block(p) + 4 * gq) = av[i];
-        }
-    }
+    for (int e = 0; e < 4; ++e) na[e] = at[(4 * gq + e) * kTA + ln];
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const Split16 sna = split16(na), snb = split16(nb);
+    const f32x4 n2 = mfma_split16(sna, snb, z);            // N^2
+    const f32x4 n2t = mfma_split16(snb, sna, z);           // (N^2)^T
+    const Split16 s2 = split16(n2), s2t = split16(n2t);
+    const f32x4 n4 = mfma_split16(s2t, s2, z);             // N^4
+    const f32x4 n4t = mfma_split16(s2, s2t, z);            // (N^4)^T
+    const Split16 s4t = split16(n4t);
+    const f32x4 n8 = mfma_split16(s4t, split16(n4), z);     // N^8
+    f32x4 acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = (4 * gq + e == ln ? 1.f : 0.f) + n4[e] + n8[e];
+    acc = mfma_split16(s4t, split16(n8), acc);             // (I + N^4)(I + N^8)
+    acc = mfma_split16(s2t, split16(acc), acc);            // (I + N^2)(I + N^4)(I + N^8)
+    const f32x4 t = mfma_split16(split16(-na), split16(acc), acc);   // (I - N)(...)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Ab[(16 * ib + 4 * gq + e) * kTA + 16 * ib + ln] = t[e];
 }
 
 // ---------------------------------------------------------------------------
-// Stage 1: intra-chunk preparation.  One workgroup per (chunk slot, value
-// head); 35 KB of LDS and at most 128 registers per lane so that four
-// workgroups share a CU.  The UT transform runs in place in the A buffer: A,
-// then Tm = (I + A)^{-1}, read out as the fp16 fragments of Tm diag(beta).
+// Stage 1: intra-chunk preparation.  One workgroup per (chunk slot, group of
+// kH value heads of one q/k head); 36 KB of LDS at kH = 2 (18 KB at kH = 1)
+// and at most 128 registers per lane so that four workgroups share a CU.
+// The UT transform of each head runs in place in its A buffer: A, then
+// Tm = (I + A)^{-1}, read out as the fp16 fragments of Tm diag(beta).
 // kStream: the intermediates go out as non-temporal stores.
 // ---------------------------------------------------------------------------
-template <bool kStream>
+template <bool kStream, int kH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void gdn_chunk_prep(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, int n_seqs, int h_qk, int h_v, ChunkWorkspace ws)
 {
+    static_assert(kH == 1 || kH == 2, "one or two value heads per workgroup");
     const int slot = blockIdx.x;
-    const int h = blockIdx.y;
+    const int h0 = kH * blockIdx.y;                   // the workgroup's first value head
     int seq, t0, len;
     if (!resolve_slot(cu, n_seqs, slot, seq, t0, len)) return;
-    const int j = h / (h_v / h_qk);
+    const int j = h0 / ws.group;
+    const bool first = h0 % ws.group == 0;            // holds the q/k head's first value head
 
-    // K^T [dim][pos] (swizzled), then Q rows: one buffer, so that four
-    // workgroups (35 KB of LDS each) share a CU
-    __shared__ __attribute__((aligned(16))) f16 KsT[kDim * kChunk];
-    __shared__ __attribute__((aligned(16))) float Ab[kChunk * kTA];  // K rows (16 KB), then A, then Tm
-    __shared__ __attribute__((aligned(16))) float Bs[kChunk];  // beta
-    __shared__ float Gs[kChunk];     // G
+    // Per head: A buffer (K rows (16 KB bf16) in head 0's until the products
+    // have read them, then A, then Tm; Q rows at the end), beta and G.
+    __shared__ __attribute__((aligned(16))) float Abuf[kH][kChunk * kTA];
+    __shared__ __attribute__((aligned(16))) float Bsh[kH][kChunk];
+    __shared__ float Gsh[kH][kChunk];
     __shared__ __attribute__((aligned(16))) float vsink[64];   // target of the value-line touches, never read
 
     const int tid = threadIdx.x;
@@ -175,28 +255,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int gq = lane >> 4;
     const int ln = lane & 15;
-    const size_t wsidx = ws.vunit(slot, h);
+    float* Ab[kH];
+    const float* Gs[kH];
+    const float* Bs[kH];
+    f16* pdst[kH];
+#pragma unroll
+    for (int hh = 0; hh < kH; ++hh) {
+        Ab[hh] = Abuf[hh];
+        Gs[hh] = Gsh[hh];
+        Bs[hh] = Bsh[hh];
+        pdst[hh] = ws.p + ws.vunit(slot, h0 + hh) * kPElems;
+    }
+
+    // ---- The decay inputs (wave hh for head hh, one lane per position),
+    //      loaded first so that their latency hides under the K and Q loads.
+    float g_in = 0.f, b_in = 0.f;
+    if (wave < kH && lane < len) {
+        g_in = g[(size_t)(t0 + lane) * h_v + h0 + wave];
+        b_in = beta[(size_t)(t0 + lane) * h_v + h0 + wave];
+    }
 
     // ---- This wave's row tile of K and Q (rows 16 w + ln, dims 32 kk + 8 gq
     //      .. +7), the only global reads of the inputs: K goes to LDS
-    //      row-major (bf16, in the A buffer, which is still free) so that every
-    //      wave can read the row tiles its Gram rows need, and, for the first
-    //      value head of a q/k head, which writes the K^T fragments,
-    //      transposed (fp16).  Q stays in registers.  Pad rows are zero.
-    uint16_t* Kr = reinterpret_cast<uint16_t*>(Ab);   // [pos][dim] bf16, chunk-swizzled
-    // ---- Touch this chunk's value rows of head h (two 128-byte lines per
-    //      row) into the last-level cache with 4-byte direct-to-LDS copies
-    //      into a sink nobody reads, drained at the end: the state kernel
-    //      gathers them on its serial path, where HBM misses stall the
-    //      recurrence (measured: 79 -> 60 us for the recurrence after a cold
-    //      4000-token prep).  Not with streaming stores: a workspace that
-    //      large outgrows the cache before the state kernel gets there.
-    if (!kStream && wave == 3) {
-        const int row = min(lane, len - 1);
-        const uint16_t* vl = v + ((size_t)(t0 + row) * h_v + h) * kDim;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vl), reinterpret_cast<void*>(vsink), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vl + 64), reinterpret_cast<void*>(vsink), 4, 0, 0);
-    }
+    //      row-major (bf16, in head 0's A buffer, which is still free) so
+    //      that every wave can read the row tiles its Gram rows need and the
+    //      K^T fragments can be read from it transposed.  Q stays in
+    //      registers.  Pad rows are zero.
+    uint16_t* Kr = reinterpret_cast<uint16_t*>(Abuf[0]);   // [pos][dim] bf16, chunk-swizzled
     bf16x8 kown[4], qf[4];
     {
         const int r = 16 * wave + ln;
@@ -212,18 +297,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             kown[kk] = __builtin_bit_cast(bf16x8, kb);
             qf[kk] = __builtin_bit_cast(bf16x8, qb);
             *reinterpret_cast<u16x8*>(Kr + rsw(r, 4 * kk + gq)) = kb;
-            if (h % ws.group == 0) {
-                const f16x8 kt8 = bf16x8_to_f16x8(kb);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) KsT[tsw(32 * kk + 8 * gq + e, r)] = kt8[e];
-            }
         }
     }
-    // ---- decay cumsum (wave 0, one lane per position) and the decay vectors
-    if (wave == 0) {
-        const bool in = lane < len;
-        float x = in ? g[(size_t)(t0 + lane) * h_v + h] : 0.f;
-        const float bt = in ? beta[(size_t)(t0 + lane) * h_v + h] : 0.f;
+    // ---- Touch this chunk's value rows of the workgroup's heads (two
+    //      128-byte lines per row and head) into the last-level cache with
+    //      4-byte direct-to-LDS copies into a sink nobody reads, drained at
+    //      the end: the state kernel gathers them on its serial path, where
+    //      HBM misses stall the recurrence (measured: 79 -> 60 us for the
+    //      recurrence after a cold 4000-token prep).  Issued after the K and
+    //      Q loads, which return first.  Not with streaming stores: a
+    //      workspace that large outgrows the cache before the state kernel
+    //      gets there.
+    if (!kStream && wave == 3) {
+        const int row = min(lane, len - 1);
+#pragma unroll
+        for (int hh = 0; hh < kH; ++hh) {
+            const uint16_t* vl = v + ((size_t)(t0 + row) * h_v + h0 + hh) * kDim;
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vl), reinterpret_cast<void*>(vsink), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vl + 64), reinterpret_cast<void*>(vsink), 4, 0, 0);
+        }
+    }
+    // ---- decay cumsum (wave hh for head hh, one lane per position) and the
+    //      decay vectors
+    if (wave < kH) {
+        float x = g_in;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(x, off, 64);
@@ -232,78 +329,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         const float gc = __shfl(x, kChunk - 1, 64);
         const float eg = exp_f(x);
         const float dc = exp_f(gc - x);
-        Gs[lane] = x;
-        Bs[lane] = bt;
-        put<kStream>(&ws.dg[wsidx * kGElems + lane], lane == kChunk - 1 ? eg : dc);
-        put<kStream>(&ws.dg[wsidx * kGElems + kChunk + lane], eg);
+        Gsh[wave][lane] = x;
+        Bsh[wave][lane] = b_in;
+        float* dg = ws.dg + ws.vunit(slot, h0 + wave) * kGElems;
+        put<kStream>(&dg[lane], lane == kChunk - 1 ? eg : dc);
+        put<kStream>(&dg[kChunk + lane], eg);
     }
     __syncthreads();
 
     // ---- K^T as A-operand fragments of the state update (which applies the
-    //      decay e^{G_C - G} to U' instead): fragment (i, qq), lane (gq, ln) =
-    //      K[p][16 i + ln] at the position slots p(gq, s) of K-step qq.  The
-    //      value heads of a q/k head share it; the first one writes it.
-    if (h % ws.group == 0) {
+    //      decay e^{G_C - G} to U' instead): fragment (i, qq) = 2 i + qq, read
+    //      transposed from the K rows.  The value heads of a q/k head share
+    //      it; the workgroup with the first one writes it.
+    if (first) {
         f16* kdst = ws.kt + ws.kunit(slot, j) * kKtElems;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int f = wave + 4 * it;          // fragment index i * 2 + qq
-            const int i = f >> 1, qq = f & 1;
-            const int d = 16 * i + ln;
-            const f16x4 lo = *reinterpret_cast<const f16x4*>(KsT + tsw(d, 32 * qq + 4 * gq));
-            const f16x4 hi = *reinterpret_cast<const f16x4*>(KsT + tsw(d, 32 * qq + 16 + 4 * gq));
-            const f16x8 fr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            put<kStream>(reinterpret_cast<f16x8*>(kdst + ((size_t)f * 64 + lane) * 8), fr);
+            const int f = wave + 4 * it;
+            put<kStream>(reinterpret_cast<f16x8*>(kdst + ((size_t)f * 64 + lane) * 8), kt_frag(Kr, f >> 1, f & 1, gq, ln));
         }
     }
 
     // ---- The Gram blocks of A = strictly lower (beta_r e^{G_r-G_s} K K^T) and
     //      P's row tile, balanced over the waves (prep_products); then, once
-    //      every wave has read its K tiles from the A buffer, A into it.
+    //      every wave has read its K tiles from head 0's A buffer, head 0's A
+    //      into it.
     f32x4 av[4];
     switch (wave) {
-        case 0: prep_products<0, kStream>(av, kown, qf, Kr, Gs, Bs, ws.p + wsidx * kPElems, lane, gq, ln); break;
-        case 1: prep_products<1, kStream>(av, kown, qf, Kr, Gs, Bs, ws.p + wsidx * kPElems, lane, gq, ln); break;
-        case 2: prep_products<2, kStream>(av, kown, qf, Kr, Gs, Bs, ws.p + wsidx * kPElems, lane, gq, ln); break;
-        default: prep_products<3, kStream>(av, kown, qf, Kr, Gs, Bs, ws.p + wsidx * kPElems, lane, gq, ln); break;
+        case 0: prep_products<0, kStream, kH>(av, kown, qf, Kr, Ab, Gs, Bs, pdst, lane, gq, ln); break;
+        case 1: prep_products<1, kStream, kH>(av, kown, qf, Kr, Ab, Gs, Bs, pdst, lane, gq, ln); break;
+        case 2: prep_products<2, kStream, kH>(av, kown, qf, Kr, Ab, Gs, Bs, pdst, lane, gq, ln); break;
+        default: prep_products<3, kStream, kH>(av, kown, qf, Kr, Ab, Gs, Bs, pdst, lane, gq, ln); break;
     }
-    __syncthreads();                                  // K rows in the A buffer are consumed
+    __syncthreads();                                  // K rows in head 0's A buffer are consumed
     switch (wave) {
-        case 0: store_a<0>(Ab, av, gq, ln); break;
-        case 1: store_a<1>(Ab, av, gq, ln); break;
-        case 2: store_a<2>(Ab, av, gq, ln); break;
-        default: store_a<3>(Ab, av, gq, ln); break;
+        case 0: store_a<0>(Ab[0], av, gq, ln); break;
+        case 1: store_a<1>(Ab[0], av, gq, ln); break;
+        case 2: store_a<2>(Ab[0], av, gq, ln); break;
+        default: store_a<3>(Ab[0], av, gq, ln); break;
     }
     __syncthreads();
 
-    // ---- Tm = (I + A)^{-1}, blocked by 16, in place.
-    //  (1) Diagonal blocks Tm_ii = (I + A_ii)^{-1}: wave i, lane c % 16 holds
-    //      column c of x = (I + A_ii)^{-1} e_c.  Forward substitution by
-    //      columns of A_ii: once x_t is final, x_r -= A_rt x_t for r > t (each
-    //      x_r sees the same subtractions in the same order as the row form).
-    {
-        const int ib = wave;
-        const float* at = Ab + 16 * diag_row_block(ib) * kTA + 16 * diag_col_block(ib);   // at[t * kTA + r] = A_ii[r][t]
-        float x[16];
+    // ---- Tm = (I + A)^{-1}, blocked by 16, in place, per head.
+    //  (1) Diagonal blocks: block i on wave i.
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
-#pragma unroll
-        for (int t = 0; t < 15; ++t) {
-            float col[16];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 c4 = *reinterpret_cast<const f32x4*>(at + t * kTA + 4 * q4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) col[4 * q4 + e] = c4[e];
-            }
-#pragma unroll
-            for (int r = t + 1; r < 16; ++r) x[r] -= col[r] * x[t];
-        }
-        if (gq == 0) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Ab[(16 * ib + r) * kTA + 16 * ib + ln] = x[r];
-        }
-    }
+    for (int hh = 0; hh < kH; ++hh) diag_inverse(Ab[hh], wave, gq, ln);
     __syncthreads();
     //  (2) Below the diagonal, block column j on wave j, rows i = j+1..3:
     //      Tm_ij = -Tm_ii sum_{k=j}^{i-1} A_ik Tm_kj, with 16x16x16 products on
@@ -311,45 +381,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     //      accumulator is already the B operand of the next one, so the column
     //      chain stays in registers.  Every A_ik a wave needs is read before
     //      any wave overwrites A blocks with Tm blocks.
-    Split16 tcol[4];   // Tm_{k, jb} in accumulator (= B operand) layout, k >= jb
-    f32x4 aik[4][4];   // A_ik, A-operand layout
-    f32x4 tii[4];      // Tm_ii, A-operand layout
     const int jb = wave;
-    if (wave < 3) {
 #pragma unroll
-        for (int kb = 0; kb < 3; ++kb) {
-            if (kb != jb) continue;
-            f32x4 t;
+    for (int hh = 0; hh < kH; ++hh) {
+        Split16 tcol[4];   // Tm_{k, jb} in accumulator (= B operand) layout, k >= jb
+        f32x4 aik[4][4];   // A_ik, A-operand layout
+        f32x4 tii[4];      // Tm_ii, A-operand layout
+        float* A = Ab[hh];
+        if (wave < 3) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) t[e] = Ab[(16 * kb + 4 * gq + e) * kTA + 16 * kb + ln];
-            tcol[kb] = split16(t);
-        }
+            for (int kb = 0; kb < 3; ++kb) {
+                if (kb != jb) continue;
+                f32x4 t;
 #pragma unroll
-        for (int i2 = 1; i2 < 4; ++i2) {
-            if (i2 <= jb) continue;
-            tii[i2] = *reinterpret_cast<const f32x4*>(Ab + (16 * i2 + ln) * kTA + 16 * i2 + 4 * gq);
+                for (int e = 0; e < 4; ++e) t[e] = A[(16 * kb + 4 * gq + e) * kTA + 16 * kb + ln];
+                tcol[kb] = split16(t);
+            }
 #pragma unroll
-            for (int kb = 0; kb < i2; ++kb) {
-                if (kb < jb) continue;
-                aik[i2][kb] = *reinterpret_cast<const f32x4*>(Ab + (16 * i2 + ln) * kTA + 16 * kb + 4 * gq);
+            for (int i2 = 1; i2 < 4; ++i2) {
+                if (i2 <= jb) continue;
+                tii[i2] = *reinterpret_cast<const f32x4*>(A + (16 * i2 + ln) * kTA + 16 * i2 + 4 * gq);
+#pragma unroll
+                for (int kb = 0; kb < i2; ++kb) {
+                    if (kb < jb) continue;
+                    aik[i2][kb] = *reinterpret_cast<const f32x4*>(A + (16 * i2 + ln) * kTA + 16 * kb + 4 * gq);
+                }
             }
         }
-    }
-    __syncthreads();
-    if (wave < 3) {
+        __syncthreads();
+        if (wave < 3) {
 #pragma unroll
-        for (int i2 = 1; i2 < 4; ++i2) {
-            if (i2 <= jb) continue;
-            f32x4 xs = {0.f, 0.f, 0.f, 0.f};
+            for (int i2 = 1; i2 < 4; ++i2) {
+                if (i2 <= jb) continue;
+                f32x4 xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < i2; ++kb) {
-                if (kb < jb) continue;
-                xs = mfma_split16(split16(aik[i2][kb]), tcol[kb], xs);
+                for (int kb = 0; kb < i2; ++kb) {
+                    if (kb < jb) continue;
+                    xs = mfma_split16(split16(aik[i2][kb]), tcol[kb], xs);
+                }
+                const f32x4 y = mfma_split16(split16(tii[i2]), split16(xs), f32x4{0.f, 0.f, 0.f, 0.f});
+                tcol[i2] = split16(-y);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) A[(16 * i2 + 4 * gq + e) * kTA + 16 * jb + ln] = -y[e];
             }
-            const f32x4 y = mfma_split16(split16(tii[i2]), split16(xs), f32x4{0.f, 0.f, 0.f, 0.f});
-            tcol[i2] = split16(-y);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Ab[(16 * i2 + 4 * gq + e) * kTA + 16 * jb + ln] = -y[e];
         }
     }
     __syncthreads();
@@ -358,13 +432,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     //      (row tile, K-step) blocks, in the order of P's: wave w writes row
     //      tile w.  Entry (r, s) = Tm[r][s] beta_s for s <= r; blocks above the
     //      diagonal block are zero (the A buffer holds leftovers there), and
-    //      inside a diagonal block the solve left exact zeros above the
-    //      diagonal.  The state kernel forms W = TU diag(e^G) K and U = TU V on
-    //      chip from these 6 KB, the K^T fragments and the value rows.
-    {
+    //      inside a diagonal block the inverse is exactly lower triangular
+    //      (every power of a strictly lower N is strictly lower).  The state
+    //      kernel forms W = TU diag(e^G) K and U = TU V on chip from these
+    //      6 KB, the K^T fragments and the value rows.
+#pragma unroll
+    for (int hh = 0; hh < kH; ++hh) {
         const int pt = wave;
         const int r = 16 * pt + ln;
-        f16* tdst = ws.tu + wsidx * kTuElems;
+        f16* tdst = ws.tu + ws.vunit(slot, h0 + hh) * kTuElems;
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
             if (qq == 1 && pt < 2) continue;          // blocks (0, 1) and (1, 1) are zero
@@ -374,8 +450,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             for (int half = 0; half < 2; ++half) {
                 const int s0 = 32 * qq + 16 * half + 4 * gq;      // slots 4 half .. 4 half + 3
                 const bool live = (s0 >> 4) <= pt;
-                const f32x4 t = live ? *reinterpret_cast<const f32x4*>(Ab + r * kTA + s0) : f32x4{0.f, 0.f, 0.f, 0.f};
-                const f32x4 b = *reinterpret_cast<const f32x4*>(Bs + s0);
+                const f32x4 t = live ? *reinterpret_cast<const f32x4*>(Ab[hh] + r * kTA + s0) : f32x4{0.f, 0.f, 0.f, 0.f};
+                const f32x4 b = *reinterpret_cast<const f32x4*>(Bs[hh] + s0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) fr[4 * half + e] = static_cast<f16>(t[e] * b[e]);
             }
@@ -385,12 +461,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
     // ---- Q as A fragments over the chunk state's d_k slots, (p, qq = wave),
     //      for the output stage's Q H0; the value heads of a q/k head share
-    //      them and the first one writes them.  The rows go through LDS (in
-    //      the K^T space, free once the fragments above have been read) because
-    //      a lane's slots span two 16-dim runs held by different lanes.
-    if (h % ws.group == 0) {
-        __syncthreads();                              // every read of K^T is done
-        uint16_t* Qr = reinterpret_cast<uint16_t*>(KsT);   // [pos][dim] bf16, chunk-swizzled
+    //      them and the workgroup with the first one writes them.  The rows
+    //      go through LDS (head 0's A buffer, free once TU has been read out
+    //      of it) because a lane's slots span two 16-dim runs held by
+    //      different lanes.
+    if (first) {
+        __syncthreads();                              // every read of head 0's Tm is done
+        uint16_t* Qr = reinterpret_cast<uint16_t*>(Abuf[0]);   // [pos][dim] bf16, chunk-swizzled
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
             *reinterpret_cast<u16x8*>(Qr + rsw(16 * wave + ln, 4 * kk + gq)) = __builtin_bit_cast(u16x8, qf[kk]);
@@ -417,12 +494,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 }
 
 // Grid width of a prep launch: the chunk slots rounded up to a multiple of 8.
-// Workgroup (slot, h) has the linear index slot + width * h and runs on XCD
+// Workgroup (slot, y) has the linear index slot + width * y and runs on XCD
 // index % 8, so with the width a multiple of 8 every value head of a chunk
 // slot runs on the same XCD, and the value heads of a q/k head, which read
 // the same q and k rows, share that XCD's L2.  The padding workgroups find
 // no chunk and leave at once.
 __host__ __forceinline__ unsigned slots_x8(int n_slots) { return ((unsigned)n_slots + 7u) & ~7u; }
+
+// Value heads per prep workgroup: two when the value heads of a q/k head
+// pair up (an even number of them), else one.
+__host__ __forceinline__ int prep_heads(int h_qk, int h_v) { return (h_v / h_qk) % 2 == 0 ? 2 : 1; }
 
 }  // namespace
 

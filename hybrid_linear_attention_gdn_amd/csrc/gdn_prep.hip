@@ -10,8 +10,12 @@ hipError_t launch_prep(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        const int32_t* cu, int n_seqs, int h_qk, int h_v, const ChunkWorkspace& ws, int n_slots,
                        hipStream_t stream)
 {
-    hipLaunchKernelGGL(gdn_chunk_prep<false>, dim3(slots_x8(n_slots), h_v), dim3(256), 0, stream,
-                       q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws);
+    if (prep_heads(h_qk, h_v) == 2)
+        hipLaunchKernelGGL((gdn_chunk_prep<false, 2>), dim3(slots_x8(n_slots), h_v / 2), dim3(256), 0, stream,
+                           q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws);
+    else
+        hipLaunchKernelGGL((gdn_chunk_prep<false, 1>), dim3(slots_x8(n_slots), h_v), dim3(256), 0, stream,
+                           q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws);
     return hipGetLastError();
 }
 

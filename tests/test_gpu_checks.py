@@ -241,10 +241,15 @@ def _dec_rowfrag(frag, n_row_tiles, n_ksteps, order):
 _P_BLOCKS = {(0, 0): 0, (1, 0): 1, (2, 0): 2, (2, 1): 3, (3, 0): 4, (3, 1): 5}
 
 
-def test_prep_intermediates_against_chunkwise_oracle():
+@pytest.mark.parametrize("hqk,hv", [(2, 4), (1, 4), (2, 6)],
+                         ids=["pairs", "pairs_of_four_per_qk_head", "single_heads_of_three_per_qk_head"])
+def test_prep_intermediates_against_chunkwise_oracle(hqk, hv):
+    """Prep serves two value heads per workgroup when a q/k head has an even
+    number of them (4 / 2, 4 / 1: there the second pair does not write the
+    shared K^T and Q fragments), one otherwise (6 / 2)."""
     lengths = [200, 64, 1, 130]
-    x = gi.make_inputs(lengths, 2, 4, 128, 128, seed=71, state_std=0.02)
-    _case("prep_stage", x)
+    x = gi.make_inputs(lengths, hqk, hv, 128, 128, seed=71, state_std=0.02)
+    _case(f"prep_stage_{hqk}x{hv}", x)
     d = DevInputs(x)
     ws = workspace_for(x)
     ws.fill_(0xFF)

@@ -91,7 +91,7 @@ def test_chunk_small_lengths(T):
     check_chunk(x, f"small_T{T}")
 
 
-@pytest.mark.parametrize("hqk,hv", [(1, 1), (1, 4), (3, 6)])
+@pytest.mark.parametrize("hqk,hv", [(1, 1), (1, 4), (3, 6), (2, 6)])
 def test_chunk_head_groupings(hqk, hv):
     x = gi.make_inputs([150, 64, 3], hqk, hv, 128, 128, seed=hv, state_std=0.02)
     check_chunk(x, f"groups_{hqk}x{hv}")
