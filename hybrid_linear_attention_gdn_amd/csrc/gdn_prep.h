@@ -299,24 +299,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             *reinterpret_cast<u16x8*>(Kr + rsw(r, 4 * kk + gq)) = kb;
         }
     }
-    // ---- Touch this chunk's value rows of the workgroup's heads (two
-    //      128-byte lines per row and head) into the last-level cache with
-    //      4-byte direct-to-LDS copies into a sink nobody reads, drained at
-    //      the end: the state kernel gathers them on its serial path, where
-    //      HBM misses stall the recurrence (measured: 79 -> 60 us for the
-    //      recurrence after a cold 4000-token prep).  Issued after the K and
-    //      Q loads, which return first.  Not with streaming stores: a
-    //      workspace that large outgrows the cache before the state kernel
-    //      gets there.
-    if (!kStream && wave == 3) {
-        const int row = min(lane, len - 1);
-#pragma unroll
-        for (int hh = 0; hh < kH; ++hh) {
-            const uint16_t* vl = v + ((size_t)(t0 + row) * h_v + h0 + hh) * kDim;
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vl), reinterpret_cast<void*>(vsink), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vl + 64), reinterpret_cast<void*>(vsink), 4, 0, 0);
-        }
-    }
     // ---- decay cumsum (wave hh for head hh, one lane per position) and the
     //      decay vectors
     if (wave < kH) {
@@ -360,6 +342,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         case 1: prep_products<1, kStream, kH>(av, kown, qf, Kr, Ab, Gs, Bs, pdst, lane, gq, ln); break;
         case 2: prep_products<2, kStream, kH>(av, kown, qf, Kr, Ab, Gs, Bs, pdst, lane, gq, ln); break;
         default: prep_products<3, kStream, kH>(av, kown, qf, Kr, Ab, Gs, Bs, pdst, lane, gq, ln); break;
+    }
+    // ---- Touch this chunk's value rows of the workgroup's heads (two
+    //      128-byte lines per row and head) into the last-level cache with
+    //      4-byte direct-to-LDS copies into a sink nobody reads, drained at
+    //      the end: the state kernel gathers them on its serial path, where
+    //      HBM misses stall the recurrence (measured: 79 -> 60 us for the
+    //      recurrence after a cold 4000-token prep).  Issued once the
+    //      products are done, so that they stream in under the UT transform,
+    //      which makes no global accesses, instead of queueing ahead of the
+    //      workgroup's own stores (measured: cold prep 47.8 -> 45.0 us at
+    //      T = 4000).  Not with streaming stores: a workspace that large
+    //      outgrows the cache before the state kernel gets there.
+    if (!kStream && wave == 3) {
+        const int row = min(lane, len - 1);
+#pragma unroll
+        for (int hh = 0; hh < kH; ++hh) {
+            const uint16_t* vl = v + ((size_t)(t0 + row) * h_v + h0 + hh) * kDim;
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vl), reinterpret_cast<void*>(vsink), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vl + 64), reinterpret_cast<void*>(vsink), 4, 0, 0);
+        }
     }
     __syncthreads();                                  // K rows in head 0's A buffer are consumed
     switch (wave) {
