@@ -410,9 +410,9 @@ __device__ __forceinline__ void out_begin(f32x4 (&oacc)[4], const float* dg, con
 // The output wave's second half: + P U', then the stores of the output rows
 // t0 .. t0 + len - 1 of the tile.  out_tile points at column 0 of the tile
 // (row 0 of the chunk); rows past len go to the sink so that the number of
-// stores never changes.
+// stores never changes.  nt: non-temporal stores (wave-uniform).
 __device__ __forceinline__ void out_end(f32x4 (&oacc)[4], const PFrag& pf, const f16* usrc, float* out_tile,
-                                        size_t row_stride, int len, float* junk, int lane, int gq, int ln) {
+                                        size_t row_stride, int len, float* junk, bool nt, int lane, int gq, int ln) {
     f16x8 ua[2];
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) ua[qq] = *reinterpret_cast<const f16x8*>(&usrc[(qq * 64 + lane) * 8]);
@@ -426,7 +426,8 @@ __device__ __forceinline__ void out_end(f32x4 (&oacc)[4], const PFrag& pf, const
     for (int p = 0; p < 4; ++p) {
         const int row = 16 * p + ln;
         float* d = row < len ? out_tile + (size_t)row * row_stride + 4 * gq : junk + 4 * lane;
-        *reinterpret_cast<f32x4*>(d) = oacc[p];
+        if (nt) __builtin_nontemporal_store(oacc[p], reinterpret_cast<f32x4*>(d));
+        else *reinterpret_cast<f32x4*>(d) = oacc[p];
     }
 }
 
@@ -445,6 +446,7 @@ struct SegArgs {
     const float* hstart;     // [segslot][h_v][128][128]: incoming state of every segment of a
                              // sequence with two or more (segment 0's copied from s0 by the scan)
     float* maps;             // [segslot][h_v][2][128][128]: Phi, R of segments s < nseg - 1
+    int stream_out;          // the output goes out as non-temporal stores
 };
 
 __device__ __forceinline__ int seg_base(const int32_t* cu, int n, int sc) {
@@ -695,7 +697,7 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
                 for (int r = 0; r < kChains; ++r)
                     out_end(oacc[r], pf, ubuf[r][(cc - c_begin) & 1],
                             out + ((size_t)t0 * h_v + h) * kDim + 16 * tile_of(r), (size_t)h_v * kDim,
-                            min(kChunk, end - t0), ws.junk, lane, gq, ln);
+                            min(kChunk, end - t0), ws.junk, sa.stream_out != 0, lane, gq, ln);
             };
             auto begin_of = [&](int cc, const QFrag& qf) {
 #pragma unroll
@@ -883,21 +885,30 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
                             const ChunkWorkspace& ws, int n_slots, int stage_mask,
                             const SegLaunch* seg, hipStream_t stream)
 {
+    // Streaming stores of prep's intermediates once they outgrow what the
+    // 256 MB last-level cache keeps for the state kernel.  Measured crossover
+    // between 114 MB (T = 4000: ordinary stores 13 us faster per layer) and
+    // 170 MB (T = 6000: streaming 2 us faster; 8-10% from 227 MB on).
+    const size_t inter = (size_t)n_slots * ((size_t)h_v * ((kTuElems + kPElems) * sizeof(f16) +
+                                                           kGElems * sizeof(float)) +
+                                            (size_t)h_qk * (kKtElems + kQfElems) * sizeof(f16));
+    const bool stream_inter = inter > kStreamWorkspaceBytes;
     if ((stage_mask & 1) && total_tokens > 0) {
-        // Streaming stores once the intermediates outgrow what the 256 MB
-        // last-level cache keeps for the state kernel.  Measured crossover
-        // between 114 MB (T = 4000: ordinary stores 13 us faster per layer)
-        // and 170 MB (T = 6000: streaming 2 us faster; 8-10% from 227 MB on).
-        const size_t inter = (size_t)n_slots * ((size_t)h_v * ((kTuElems + kPElems) * sizeof(f16) +
-                                                               kGElems * sizeof(float)) +
-                                                (size_t)h_qk * (kKtElems + kQfElems) * sizeof(f16));
-        const hipError_t e = inter > kStreamWorkspaceBytes
+        const hipError_t e = stream_inter
                                  ? launch_prep_stream(q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws, n_slots, stream)
                                  : launch_prep(q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws, n_slots, stream);
         if (e != hipSuccess) return e;
     }
     if ((stage_mask & 2) && n_seqs > 0) {
         SegArgs sa = {};
+        // While the intermediates stay in the last-level cache (prep stores
+        // them ordinarily), the output goes around it, so that it neither
+        // evicts them nor, after other work, makes the cache write back
+        // dirty lines to take it in (measured at T = 4000: recurrence 59.0 ->
+        // 56.3 us cold, 92.7 -> 90.5 us per layer warm).  Once they come
+        // from HBM anyway, ordinary stores were faster (varlen batch 268 ->
+        // 292 us, T = 131072 2.04 -> 2.18 ms with non-temporal ones).
+        sa.stream_out = !stream_inter;
         if (!seg) {
             const int units = n_seqs * h_v;
             const dim3 grid(state_grid(units, 8));
