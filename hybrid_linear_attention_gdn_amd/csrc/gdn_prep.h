@@ -223,7 +223,7 @@ __device__ __forceinline__ void diag_inverse(float* Ab, int ib, int gq, int ln) 
 
 // ---------------------------------------------------------------------------
 // Stage 1: intra-chunk preparation.  One workgroup per (chunk slot, group of
-// kH value heads of one q/k head); 36 KB of LDS at kH = 2 (18 KB at kH = 1)
+// kH value heads of one q/k head); 36 KB of LDS
 // and at most 128 registers per lane so that four workgroups share a CU.
 // The UT transform of each head runs in place in its A buffer: A, then
 // Tm = (I + A)^{-1}, read out as the fp16 fragments of Tm diag(beta).
@@ -243,9 +243,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const int j = h0 / ws.group;
     const bool first = h0 % ws.group == 0;            // holds the q/k head's first value head
 
-    // Per head: A buffer (K rows (16 KB bf16) in head 0's until the products
-    // have read them, then A, then Tm; Q rows at the end), beta and G.
-    __shared__ __attribute__((aligned(16))) float Abuf[kH][kChunk * kTA];
+    // Per head: A buffer (K rows (16 KB bf16) in head 0's and Q rows in the
+    // second until the products have read them, then A, then Tm; Q rows in
+    // head 0's at the end), beta and G.  Two buffers also at kH = 1.
+    __shared__ __attribute__((aligned(16))) float Abuf[kH < 2 ? 2 : kH][kChunk * kTA];
     __shared__ __attribute__((aligned(16))) float Bsh[kH][kChunk];
     __shared__ float Gsh[kH][kChunk];
     __shared__ __attribute__((aligned(16))) float vsink[64];   // target of the value-line touches, never read
@@ -275,28 +276,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         b_in = beta[(size_t)(t0 + lane) * h_v + h0 + wave];
     }
 
-    // ---- This wave's row tile of K and Q (rows 16 w + ln, dims 32 kk + 8 gq
-    //      .. +7), the only global reads of the inputs: K goes to LDS
-    //      row-major (bf16, in head 0's A buffer, which is still free) so
+    // ---- The chunk's K and Q rows, the only global reads of the inputs, by
+    //      direct-to-LDS copies of whole rows (bf16, row-major, chunk-swizzled:
+    //      K in head 0's A buffer, Q in the second one, both still free), so
     //      that every wave can read the row tiles its Gram rows need and the
-    //      K^T fragments can be read from it transposed.  Q stays in
-    //      registers.  Pad rows are zero.
+    //      K^T fragments can be read from them transposed.  Each wave then
+    //      takes its own row tile of K and Q (rows 16 w + ln, dims 32 kk +
+    //      8 gq .. +7) into registers.  Pad rows of a short chunk are zero
+    //      (they copy the last row, and the owning wave clears them).
+    //      Measured against 16-byte register loads of the row tiles: prep at
+    //      T = 131072 650 -> 630 us, varlen batch 130 -> 124 us.
     uint16_t* Kr = reinterpret_cast<uint16_t*>(Abuf[0]);   // [pos][dim] bf16, chunk-swizzled
     bf16x8 kown[4], qf[4];
     {
+        uint16_t* Qs = reinterpret_cast<uint16_t*>(Abuf[1]);   // Q rows, until the products
+        // wave w copies rows 16 w .. 16 w + 15 of K and Q, four rows (1 KB)
+        // per instruction: lane l of copy i takes row r = 16 w + 4 i + l / 16
+        // into chunk slot l % 16, i.e. global chunk (l % 16) ^ (r % 16)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * wave + 4 * i + (lane >> 4);
+            const int c = (lane & 15) ^ (r & 15);
+            const size_t off = ((size_t)(t0 + min(r, len - 1)) * h_qk + j) * kDim + 8 * c;
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(k + off),
+                                             reinterpret_cast<void*>(Kr + (16 * wave + 4 * i) * kDim), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(q + off),
+                                             reinterpret_cast<void*>(Qs + (16 * wave + 4 * i) * kDim), 16, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
         const int r = 16 * wave + ln;
-        const size_t krow = ((size_t)(t0 + r) * h_qk + j) * kDim;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             u16x8 kb = {0, 0, 0, 0, 0, 0, 0, 0};
             u16x8 qb = {0, 0, 0, 0, 0, 0, 0, 0};
             if (r < len) {
-                kb = *reinterpret_cast<const u16x8*>(k + krow + 32 * kk + 8 * gq);
-                qb = *reinterpret_cast<const u16x8*>(q + krow + 32 * kk + 8 * gq);
+                kb = *reinterpret_cast<const u16x8*>(Kr + rsw(r, 4 * kk + gq));
+                qb = *reinterpret_cast<const u16x8*>(Qs + rsw(r, 4 * kk + gq));
+            } else {
+                *reinterpret_cast<u16x8*>(Kr + rsw(r, 4 * kk + gq)) = kb;     // pad rows are zero
             }
             kown[kk] = __builtin_bit_cast(bf16x8, kb);
             qf[kk] = __builtin_bit_cast(bf16x8, qb);
-            *reinterpret_cast<u16x8*>(Kr + rsw(r, 4 * kk + gq)) = kb;
         }
     }
     // ---- decay cumsum (wave hh for head hh, one lane per position) and the
