@@ -19,7 +19,8 @@ struct SegLaunch {
 };
 
 // Enqueues the intra-chunk preparation (one workgroup per chunk slot and
-// value head) on `stream`, with ordinary or with non-temporal stores of the
+// pair of value heads sharing a q/k head, or per value head when they do not
+// pair up) on `stream`, with ordinary or with non-temporal stores of the
 // intermediates.
 hipError_t launch_prep(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
                        const int32_t* cu, int n_seqs, int h_qk, int h_v, const ChunkWorkspace& ws, int n_slots,
