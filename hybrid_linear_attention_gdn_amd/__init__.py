@@ -150,13 +150,7 @@ def _stream(stream, *tensors) -> Optional[int]:
     import torch
     for t in tensors:
         if isinstance(t, torch.Tensor) and t.is_cuda:
-            # the current stream's handle without building a Stream object
-            # (0.1 instead of 2 us per call; the same handle, also inside
-            # torch.cuda.stream(...) and graph capture)
-            raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-            if raw is not None:
-                return raw(t.get_device())
-            return torch.cuda.current_stream(t.device).cuda_stream
+            return _current_stream(t.get_device())
     return None
 
 
@@ -348,11 +342,8 @@ def gdn_chunk_fwd_segmented(q, k, v, g, beta, cu_seqlens, initial_state, out, fi
     _check(lib, st, "gdn_chunk_fwd_segmented")
 
 
-def gdn_recurrent_step(q, k, v, g, beta, n_requests: int, tokens_per_request: int,
-                       state_in, state_out, out, intermediate_states, save_intermediate_states: bool,
-                       *, dims: Optional[gdn_dims] = None, stream=None) -> None:
-    """Per-token update for decode / speculative verify (see include/gdn.h)."""
-    lib = load_library()
+def _recurrent_step_args(q, k, v, g, beta, n_requests, tokens_per_request, state_in, state_out, out,
+                         intermediate_states, save_intermediate_states, dims):
     if dims is None:
         dims = _dims_from(q, v, n_requests, n_requests * tokens_per_request)
     import torch
@@ -362,12 +353,77 @@ def gdn_recurrent_step(q, k, v, g, beta, n_requests: int, tokens_per_request: in
     _check_arg(state_out, "gdn_recurrent_step", "state_out", (torch.float32,), state)
     _check_arg(intermediate_states, "gdn_recurrent_step", "intermediate_states", (torch.float32,),
                (dims.n_seqs, tokens_per_request) + state[1:])
-    st = lib.gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                int(n_requests), int(tokens_per_request),
-                                _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(intermediate_states),
-                                1 if save_intermediate_states else 0, ctypes.byref(dims),
-                                _stream(stream, q, state_in, out))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), int(n_requests), int(tokens_per_request),
+            _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(intermediate_states),
+            1 if save_intermediate_states else 0, ctypes.byref(dims))
+    return args, dims
+
+
+def gdn_recurrent_step(q, k, v, g, beta, n_requests: int, tokens_per_request: int,
+                       state_in, state_out, out, intermediate_states, save_intermediate_states: bool,
+                       *, dims: Optional[gdn_dims] = None, stream=None) -> None:
+    """Per-token update for decode / speculative verify (see include/gdn.h)."""
+    lib = load_library()
+    args, _ = _recurrent_step_args(q, k, v, g, beta, n_requests, tokens_per_request, state_in, state_out, out,
+                                   intermediate_states, save_intermediate_states, dims)
+    st = lib.gdn_recurrent_step(*args, _stream(stream, q, state_in, out))
     _check(lib, st, "gdn_recurrent_step")
+
+
+class Prepared:
+    """One entry point's call with its arguments checked and marshalled once.
+
+    For a serving loop that reuses the same buffers, writing each step's
+    token inputs into them in place: calling the object enqueues the step on
+    `stream` (a torch stream or a raw handle), or on the current stream of
+    the buffers' device, with no tensor checks, so that the host cost of an
+    eager step is the library call alone.  The buffers must stay alive, on
+    their device, with their shapes; the object keeps references to them."""
+
+    __slots__ = ("_lib", "_fn", "_args", "_device", "_what", "_keep")
+
+    def __init__(self, lib, fn, args, device, what, keep):
+        self._lib, self._fn, self._args, self._device, self._what, self._keep = lib, fn, args, device, what, keep
+
+    def __call__(self, stream=None) -> None:
+        if stream is None:
+            if self._device is None:
+                raise GDNError(GDN_ERR_INVALID_VALUE, f"{self._what}: raw addresses need an explicit stream")
+            handle = _current_stream(self._device)
+        else:
+            handle = stream if isinstance(stream, int) else stream.cuda_stream
+        st = self._fn(*self._args, handle)
+        if st != GDN_SUCCESS:
+            _check(self._lib, st, self._what)
+
+
+def _current_stream(device: int) -> int:
+    """The current stream's handle without building a Stream object (0.1
+    instead of 2 us per call; the same handle, also inside
+    torch.cuda.stream(...) and graph capture)."""
+    import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(device)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _device_of(*tensors) -> Optional[int]:
+    for t in tensors:
+        if t is not None and not isinstance(t, int):
+            return t.get_device()
+    return None
+
+
+def prepare_recurrent_step(q, k, v, g, beta, n_requests: int, tokens_per_request: int,
+                           state_in, state_out, out, intermediate_states, save_intermediate_states: bool,
+                           *, dims: Optional[gdn_dims] = None) -> Prepared:
+    """gdn_recurrent_step with its arguments checked once (see Prepared)."""
+    lib = load_library()
+    args, dims = _recurrent_step_args(q, k, v, g, beta, n_requests, tokens_per_request, state_in, state_out, out,
+                                      intermediate_states, save_intermediate_states, dims)
+    keep = (q, k, v, g, beta, state_in, state_out, out, intermediate_states, dims)
+    return Prepared(lib, lib.gdn_recurrent_step, args, _device_of(q, state_in, out), "gdn_recurrent_step", keep)
 
 
 def _state_dtype(pool) -> int:
@@ -379,16 +435,8 @@ def _state_dtype(pool) -> int:
     raise GDNError(GDN_ERR_INVALID_VALUE, f"state pool dtype {pool.dtype} is neither float32 nor float16")
 
 
-def gdn_recurrent_step_slots(q, k, v, g, beta, cu_tokens, n_requests: int, max_tokens: int,
-                             state_pool, slot_table, num_accepted, out, *,
-                             state_dtype: Optional[int] = None, pool_slots: Optional[int] = None,
-                             dims: Optional[gdn_dims] = None, stream=None) -> None:
-    """Per-token update over a pool of state slots (see include/gdn.h).
-
-    ``state_pool`` is a float32 or float16 tensor [pool_slots, H_v, d_k, d_v];
-    ``slot_table`` int32 [R, max_tokens + 1]; ``num_accepted`` int32 [R] or None.
-    """
-    lib = load_library()
+def _recurrent_step_slots_args(q, k, v, g, beta, cu_tokens, n_requests, max_tokens, state_pool, slot_table,
+                               num_accepted, out, state_dtype, pool_slots, dims):
     if dims is None:
         dims = _dims_from(q, v, n_requests, q.shape[0])
     if state_dtype is None:
@@ -404,11 +452,39 @@ def gdn_recurrent_step_slots(q, k, v, g, beta, cu_tokens, n_requests: int, max_t
                (pool_slots, dims.n_heads_v, dims.d_k, dims.d_v))
     _check_arg(slot_table, "gdn_recurrent_step_slots", "slot_table", i32, (dims.n_seqs, int(max_tokens) + 1))
     _check_arg(num_accepted, "gdn_recurrent_step_slots", "num_accepted", i32, (dims.n_seqs,))
-    st = lib.gdn_recurrent_step_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_tokens),
-                                      int(n_requests), int(max_tokens), _ptr(state_pool), int(state_dtype),
-                                      int(pool_slots), _ptr(slot_table), _ptr(num_accepted), _ptr(out),
-                                      ctypes.byref(dims), _stream(stream, q, state_pool, out))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_tokens),
+            int(n_requests), int(max_tokens), _ptr(state_pool), int(state_dtype),
+            int(pool_slots), _ptr(slot_table), _ptr(num_accepted), _ptr(out), ctypes.byref(dims))
+    return args, dims
+
+
+def gdn_recurrent_step_slots(q, k, v, g, beta, cu_tokens, n_requests: int, max_tokens: int,
+                             state_pool, slot_table, num_accepted, out, *,
+                             state_dtype: Optional[int] = None, pool_slots: Optional[int] = None,
+                             dims: Optional[gdn_dims] = None, stream=None) -> None:
+    """Per-token update over a pool of state slots (see include/gdn.h).
+
+    ``state_pool`` is a float32 or float16 tensor [pool_slots, H_v, d_k, d_v];
+    ``slot_table`` int32 [R, max_tokens + 1]; ``num_accepted`` int32 [R] or None.
+    """
+    lib = load_library()
+    args, _ = _recurrent_step_slots_args(q, k, v, g, beta, cu_tokens, n_requests, max_tokens, state_pool,
+                                         slot_table, num_accepted, out, state_dtype, pool_slots, dims)
+    st = lib.gdn_recurrent_step_slots(*args, _stream(stream, q, state_pool, out))
     _check(lib, st, "gdn_recurrent_step_slots")
+
+
+def prepare_recurrent_step_slots(q, k, v, g, beta, cu_tokens, n_requests: int, max_tokens: int,
+                                 state_pool, slot_table, num_accepted, out, *,
+                                 state_dtype: Optional[int] = None, pool_slots: Optional[int] = None,
+                                 dims: Optional[gdn_dims] = None) -> Prepared:
+    """gdn_recurrent_step_slots with its arguments checked once (see Prepared)."""
+    lib = load_library()
+    args, dims = _recurrent_step_slots_args(q, k, v, g, beta, cu_tokens, n_requests, max_tokens, state_pool,
+                                            slot_table, num_accepted, out, state_dtype, pool_slots, dims)
+    keep = (q, k, v, g, beta, cu_tokens, state_pool, slot_table, num_accepted, out, dims)
+    return Prepared(lib, lib.gdn_recurrent_step_slots, args, _device_of(q, state_pool, out),
+                    "gdn_recurrent_step_slots", keep)
 
 
 def _host_ptr(a):

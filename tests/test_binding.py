@@ -96,3 +96,19 @@ def test_slot_step_checks_its_index_arrays():
         gdn.gdn_recurrent_step_slots(ADDR, ADDR, ADDR, ADDR, ADDR, ADDR, R, mt, pool[1:], ADDR, None, ADDR, **kw)
     with pytest.raises(gdn.GDNError, match="state_pool is not a GPU tensor"):
         gdn.gdn_recurrent_step_slots(ADDR, ADDR, ADDR, ADDR, ADDR, ADDR, R, mt, pool, ADDR, None, ADDR, dims=dims)
+
+
+def test_prepared_calls_check_their_arguments_once_like_the_plain_calls():
+    R, n = 3, 6
+    dims = gdn.make_dims(R, R * n, HQK, HV)
+    with pytest.raises(gdn.GDNError, match="intermediate_states has shape"):
+        gdn.prepare_recurrent_step(ADDR, ADDR, ADDR, ADDR, ADDR, R, n, ADDR, None, ADDR,
+                                   torch.zeros(R, n - 1, HV, D, D), True, dims=dims)
+    pool = torch.zeros(9, HV, D, D, dtype=torch.float16)
+    with pytest.raises(gdn.GDNError, match="state_pool is not a GPU tensor"):
+        gdn.prepare_recurrent_step_slots(ADDR, ADDR, ADDR, ADDR, ADDR, ADDR, R, 5, pool, ADDR, None, ADDR,
+                                         dims=gdn.make_dims(R, 7, HQK, HV))
+    # raw addresses carry no device, so a call needs an explicit stream
+    step = gdn.prepare_recurrent_step(ADDR, ADDR, ADDR, ADDR, ADDR, R, n, ADDR, ADDR, ADDR, None, False, dims=dims)
+    with pytest.raises(gdn.GDNError, match="need an explicit stream"):
+        step()

@@ -4,6 +4,7 @@
 * inputs scaled toward the fp16 operand range (v and states x 1024);
 * guard bands around every output of the recurrent step, the slot pool and
   the chunk-boundary snapshots (nothing written outside its tensor);
+* the prepared (checked-once) step calls against the plain ones, bit for bit;
 * the intra-chunk preparation checked on its own, kernel by kernel as the
   "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page does in its section on
   precision (each kernel against an fp32-or-better reference): its
@@ -349,3 +350,58 @@ def test_debug_checks_reject_bad_device_contents(monkeypatch):
         gdn.gdn_recurrent_step(dy.q, dy.k, dy.v, dy.g, dy.beta, 8, 6, s_bad, s_bad, vout, None, False)
     assert "state_in" in str(ei.value)
     monkeypatch.delenv("GDN_DEBUG_CHECKS")
+
+
+# ------------------------------------------------------------ prepared calls
+
+def test_prepared_steps_match_the_plain_calls_bitwise():
+    """prepare_recurrent_step / prepare_recurrent_step_slots check and marshal
+    their arguments once; each later call must compute what the plain call
+    computes on the buffers' contents at that time, bit for bit: decode in
+    place over three steps with new tokens written into the same buffers,
+    verify with snapshots on an explicit stream, and an fp16 slot-pool step."""
+    R = 8
+    xs = [gi.make_inputs([1] * R, 16, 32, 128, 128, seed=90 + i, state_std=0.02) for i in range(3)]
+    _case("prepared_decode", xs[0])
+    d0 = DevInputs(xs[0])
+    s_a, s_b = d0.s0.clone(), d0.s0.clone()
+    out_a = torch.full((R, 32, 128), float("nan"), device="cuda")
+    out_b = torch.full_like(out_a, float("nan"))
+    step = gdn.prepare_recurrent_step(d0.q, d0.k, d0.v, d0.g, d0.beta, R, 1, s_a, s_a, out_a, None, False)
+    for x in xs:
+        dx = DevInputs(x)
+        for name in ("q", "k", "v", "g", "beta"):
+            getattr(d0, name).copy_(getattr(dx, name))
+        step()
+        gdn.gdn_recurrent_step(d0.q, d0.k, d0.v, d0.g, d0.beta, R, 1, s_b, s_b, out_b, None, False)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a, out_b) and torch.equal(s_a, s_b)
+
+    y = gi.verify_8x6(seed=3)
+    dy = DevInputs(y)
+    inter_a = torch.full((R, 6, 32, 128, 128), float("nan"), device="cuda")
+    inter_b = torch.full_like(inter_a, float("nan"))
+    vo_a = torch.empty((R * 6, 32, 128), device="cuda")
+    vo_b = torch.empty_like(vo_a)
+    side = torch.cuda.Stream()
+    vstep = gdn.prepare_recurrent_step(dy.q, dy.k, dy.v, dy.g, dy.beta, R, 6, dy.s0, None, vo_a, inter_a, True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        vstep(side)
+    side.synchronize()
+    gdn.gdn_recurrent_step(dy.q, dy.k, dy.v, dy.g, dy.beta, R, 6, dy.s0, None, vo_b, inter_b, True)
+    torch.cuda.synchronize()
+    assert torch.equal(vo_a, vo_b) and torch.equal(inter_a, inter_b)
+
+    pool_np = gi.state_pool(y, R * 6, f16=True)
+    pool_a = torch.from_numpy(pool_np).to("cuda")
+    pool_b = pool_a.clone()
+    table = torch.from_numpy(gi.slot_table_contiguous(R, 6, R)).to("cuda")
+    cu_tok = torch.from_numpy(y.cu_seqlens).to("cuda")
+    so_a = torch.empty((R * 6, 32, 128), device="cuda")
+    so_b = torch.empty_like(so_a)
+    sstep = gdn.prepare_recurrent_step_slots(dy.q, dy.k, dy.v, dy.g, dy.beta, cu_tok, R, 6, pool_a, table, None, so_a)
+    sstep()
+    gdn.gdn_recurrent_step_slots(dy.q, dy.k, dy.v, dy.g, dy.beta, cu_tok, R, 6, pool_b, table, None, so_b)
+    torch.cuda.synchronize()
+    assert torch.equal(so_a, so_b) and torch.equal(pool_a, pool_b)
