@@ -221,6 +221,48 @@ __device__ __forceinline__ void diag_inverse(float* Ab, int ib, int gq, int ln) 
     for (int e = 0; e < 4; ++e) Ab[(16 * ib + 4 * gq + e) * kTA + 16 * ib + ln] = t[e];
 }
 
+// One block column JB of the off-diagonal solve of one head's Tm = (I + A)^{-1}:
+// Tm_ij = -Tm_ii sum_{k=JB}^{i-1} A_ik Tm_kJB for i = JB+1..3, with 16x16x16
+// products on the matrix cores (split fp16 operands, ~fp32 accuracy).  A
+// product's accumulator is already the B operand of the next one, so the
+// column chain stays in registers.  offcol_load reads the blocks the column
+// needs (Tm_JBJB, Tm_ii, A_ik), offcol_solve forms and stores the column's Tm
+// blocks over A's; every read of a head's blocks must precede every store.
+struct OffCol {
+    Split16 tcol[4];   // Tm_{k, JB} in accumulator (= B operand) layout, k >= JB
+    f32x4 aik[4][4];   // A_ik, A-operand layout
+    f32x4 tii[4];      // Tm_ii, A-operand layout
+};
+
+template <int JB>
+__device__ __forceinline__ void offcol_load(OffCol& o, const float* A, int gq, int ln) {
+    f32x4 t;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = A[(16 * JB + 4 * gq + e) * kTA + 16 * JB + ln];
+    o.tcol[JB] = split16(t);
+#pragma unroll
+    for (int i2 = JB + 1; i2 < 4; ++i2) {
+        o.tii[i2] = *reinterpret_cast<const f32x4*>(A + (16 * i2 + ln) * kTA + 16 * i2 + 4 * gq);
+#pragma unroll
+        for (int kb = JB; kb < i2; ++kb)
+            o.aik[i2][kb] = *reinterpret_cast<const f32x4*>(A + (16 * i2 + ln) * kTA + 16 * kb + 4 * gq);
+    }
+}
+
+template <int JB>
+__device__ __forceinline__ void offcol_solve(OffCol& o, float* A, int gq, int ln) {
+#pragma unroll
+    for (int i2 = JB + 1; i2 < 4; ++i2) {
+        f32x4 xs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = JB; kb < i2; ++kb) xs = mfma_split16(split16(o.aik[i2][kb]), o.tcol[kb], xs);
+        const f32x4 y = mfma_split16(split16(o.tii[i2]), split16(xs), f32x4{0.f, 0.f, 0.f, 0.f});
+        o.tcol[i2] = split16(-y);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) A[(16 * i2 + 4 * gq + e) * kTA + 16 * JB + ln] = -y[e];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Stage 1: intra-chunk preparation.  One workgroup per (chunk slot, group of
 // kH value heads of one q/k head); 36 KB of LDS
@@ -397,54 +439,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
     for (int hh = 0; hh < kH; ++hh) diag_inverse(Ab[hh], wave, gq, ln);
     __syncthreads();
-    //  (2) Below the diagonal, block column j on wave j, rows i = j+1..3:
-    //      Tm_ij = -Tm_ii sum_{k=j}^{i-1} A_ik Tm_kj, with 16x16x16 products on
-    //      the matrix cores (split fp16 operands, ~fp32 accuracy).  A product's
-    //      accumulator is already the B operand of the next one, so the column
-    //      chain stays in registers.  Every A_ik a wave needs is read before
-    //      any wave overwrites A blocks with Tm blocks.
-    const int jb = wave;
-#pragma unroll
-    for (int hh = 0; hh < kH; ++hh) {
-        Split16 tcol[4];   // Tm_{k, jb} in accumulator (= B operand) layout, k >= jb
-        f32x4 aik[4][4];   // A_ik, A-operand layout
-        f32x4 tii[4];      // Tm_ii, A-operand layout
-        float* A = Ab[hh];
-        if (wave < 3) {
-#pragma unroll
-            for (int kb = 0; kb < 3; ++kb) {
-                if (kb != jb) continue;
-                f32x4 t;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) t[e] = A[(16 * kb + 4 * gq + e) * kTA + 16 * kb + ln];
-                tcol[kb] = split16(t);
+    //  (2) Below the diagonal, by block columns (offcol_*): column 0 is a
+    //      chain of nine split products, column 1 of five, column 2 of two.
+    //      With two heads, waves 0 and 1 take column 0 of head 0 and head 1,
+    //      waves 2 and 3 columns 1 and 2 of head 0 and head 1, so that no
+    //      wave runs more than one nine-product chain; with one head, wave j
+    //      takes column j.
+    {
+        OffCol oa, ob;
+        if constexpr (kH == 2) {
+            switch (wave) {
+                case 0: offcol_load<0>(oa, Ab[0], gq, ln); break;
+                case 1: offcol_load<0>(oa, Ab[1], gq, ln); break;
+                case 2: offcol_load<1>(oa, Ab[0], gq, ln); offcol_load<2>(ob, Ab[0], gq, ln); break;
+                default: offcol_load<1>(oa, Ab[1], gq, ln); offcol_load<2>(ob, Ab[1], gq, ln); break;
             }
-#pragma unroll
-            for (int i2 = 1; i2 < 4; ++i2) {
-                if (i2 <= jb) continue;
-                tii[i2] = *reinterpret_cast<const f32x4*>(A + (16 * i2 + ln) * kTA + 16 * i2 + 4 * gq);
-#pragma unroll
-                for (int kb = 0; kb < i2; ++kb) {
-                    if (kb < jb) continue;
-                    aik[i2][kb] = *reinterpret_cast<const f32x4*>(A + (16 * i2 + ln) * kTA + 16 * kb + 4 * gq);
-                }
+            __syncthreads();
+            switch (wave) {
+                case 0: offcol_solve<0>(oa, Ab[0], gq, ln); break;
+                case 1: offcol_solve<0>(oa, Ab[1], gq, ln); break;
+                case 2: offcol_solve<1>(oa, Ab[0], gq, ln); offcol_solve<2>(ob, Ab[0], gq, ln); break;
+                default: offcol_solve<1>(oa, Ab[1], gq, ln); offcol_solve<2>(ob, Ab[1], gq, ln); break;
             }
-        }
-        __syncthreads();
-        if (wave < 3) {
-#pragma unroll
-            for (int i2 = 1; i2 < 4; ++i2) {
-                if (i2 <= jb) continue;
-                f32x4 xs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < i2; ++kb) {
-                    if (kb < jb) continue;
-                    xs = mfma_split16(split16(aik[i2][kb]), tcol[kb], xs);
-                }
-                const f32x4 y = mfma_split16(split16(tii[i2]), split16(xs), f32x4{0.f, 0.f, 0.f, 0.f});
-                tcol[i2] = split16(-y);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) A[(16 * i2 + 4 * gq + e) * kTA + 16 * jb + ln] = -y[e];
+        } else {
+            switch (wave) {
+                case 0: offcol_load<0>(oa, Ab[0], gq, ln); break;
+                case 1: offcol_load<1>(oa, Ab[0], gq, ln); break;
+                case 2: offcol_load<2>(oa, Ab[0], gq, ln); break;
+                default: break;
+            }
+            __syncthreads();
+            switch (wave) {
+                case 0: offcol_solve<0>(oa, Ab[0], gq, ln); break;
+                case 1: offcol_solve<1>(oa, Ab[0], gq, ln); break;
+                case 2: offcol_solve<2>(oa, Ab[0], gq, ln); break;
+                default: break;
             }
         }
     }
