@@ -54,6 +54,12 @@ struct ChunkWorkspace {
     __device__ __forceinline__ size_t kunit(int slot, int j) const { return (size_t)slot * h_qk + j; }
 };
 
+// Cache-policy operand of a direct global-to-LDS copy
+// (__builtin_amdgcn_global_load_lds): 0 ordinary, 2 non-temporal (the line
+// is not kept for reuse).
+constexpr int kCopyCached = 0;
+constexpr int kCopyNonTemporal = 2;
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }

@@ -327,7 +327,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     //      8 gq .. +7) into registers.  Pad rows of a short chunk are zero
     //      (they copy the last row, and the owning wave clears them).
     //      Measured against 16-byte register loads of the row tiles: prep at
-    //      T = 131072 650 -> 630 us, varlen batch 130 -> 124 us.
+    //      T = 131072 650 -> 630 us, varlen batch 130 -> 124 us.  The copies
+    //      are non-temporal: nothing reads these rows again, and kept in the
+    //      caches they would only push out lines the state kernel reads next
+    //      (dirty ones among them, written back on the way).  Measured: cold
+    //      prep 42 -> 36 us at T = 4000, 122 -> 95 us on the varlen batch,
+    //      630 -> 576 us at T = 131072; back-to-back repeats of one layer,
+    //      which could reuse cached rows, lose 3 us.
     uint16_t* Kr = reinterpret_cast<uint16_t*>(Abuf[0]);   // [pos][dim] bf16, chunk-swizzled
     bf16x8 kown[4], qf[4];
     {
@@ -341,9 +347,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             const int c = (lane & 15) ^ (r & 15);
             const size_t off = ((size_t)(t0 + min(r, len - 1)) * h_qk + j) * kDim + 8 * c;
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(k + off),
-                                             reinterpret_cast<void*>(Kr + (16 * wave + 4 * i) * kDim), 16, 0, 0);
+                                             reinterpret_cast<void*>(Kr + (16 * wave + 4 * i) * kDim), 16, 0,
+                                             kCopyNonTemporal);
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(q + off),
-                                             reinterpret_cast<void*>(Qs + (16 * wave + 4 * i) * kDim), 16, 0, 0);
+                                             reinterpret_cast<void*>(Qs + (16 * wave + 4 * i) * kDim), 16, 0,
+                                             kCopyNonTemporal);
         }
         __builtin_amdgcn_s_waitcnt(0);
         const int r = 16 * wave + ln;
