@@ -107,13 +107,13 @@ MEASURED_TRAFFIC = {
     # warm and cold launches of the counter run)
     "gdn_chunk_state": {
         "sources": [CSRC + "gdn_chunk.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
-        "sources_sha256_prefix": "6a71cb17230f8c9f",
+        "sources_sha256_prefix": "9086347b1e0a8780",
         "bytes": (44848 * 2 + 66056) * 1024,
     },
     "gdn_chunk_prep": {
         "sources": [CSRC + "gdn_prep.h", CSRC + "gdn_prep.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
-        "sources_sha256_prefix": "788776950ba76bb8",
-        "bytes": (32680 * 2 + 57456) * 1024,
+        "sources_sha256_prefix": "756fce83b5a71959",
+        "bytes": (32693 * 2 + 57456) * 1024,
     },
 }
 
