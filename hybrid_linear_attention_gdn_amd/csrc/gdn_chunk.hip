@@ -447,6 +447,14 @@ struct SegArgs {
                              // sequence with two or more (segment 0's copied from s0 by the scan)
     float* maps;             // [segslot][h_v][2][128][128]: Phi, R of segments s < nseg - 1
     int stream_out;          // the output goes out as non-temporal stores
+    // Whole sequences: the launch runs the chunks whose slots lie in
+    // slot_lo .. slot_hi - 1, whose intermediates sit in workspace slots
+    // 0 .. slot_hi - slot_lo - 1.  A sequence that starts before slot_lo
+    // takes its incoming state from carry, one that goes on past slot_hi
+    // leaves its state there ([seq][h_v][128][128]); null when the launch
+    // covers every slot.
+    int slot_lo, slot_hi;
+    float* carry;
 };
 
 __device__ __forceinline__ int seg_base(const int32_t* cu, int n, int sc) {
@@ -585,19 +593,23 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
     const int start = cu[seq];
     const int end = cu[seq + 1];
     const int nchunks = (end - start + kChunk - 1) / kChunk;
-    const int c_begin = kSeg ? sg * sa.seg_chunks : 0;
-    const int c_end = kSeg ? min(c_begin + sa.seg_chunks, nchunks) : nchunks;
     const int slot0 = slot_base(cu, seq);
-    auto vidx = [&](int c) { return ws.vunit(slot0 + min(c, c_end - 1), h); };
-    auto kidx = [&](int c) { return ws.kunit(slot0 + min(c, c_end - 1), j); };
+    const int c_begin = kSeg ? sg * sa.seg_chunks : max(0, sa.slot_lo - slot0);
+    const int c_end = kSeg ? min(c_begin + sa.seg_chunks, nchunks) : min(nchunks, sa.slot_hi - slot0);
+    // a whole sequence with no chunk in the launch's slots has nothing to do
+    // here (an empty one is handled by the launch that holds its slot)
+    if (!kSeg && (nchunks > 0 ? c_begin >= c_end : slot0 < sa.slot_lo || slot0 >= sa.slot_hi)) return;
+    const int wslot0 = kSeg ? slot0 : slot0 - sa.slot_lo;     // workspace slot of chunk 0
+    auto vidx = [&](int c) { return ws.vunit(wslot0 + min(c, c_end - 1), h); };
+    auto kidx = [&](int c) { return ws.kunit(wslot0 + min(c, c_end - 1), j); };
     const size_t vstride = (size_t)h_v * kDim;                // elements between token rows of v
     // chunk c's operands; chunks past the last one are clamped to it
     auto src_of = [&](int c) {
         const int cc = min(c, c_end - 1);
         const int t0 = start + kChunk * cc;
         ChunkSrc s;
-        s.vu = ws.vunit(slot0 + cc, h);
-        s.ku = ws.kunit(slot0 + cc, j);
+        s.vu = ws.vunit(wslot0 + cc, h);
+        s.ku = ws.kunit(wslot0 + cc, j);
         s.vrow = v + (size_t)t0 * vstride + (size_t)h * kDim;
         s.len = min(kChunk, end - t0);
         return s;
@@ -632,6 +644,13 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     H[i][e] = sa.hstart[gbase + (size_t)(16 * i + 4 * gq + e) * kDim + col];
+        } else if (!kSeg && c_begin > 0) {
+            // carried over from the launch that ran the chunks before
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    H[i][e] = sa.carry[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col];
         } else if (s0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -672,6 +691,11 @@ __global__ __launch_bounds__(state_threads(kMode)) void gdn_chunk_state(
             for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) dst[(size_t)(16 * i + 4 * gq + e) * kDim + col] = H[i][e];
+        } else if (!kSeg && c_end < nchunks) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sa.carry[sbase + (size_t)(16 * i + 4 * gq + e) * kDim + col] = H[i][e];
         } else if (s_final && sg == nseg - 1) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -878,6 +902,34 @@ static int state_cus() {
 // Workspace intermediates above which prep streams its stores.
 constexpr size_t kStreamWorkspaceBytes = (size_t)160 << 20;
 
+// The whole-sequence recurrence (single tiles, or tile pairs once the tiles
+// outnumber the CUs) over the chunk slots sa.slot_lo .. sa.slot_hi - 1.
+static void launch_state_whole(const int32_t* cu, int n_seqs, int h_v, const uint16_t* v, const float* s0,
+                               float* s_final, float* out, float* chunk_states, const ChunkWorkspace& ws,
+                               const SegArgs& sa, hipStream_t stream) {
+    const int units = n_seqs * h_v;
+    const dim3 grid(state_grid(units, 8));
+    if (chunk_states)
+        hipLaunchKernelGGL(gdn_chunk_state<kModeWholeSnap>, grid, dim3(state_threads(kModeWholeSnap)), 0, stream,
+                           cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
+    else if (8 * units > state_cus())
+        // more tiles than CUs: the workgroups run in rounds, and a pair of
+        // tiles sharing one copy ring halves them
+        hipLaunchKernelGGL(gdn_chunk_state<kModeWholePair>, dim3(state_grid(units, 4)),
+                           dim3(state_threads(kModeWholePair)), 0, stream,
+                           cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
+    else
+        hipLaunchKernelGGL(gdn_chunk_state<kModeWhole>, grid, dim3(state_threads(kModeWhole)), 0, stream,
+                           cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
+}
+
+// Chunk slots per range when one long sequence runs range by range: as many
+// as give one full round of prep workgroups (four per CU), a multiple of 8.
+static int range_slots(int h_qk, int h_v) {
+    const int per_slot = h_v / prep_heads_per_workgroup(h_qk, h_v);   // prep workgroups per chunk slot
+    return max(8, (4 * state_cus() / per_slot) & ~7);
+}
+
 hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* g, const float* beta, const int32_t* cu,
                             int n_seqs, int64_t total_tokens, int h_qk, int h_v,
@@ -893,10 +945,43 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
                                                            kGElems * sizeof(float)) +
                                             (size_t)h_qk * (kKtElems + kQfElems) * sizeof(f16));
     const bool stream_inter = inter > kStreamWorkspaceBytes;
+
+    // One sequence whose intermediates outgrow the last-level cache runs
+    // range by range: prep of a range of chunk slots, then the recurrence
+    // over them, the state handed from range to range in fp32 through a
+    // carry region, so that each range's intermediates are written into and
+    // read from the cache, and the next range overwrites them there.  The
+    // arithmetic is that of the single pass, bit for bit.  A range is one
+    // full round of prep workgroups (64 chunks at 32 value / 16 q/k heads),
+    // so that no round runs part-empty.  Measured at T = 131072: 2.84 ->
+    // 2.47 ms per layer cold (single pass: prep with streaming stores, then
+    // the recurrence with every operand from HBM).  The carry region follows
+    // the range's TU units in the workspace, which is sized for every slot.
+    if (stage_mask == 3 && !seg && !chunk_states && n_seqs == 1 && stream_inter) {
+        const int range = range_slots(h_qk, h_v);
+        const int nch = (int)((total_tokens + kChunk - 1) / kChunk);
+        const size_t carry_units = ((size_t)h_v * kDim * kDim * sizeof(float) + kTuElems * sizeof(f16) - 1) /
+                                   (kTuElems * sizeof(f16));                // TU units the carry takes
+        if ((size_t)range * h_v + carry_units <= (size_t)n_slots * h_v) {
+            SegArgs sa = {};
+            sa.stream_out = 1;
+            sa.carry = reinterpret_cast<float*>(ws.tu + (size_t)range * h_v * kTuElems);
+            for (int lo = 0; lo < nch; lo += range) {
+                const int hi = min(nch, lo + range);
+                const hipError_t e = launch_prep(q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws, lo, hi, stream);
+                if (e != hipSuccess) return e;
+                sa.slot_lo = lo;
+                sa.slot_hi = hi;
+                launch_state_whole(cu, n_seqs, h_v, v, s0, s_final, out, nullptr, ws, sa, stream);
+            }
+            return hipGetLastError();
+        }
+    }
+
     if ((stage_mask & 1) && total_tokens > 0) {
         const hipError_t e = stream_inter
-                                 ? launch_prep_stream(q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws, n_slots, stream)
-                                 : launch_prep(q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws, n_slots, stream);
+                                 ? launch_prep_stream(q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws, 0, n_slots, stream)
+                                 : launch_prep(q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws, 0, n_slots, stream);
         if (e != hipSuccess) return e;
     }
     if ((stage_mask & 2) && n_seqs > 0) {
@@ -909,21 +994,10 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
         // from HBM anyway, ordinary stores were faster (varlen batch 268 ->
         // 292 us, T = 131072 2.04 -> 2.18 ms with non-temporal ones).
         sa.stream_out = !stream_inter;
+        sa.slot_lo = 0;
+        sa.slot_hi = n_slots;
         if (!seg) {
-            const int units = n_seqs * h_v;
-            const dim3 grid(state_grid(units, 8));
-            if (chunk_states)
-                hipLaunchKernelGGL(gdn_chunk_state<kModeWholeSnap>, grid, dim3(state_threads(kModeWholeSnap)), 0, stream,
-                                   cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
-            else if (8 * units > state_cus())
-                // more tiles than CUs: the workgroups run in rounds, and a
-                // pair of tiles sharing one copy ring halves them
-                hipLaunchKernelGGL(gdn_chunk_state<kModeWholePair>, dim3(state_grid(units, 4)),
-                                   dim3(state_threads(kModeWholePair)), 0, stream,
-                                   cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
-            else
-                hipLaunchKernelGGL(gdn_chunk_state<kModeWhole>, grid, dim3(state_threads(kModeWhole)), 0, stream,
-                                   cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
+            launch_state_whole(cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa, stream);
         } else {
             sa.seg_chunks = seg->seg_chunks;
             sa.n_segslots = seg->n_segslots;

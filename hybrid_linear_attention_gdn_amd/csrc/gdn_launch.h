@@ -18,16 +18,20 @@ struct SegLaunch {
     float* maps;        // [n_segslots][h_v][2][128][128]
 };
 
-// Enqueues the intra-chunk preparation (one workgroup per chunk slot and
-// pair of value heads sharing a q/k head, or per value head when they do not
-// pair up) on `stream`, with ordinary or with non-temporal stores of the
-// intermediates.
+// Enqueues the intra-chunk preparation of chunk slots slot_lo .. slot_hi - 1
+// (one workgroup per chunk slot and pair of value heads sharing a q/k head,
+// or per value head when they do not pair up) on `stream`, with ordinary or
+// with non-temporal stores of the intermediates, which go to workspace slots
+// 0 .. slot_hi - slot_lo - 1.
 hipError_t launch_prep(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
-                       const int32_t* cu, int n_seqs, int h_qk, int h_v, const ChunkWorkspace& ws, int n_slots,
-                       hipStream_t stream);
+                       const int32_t* cu, int n_seqs, int h_qk, int h_v, const ChunkWorkspace& ws, int slot_lo,
+                       int slot_hi, hipStream_t stream);
+// Value heads per prep workgroup (two when the value heads of a q/k head
+// pair up, else one).
+int prep_heads_per_workgroup(int h_qk, int h_v);
 hipError_t launch_prep_stream(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
                               const float* beta, const int32_t* cu, int n_seqs, int h_qk, int h_v,
-                              const ChunkWorkspace& ws, int n_slots, hipStream_t stream);
+                              const ChunkWorkspace& ws, int slot_lo, int slot_hi, hipStream_t stream);
 
 // Enqueues the chunked prefill on `stream`: prep (stage bit 0) and the state
 // recurrence with the output (stage bit 1); chunk_states may be null; seg

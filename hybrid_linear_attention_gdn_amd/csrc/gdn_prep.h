@@ -264,8 +264,8 @@ __device__ __forceinline__ void offcol_solve(OffCol& o, float* A, int gq, int ln
 }
 
 // ---------------------------------------------------------------------------
-// Stage 1: intra-chunk preparation.  One workgroup per (chunk slot, group of
-// kH value heads of one q/k head); 36 KB of LDS
+// Stage 1: intra-chunk preparation.  One workgroup per (chunk slot of the
+// range slot_lo .. slot_hi - 1, group of kH value heads of one q/k head); 36 KB of LDS
 // and at most 128 registers per lane so that four workgroups share a CU.
 // The UT transform of each head runs in place in its A buffer: A, then
 // Tm = (I + A)^{-1}, read out as the fp16 fragments of Tm diag(beta).
@@ -275,13 +275,16 @@ template <bool kStream, int kH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void gdn_chunk_prep(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
-    const int32_t* __restrict__ cu, int n_seqs, int h_qk, int h_v, ChunkWorkspace ws)
+    const int32_t* __restrict__ cu, int n_seqs, int h_qk, int h_v, ChunkWorkspace ws, int slot_lo, int slot_hi)
 {
     static_assert(kH == 1 || kH == 2, "one or two value heads per workgroup");
-    const int slot = blockIdx.x;
+    // chunk slot slot_lo + x of the batch; its intermediates go to workspace
+    // slot x (the range's own slots)
+    const int ls = blockIdx.x;
+    const int slot = slot_lo + ls;
     const int h0 = kH * blockIdx.y;                   // the workgroup's first value head
     int seq, t0, len;
-    if (!resolve_slot(cu, n_seqs, slot, seq, t0, len)) return;
+    if (slot >= slot_hi || !resolve_slot(cu, n_seqs, slot, seq, t0, len)) return;
     const int j = h0 / ws.group;
     const bool first = h0 % ws.group == 0;            // holds the q/k head's first value head
 
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         Ab[hh] = Abuf[hh];
         Gs[hh] = Gsh[hh];
         Bs[hh] = Bsh[hh];
-        pdst[hh] = ws.p + ws.vunit(slot, h0 + hh) * kPElems;
+        pdst[hh] = ws.p + ws.vunit(ls, h0 + hh) * kPElems;
     }
 
     // ---- The decay inputs (wave hh for head hh, one lane per position),
@@ -383,7 +386,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         const float dc = exp_f(gc - x);
         Gsh[wave][lane] = x;
         Bsh[wave][lane] = b_in;
-        float* dg = ws.dg + ws.vunit(slot, h0 + wave) * kGElems;
+        float* dg = ws.dg + ws.vunit(ls, h0 + wave) * kGElems;
         put<kStream>(&dg[lane], lane == kChunk - 1 ? eg : dc);
         put<kStream>(&dg[kChunk + lane], eg);
     }
@@ -394,7 +397,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     //      transposed from the K rows.  The value heads of a q/k head share
     //      it; the workgroup with the first one writes it.
     if (first) {
-        f16* kdst = ws.kt + ws.kunit(slot, j) * kKtElems;
+        f16* kdst = ws.kt + ws.kunit(ls, j) * kKtElems;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int f = wave + 4 * it;
@@ -499,7 +502,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     for (int hh = 0; hh < kH; ++hh) {
         const int pt = wave;
         const int r = 16 * pt + ln;
-        f16* tdst = ws.tu + ws.vunit(slot, h0 + hh) * kTuElems;
+        f16* tdst = ws.tu + ws.vunit(ls, h0 + hh) * kTuElems;
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
             if (qq == 1 && pt < 2) continue;          // blocks (0, 1) and (1, 1) are zero
@@ -531,7 +534,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         for (int kk = 0; kk < 4; ++kk)
             *reinterpret_cast<u16x8*>(Qr + rsw(16 * wave + ln, 4 * kk + gq)) = __builtin_bit_cast(u16x8, qf[kk]);
         __syncthreads();
-        f16* qdst = ws.qf + ws.kunit(slot, j) * kQfElems;
+        f16* qdst = ws.qf + ws.kunit(ls, j) * kQfElems;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int row = 16 * p + ln;

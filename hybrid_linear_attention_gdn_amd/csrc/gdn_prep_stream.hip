@@ -7,15 +7,15 @@
 namespace gdn {
 
 hipError_t launch_prep_stream(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
-                              const int32_t* cu, int n_seqs, int h_qk, int h_v, const ChunkWorkspace& ws, int n_slots,
-                              hipStream_t stream)
+                              const int32_t* cu, int n_seqs, int h_qk, int h_v, const ChunkWorkspace& ws, int slot_lo,
+                              int slot_hi, hipStream_t stream)
 {
     if (prep_heads(h_qk, h_v) == 2)
-        hipLaunchKernelGGL((gdn_chunk_prep<true, 2>), dim3(slots_x8(n_slots), h_v / 2), dim3(256), 0, stream,
-                           q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws);
+        hipLaunchKernelGGL((gdn_chunk_prep<true, 2>), dim3(slots_x8(slot_hi - slot_lo), h_v / 2), dim3(256), 0, stream,
+                           q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws, slot_lo, slot_hi);
     else
-        hipLaunchKernelGGL((gdn_chunk_prep<true, 1>), dim3(slots_x8(n_slots), h_v), dim3(256), 0, stream,
-                           q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws);
+        hipLaunchKernelGGL((gdn_chunk_prep<true, 1>), dim3(slots_x8(slot_hi - slot_lo), h_v), dim3(256), 0, stream,
+                           q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws, slot_lo, slot_hi);
     return hipGetLastError();
 }
 

@@ -113,6 +113,12 @@ gdn_status gdn_chunk_fwd_workspace_size(const gdn_dims* dims, size_t* bytes);
  *                initial_state (in-place state update).
  *  workspace     device buffer of at least gdn_chunk_fwd_workspace_size bytes.
  * Empty sequences are allowed (their final state equals the initial state).
+ * A batch of one sequence whose intermediates exceed 160 MiB runs range by
+ * range: prep and the recurrence alternate over ranges of chunks (as many
+ * as one full round of prep workgroups covers), the state handed from range
+ * to range in fp32 through the workspace, so that each range's
+ * intermediates stay in the last-level cache.  The results are bit for bit
+ * those of the single pass (gdn_chunk_fwd_stages with mask 1, then 2).
  */
 gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
                          const float* g, const float* beta,

@@ -451,6 +451,52 @@ def test_streaming_prep_matches_ordinary_prep_bitwise():
         assert torch.equal(f1.cpu()[0], fin[n]), n
 
 
+@pytest.mark.parametrize("hqk,hv,T,init,final", [
+    (16, 32, 12037, True, True),      # 189 chunks: ranges of 64, 64, 61 (two value heads per prep workgroup)
+    (16, 32, 12037, False, False),    # zero initial state; no final state wanted (the carry still runs)
+    (8, 16, 24000, True, True),       # ranges of 128 chunks
+    (2, 6, 76013, True, True),        # three value heads per q/k head: one per prep workgroup, ranges of 168
+])
+def test_long_sequence_ranges_match_single_pass_bitwise(hqk, hv, T, init, final):
+    """One sequence whose intermediates exceed 160 MiB runs range by range
+    (prep of a range of chunk slots, then the recurrence over them, the state
+    carried in fp32 from range to range); the stage-by-stage call runs the
+    single pass (streaming prep over all slots, then one recurrence).  The
+    arithmetic is the same: outputs and final states equal bit for bit.  The
+    tail TU units of a poisoned workspace show that the ranged call used only
+    the first range's slots."""
+    import hybrid_linear_attention_gdn_amd as gdn
+    from gpu_util import workspace_for
+    x = gi.make_inputs([T], hqk, hv, 128, 128, seed=41, state_std=0.02 if init else None)
+    _print_case(f"ranges vs single pass H_qk={hqk} H_v={hv} T={T}", x)
+    d = DevInputs(x)
+    n_slots = gdn.gdn_chunk_state_slots(1, T, hqk, hv)
+    ws = workspace_for(x)
+    ws.fill_(0xFF)
+    out_r = torch.full((T, hv, 128), float("nan"), device="cuda")
+    fin_r = torch.full((1, hv, 128, 128), float("nan"), device="cuda") if final else None
+    gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.g, d.beta, d.cu, d.s0, out_r, fin_r, ws)
+    torch.cuda.synchronize()
+    tail = ws[(n_slots - 1) * hv * 6144:n_slots * hv * 6144]        # TU units of the last slot
+    assert bool((tail == 0xFF).all()), "the ranged path did not run"
+    out_s = torch.full((T, hv, 128), float("nan"), device="cuda")
+    fin_s = torch.full((1, hv, 128, 128), float("nan"), device="cuda") if final else None
+    gdn.gdn_chunk_fwd_stages(d.q, d.k, d.v, d.g, d.beta, d.cu, d.s0, out_s, fin_s, ws, 1)
+    gdn.gdn_chunk_fwd_stages(d.q, d.k, d.v, d.g, d.beta, d.cu, d.s0, out_s, fin_s, ws, 2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_r).all()
+    assert torch.equal(out_r, out_s)
+    if final:
+        assert torch.isfinite(fin_r).all()
+        assert torch.equal(fin_r, fin_s)
+    # and the oracle over the whole sequence
+    ro, rf, _ = oracle.forward_inputs(x, precision="f64")
+    o = out_r.cpu().numpy()
+    assert rel_l2(o, ro) <= OUT_TOL
+    if final:
+        assert rel_l2(fin_r.cpu().numpy(), rf) <= STATE_TOL
+
+
 def test_segmented_tile_pairs_match_single_tiles_bitwise():
     """At 32 value heads in segments of 8 chunks, the map and segment passes
     have more tiles than CUs and run as tile pairs; one head alone runs them
