@@ -107,13 +107,13 @@ MEASURED_TRAFFIC = {
     # warm and cold launches of the counter run)
     "gdn_chunk_state": {
         "sources": [CSRC + "gdn_chunk.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
-        "sources_sha256_prefix": "9086347b1e0a8780",
-        "bytes": (44848 * 2 + 66056) * 1024,
+        "sources_sha256_prefix": "cb940436363f794d",
+        "bytes": (44852 * 2 + 66056) * 1024,
     },
     "gdn_chunk_prep": {
         "sources": [CSRC + "gdn_prep.h", CSRC + "gdn_prep.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
-        "sources_sha256_prefix": "756fce83b5a71959",
-        "bytes": (32693 * 2 + 57456) * 1024,
+        "sources_sha256_prefix": "f2df0f1d6ebb9f09",
+        "bytes": (32695 * 2 + 57456) * 1024,
     },
 }
 

@@ -953,10 +953,12 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
     // read from the cache, and the next range overwrites them there.  The
     // arithmetic is that of the single pass, bit for bit.  A range is one
     // full round of prep workgroups (64 chunks at 32 value / 16 q/k heads),
-    // so that no round runs part-empty.  Measured at T = 131072: 2.84 ->
-    // 2.47 ms per layer cold (single pass: prep with streaming stores, then
-    // the recurrence with every operand from HBM).  The carry region follows
-    // the range's TU units in the workspace, which is sized for every slot.
+    // so that no round runs part-empty.  Measured at T = 131072 against the
+    // single pass (prep with streaming stores, then the recurrence with
+    // every operand from HBM): 2.65 -> 2.47 ms per layer back to back,
+    // 2.76-2.88 -> 2.68-2.75 ms after a cache flush, and 2.13 -> 1.94 ms at
+    // 16 value / 8 q/k heads.  The carry region follows the range's TU units
+    // in the workspace, which is sized for every slot.
     if (stage_mask == 3 && !seg && !chunk_states && n_seqs == 1 && stream_inter) {
         const int range = range_slots(h_qk, h_v);
         const int nch = (int)((total_tokens + kChunk - 1) / kChunk);
