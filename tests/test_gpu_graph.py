@@ -97,10 +97,15 @@ def test_in_place_decode_graph_replays_match_eager():
         assert torch.equal(st_g, st_e), rep
 
 
-def test_prefill_graph_replays_match_eager():
-    x = gi.prefill_4000()
+@pytest.mark.parametrize("case", ["prefill_4000", "ranges_12037"])
+def test_prefill_graph_replays_match_eager(case):
+    """The T = 4000 prefill (two launches), and one 12037-token sequence with
+    an initial state, whose 173 MB of intermediates make gdn_chunk_fwd run
+    it range by range (three ranges: six launches and the carried state)."""
+    x = (gi.prefill_4000() if case == "prefill_4000"
+         else gi.make_inputs([12037], 16, 32, 128, 128, seed=43, state_std=0.02))
     d = DevInputs(x)
-    print(f"[case] graph prefill T={x.total_tokens}", flush=True)
+    print(f"[case] graph prefill {case} T={x.total_tokens}", flush=True)
     shape_o = (x.total_tokens, x.h_v, 128)
     shape_f = (x.n_seqs, x.h_v, 128, 128)
     ws = workspace_for(x)
