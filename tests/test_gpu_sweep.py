@@ -1,0 +1,78 @@
+"""GPU parity over seeded random batches.
+
+Each case draws a batch shape from a fixed seed: head layout, number of
+sequences, lengths (with empty, one-token and chunk-boundary lengths mixed
+in), decay strength, whether q alone or q and k carry the 1/sqrt(d_k)
+scale, and whether there is an initial state.  The chunked prefill and the
+recurrent step are checked against the fp64 oracle with the same gates as
+the named workloads: whole-tensor, per (sequence, value head) and per
+boundary row.
+"""
+
+import numpy as np
+import pytest
+
+import gdn_inputs as gi
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from gpu_util import (OUT_TOL, STATE_TOL, DevInputs, check_detail, chunk_fwd,  # noqa: E402
+                      recurrent_step, rel_l2)
+
+# (q/k heads, value heads): one, two, three, four and eight value heads per
+# q/k head, including the odd groupings that run one value head per prep
+# workgroup
+HEADS = [(1, 1), (2, 4), (4, 8), (2, 6), (1, 3), (16, 32), (2, 16), (3, 12)]
+SPECIAL = [0, 1, 2, 63, 64, 65, 127, 128, 129]
+
+
+def _draw(seed):
+    rng = np.random.default_rng(7000 + seed)
+    hqk, hv = HEADS[seed % len(HEADS)]
+    n = int(rng.integers(1, 11))
+    lengths = [int(rng.choice(SPECIAL)) if rng.random() < 0.35 else int(rng.integers(1, 600))
+               for _ in range(n)]
+    g_mean = float(rng.choice([0.0, -2.0, 2.0]))
+    state = bool(rng.random() < 0.6)
+    k_scale = bool(rng.random() < 0.25)
+    x = gi.make_inputs(lengths, hqk, hv, 128, 128, seed=7000 + seed, g_mean=g_mean,
+                       state_std=0.02 if state else None, k_scale=k_scale, name=f"sweep{seed}")
+    return x, dict(heads=(hqk, hv), lengths=lengths, g_mean=g_mean, state=state, k_scale=k_scale)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_chunk_random_batch(seed):
+    x, desc = _draw(seed)
+    print(f"[case] sweep chunk {seed}: {desc}", flush=True)
+    out, fin = chunk_fwd(DevInputs(x), poison=True)
+    ro, rf, _ = oracle.forward_inputs(x, precision="f64")
+    o, f = out.cpu().numpy(), fin.cpu().numpy()
+    assert np.isfinite(o).all() and np.isfinite(f).all()
+    eo, ef = rel_l2(o, ro), rel_l2(f, rf)
+    print(f"[result] sweep chunk {seed}: out {eo:.3e} state {ef:.3e}", flush=True)
+    assert eo <= OUT_TOL and ef <= STATE_TOL
+    check_detail(f"sweep{seed}", o, ro, f, rf, x.cu_seqlens)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_recurrent_random_batch(seed):
+    """R requests of n tokens each (the step's fixed tokens per request), with
+    every per-token state saved, against the oracle's per-token states."""
+    rng = np.random.default_rng(8000 + seed)
+    hqk, hv = HEADS[seed % len(HEADS)]
+    R, n = int(rng.integers(1, 11)), int(rng.integers(1, 9))
+    x = gi.make_inputs([n] * R, hqk, hv, 128, 128, seed=8000 + seed, state_std=0.02,
+                       g_mean=float(rng.choice([0.0, -2.0])), name=f"sweep_step{seed}")
+    print(f"[case] sweep step {seed}: heads {hqk}/{hv} R={R} n={n}", flush=True)
+    d = DevInputs(x)
+    out, s_out, inter = recurrent_step(d, R, n, save=True)
+    ro, rf, rs = oracle.forward_inputs(x, precision="f64", record_states=True)
+    assert rel_l2(out.cpu().numpy(), ro) <= OUT_TOL
+    assert rel_l2(s_out.cpu().numpy(), rf) <= STATE_TOL
+    snaps = inter.cpu().numpy().reshape(rs.shape)
+    for t in range(R * n):
+        assert rel_l2(snaps[t], rs[t]) <= STATE_TOL, t
+    check_detail(f"sweep_step{seed}", out.cpu().numpy(), ro, s_out.cpu().numpy(), rf, x.cu_seqlens)
