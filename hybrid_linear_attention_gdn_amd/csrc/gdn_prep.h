@@ -194,7 +194,7 @@ __device__ __forceinline__ void store_a(float* Ab, const f32x4 (&av)[4], int gq,
 // in six dependent steps.  A product's accumulator Xc (lane (gq, ln) holds
 // X[4 gq + e][ln]) is X's B operand and X^T's A operand, so a power is also
 // formed transposed where the next product needs it as an A operand.  Split
-// fp16 operands (~2^-22 relative per product); for |N_rs| <= 1 every power
+// fp16 operands (~2^-21 relative per product); for |N_rs| <= 1 every power
 // and partial product stays below 2^14, inside fp16 range.
 __device__ __forceinline__ void diag_inverse(float* Ab, int ib, int gq, int ln) {
     const float* at = Ab + 16 * diag_row_block(ib) * kTA + 16 * diag_col_block(ib);   // at[t * kTA + r] = A_ii[r][t]
