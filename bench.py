@@ -107,13 +107,13 @@ MEASURED_TRAFFIC = {
     # warm and cold launches of the counter run)
     "gdn_chunk_state": {
         "sources": [CSRC + "gdn_chunk.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
-        "sources_sha256_prefix": "cb940436363f794d",
+        "sources_sha256_prefix": "42a19baa479b3e80",
         "bytes": (44852 * 2 + 66056) * 1024,
     },
     "gdn_chunk_prep": {
         "sources": [CSRC + "gdn_prep.h", CSRC + "gdn_prep.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
-        "sources_sha256_prefix": "f2df0f1d6ebb9f09",
-        "bytes": (32695 * 2 + 57456) * 1024,
+        "sources_sha256_prefix": "35ab5e43f7e424d5",
+        "bytes": (32688 * 2 + 57456) * 1024,
     },
 }
 
