@@ -497,6 +497,28 @@ def test_long_sequence_ranges_match_single_pass_bitwise(hqk, hv, T, init, final)
         assert rel_l2(fin_r.cpu().numpy(), rf) <= STATE_TOL
 
 
+def test_long_sequence_ranges_final_state_may_alias_initial():
+    """Range by range, the initial state is read by the first range's
+    launch only and the final state written by the last one's, so an
+    in-place update (final_state aliasing initial_state) gives the same bits
+    as separate buffers."""
+    import hybrid_linear_attention_gdn_amd as gdn
+    from gpu_util import workspace_for
+    x = gi.make_inputs([12037], 16, 32, 128, 128, seed=47, state_std=0.02)
+    _print_case("ranges, final state aliasing the initial state", x)
+    d = DevInputs(x)
+    ws = workspace_for(x)
+    out1 = torch.empty((x.total_tokens, 32, 128), device="cuda")
+    fin1 = torch.empty((1, 32, 128, 128), device="cuda")
+    gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.g, d.beta, d.cu, d.s0, out1, fin1, ws)
+    s = d.s0.clone()
+    out2 = torch.empty_like(out1)
+    gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.g, d.beta, d.cu, s, out2, s, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    assert torch.equal(fin1, s)
+
+
 def test_segmented_tile_pairs_match_single_tiles_bitwise():
     """At 32 value heads in segments of 8 chunks, the map and segment passes
     have more tiles than CUs and run as tile pairs; one head alone runs them
