@@ -5,6 +5,8 @@ behind the C ABI (``include/gdn.h``).  PyTorch provides device memory and the
 current stream.  The names mirror the C entry points:
 
 * ``gdn_chunk_fwd_workspace_size(n_seqs, total_tokens, h_qk, h_v)``
+* ``gdn_chunk_fwd_min_workspace_size(n_seqs, total_tokens, h_qk, h_v)`` (what
+  ``gdn_chunk_fwd`` accepts: one range's worth for one long sequence)
 * ``gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace)``
 * ``gdn_chunk_fwd_stages(..., stage_mask)`` (prep = 1, state with output = 2)
 * ``gdn_chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state)``
@@ -51,6 +53,7 @@ GDN_STATE_F16 = 1
 
 EXPORTED_SYMBOLS = (
     "gdn_chunk_fwd_workspace_size",
+    "gdn_chunk_fwd_min_workspace_size",
     "gdn_chunk_fwd",
     "gdn_chunk_fwd_stages",
     "gdn_chunk_state_slots",
@@ -97,6 +100,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     dims_p = ctypes.POINTER(gdn_dims)
     lib.gdn_chunk_fwd_workspace_size.argtypes = [dims_p, ctypes.POINTER(sz)]
     lib.gdn_chunk_fwd_workspace_size.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_min_workspace_size.argtypes = [dims_p, ctypes.POINTER(sz)]
+    lib.gdn_chunk_fwd_min_workspace_size.restype = ctypes.c_int
     lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, dims_p, vp, sz, vp]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
     lib.gdn_chunk_fwd_stages.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, dims_p, vp, sz, ctypes.c_int, vp]
@@ -233,6 +238,16 @@ def gdn_chunk_fwd_workspace_size(n_seqs: int, total_tokens: int, h_qk: int, h_v:
     out = ctypes.c_size_t(0)
     _check(lib, lib.gdn_chunk_fwd_workspace_size(ctypes.byref(dims), ctypes.byref(out)),
            "gdn_chunk_fwd_workspace_size")
+    return int(out.value)
+
+
+def gdn_chunk_fwd_min_workspace_size(n_seqs: int, total_tokens: int, h_qk: int, h_v: int,
+                                     d_k: int = 128, d_v: int = 128) -> int:
+    lib = load_library()
+    dims = make_dims(n_seqs, total_tokens, h_qk, h_v, d_k, d_v)
+    out = ctypes.c_size_t(0)
+    _check(lib, lib.gdn_chunk_fwd_min_workspace_size(ctypes.byref(dims), ctypes.byref(out)),
+           "gdn_chunk_fwd_min_workspace_size")
     return int(out.value)
 
 

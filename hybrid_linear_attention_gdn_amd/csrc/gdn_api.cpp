@@ -113,7 +113,10 @@ gdn_status gdn::chunk_fwd_impl(const void* q, const void* k, const void* v, cons
         GDN_REQUIRE_PTR(beta);
         GDN_REQUIRE_PTR(out);
     }
-    const Layout L = gdn::workspace_layout(dims, seg_chunks);
+    // one long sequence through gdn_chunk_fwd runs range by range, in a
+    // workspace laid out for one range
+    const int range = (stage_mask == 3 && !chunk_states && seg_chunks == 0) ? gdn::chunk_range(dims) : 0;
+    const Layout L = range ? gdn::range_layout(dims, range) : gdn::workspace_layout(dims, seg_chunks);
     if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes required)", L.total);
     if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
         return fail(GDN_ERR_MISALIGNED, "workspace is not 256-byte aligned");
@@ -153,7 +156,8 @@ gdn_status gdn::chunk_fwd_impl(const void* q, const void* k, const void* v, cons
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
         g, beta, cu_seqlens, dims->n_seqs, dims->total_tokens, dims->n_heads_qk, dims->n_heads_v,
         initial_state, out, final_state, chunk_states, ws, (int)slots, stage_mask,
-        seg_chunks > 0 ? &seg : nullptr, static_cast<hipStream_t>(stream));
+        seg_chunks > 0 ? &seg : nullptr, range, reinterpret_cast<float*>(base + L.carry),
+        static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "%s launch: %s", what, hipGetErrorString(e));
     return ok();
 }

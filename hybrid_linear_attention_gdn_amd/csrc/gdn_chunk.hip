@@ -899,9 +899,6 @@ static int state_cus() {
     return n;
 }
 
-// Workspace intermediates above which prep streams its stores.
-constexpr size_t kStreamWorkspaceBytes = (size_t)160 << 20;
-
 // The whole-sequence recurrence (single tiles, or tile pairs once the tiles
 // outnumber the CUs) over the chunk slots sa.slot_lo .. sa.slot_hi - 1.
 static void launch_state_whole(const int32_t* cu, int n_seqs, int h_v, const uint16_t* v, const float* s0,
@@ -923,61 +920,45 @@ static void launch_state_whole(const int32_t* cu, int n_seqs, int h_v, const uin
                            cu, n_seqs, h_v, v, s0, s_final, out, chunk_states, ws, sa);
 }
 
-// Chunk slots per range when one long sequence runs range by range: as many
-// as give one full round of prep workgroups (four per CU), a multiple of 8.
-static int range_slots(int h_qk, int h_v) {
-    const int per_slot = h_v / prep_heads_per_workgroup(h_qk, h_v);   // prep workgroups per chunk slot
-    return max(8, (4 * state_cus() / per_slot) & ~7);
-}
-
 hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* g, const float* beta, const int32_t* cu,
                             int n_seqs, int64_t total_tokens, int h_qk, int h_v,
                             const float* s0, float* out, float* s_final, float* chunk_states,
                             const ChunkWorkspace& ws, int n_slots, int stage_mask,
-                            const SegLaunch* seg, hipStream_t stream)
+                            const SegLaunch* seg, int range, float* carry, hipStream_t stream)
 {
     // Streaming stores of prep's intermediates once they outgrow what the
     // 256 MB last-level cache keeps for the state kernel.  Measured crossover
     // between 114 MB (T = 4000: ordinary stores 13 us faster per layer) and
     // 170 MB (T = 6000: streaming 2 us faster; 8-10% from 227 MB on).
-    const size_t inter = (size_t)n_slots * ((size_t)h_v * ((kTuElems + kPElems) * sizeof(f16) +
-                                                           kGElems * sizeof(float)) +
-                                            (size_t)h_qk * (kKtElems + kQfElems) * sizeof(f16));
-    const bool stream_inter = inter > kStreamWorkspaceBytes;
+    const bool stream_inter = (size_t)n_slots * chunk_slot_bytes(h_qk, h_v) > kStreamWorkspaceBytes;
 
     // One sequence whose intermediates outgrow the last-level cache runs
-    // range by range: prep of a range of chunk slots, then the recurrence
-    // over them, the state handed from range to range in fp32 through a
-    // carry region, so that each range's intermediates are written into and
-    // read from the cache, and the next range overwrites them there.  The
-    // arithmetic is that of the single pass, bit for bit.  A range is one
-    // full round of prep workgroups (64 chunks at 32 value / 16 q/k heads),
-    // so that no round runs part-empty.  Measured at T = 131072 against the
-    // single pass (prep with streaming stores, then the recurrence with
-    // every operand from HBM): 2.65 -> 2.47 ms per layer back to back,
-    // 2.76-2.88 -> 2.68-2.75 ms after a cache flush, and 2.13 -> 1.94 ms at
-    // 16 value / 8 q/k heads.  The carry region follows the range's TU units
-    // in the workspace, which is sized for every slot.
-    if (stage_mask == 3 && !seg && !chunk_states && n_seqs == 1 && stream_inter) {
-        const int range = range_slots(h_qk, h_v);
+    // range by range (the caller decides, and lays the workspace out for one
+    // range): prep of a range of chunk slots, then the recurrence over them,
+    // the state handed from range to range in fp32 through `carry`, so that
+    // each range's intermediates are written into and read from the cache,
+    // and the next range overwrites them there.  The arithmetic is that of
+    // the single pass, bit for bit.  A range is one full round of prep
+    // workgroups (64 chunks at 32 value / 16 q/k heads), so that no round
+    // runs part-empty.  Measured at T = 131072 against the single pass (prep
+    // with streaming stores, then the recurrence with every operand from
+    // HBM): 2.65 -> 2.47 ms per layer back to back, 2.76-2.88 -> 2.68-2.75
+    // ms after a cache flush, and 2.13 -> 1.94 ms at 16 value / 8 q/k heads.
+    if (range > 0) {
         const int nch = (int)((total_tokens + kChunk - 1) / kChunk);
-        const size_t carry_units = ((size_t)h_v * kDim * kDim * sizeof(float) + kTuElems * sizeof(f16) - 1) /
-                                   (kTuElems * sizeof(f16));                // TU units the carry takes
-        if ((size_t)range * h_v + carry_units <= (size_t)n_slots * h_v) {
-            SegArgs sa = {};
-            sa.stream_out = 1;
-            sa.carry = reinterpret_cast<float*>(ws.tu + (size_t)range * h_v * kTuElems);
-            for (int lo = 0; lo < nch; lo += range) {
-                const int hi = min(nch, lo + range);
-                const hipError_t e = launch_prep(q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws, lo, hi, stream);
-                if (e != hipSuccess) return e;
-                sa.slot_lo = lo;
-                sa.slot_hi = hi;
-                launch_state_whole(cu, n_seqs, h_v, v, s0, s_final, out, nullptr, ws, sa, stream);
-            }
-            return hipGetLastError();
+        SegArgs sa = {};
+        sa.stream_out = 1;
+        sa.carry = carry;
+        for (int lo = 0; lo < nch; lo += range) {
+            const int hi = min(nch, lo + range);
+            const hipError_t e = launch_prep(q, k, v, g, beta, cu, n_seqs, h_qk, h_v, ws, lo, hi, stream);
+            if (e != hipSuccess) return e;
+            sa.slot_lo = lo;
+            sa.slot_hi = hi;
+            launch_state_whole(cu, n_seqs, h_v, v, s0, s_final, out, nullptr, ws, sa, stream);
         }
+        return hipGetLastError();
     }
 
     if ((stage_mask & 1) && total_tokens > 0) {

@@ -26,9 +26,6 @@ struct SegLaunch {
 hipError_t launch_prep(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
                        const int32_t* cu, int n_seqs, int h_qk, int h_v, const ChunkWorkspace& ws, int slot_lo,
                        int slot_hi, hipStream_t stream);
-// Value heads per prep workgroup (two when the value heads of a q/k head
-// pair up, else one).
-int prep_heads_per_workgroup(int h_qk, int h_v);
 hipError_t launch_prep_stream(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
                               const float* beta, const int32_t* cu, int n_seqs, int h_qk, int h_v,
                               const ChunkWorkspace& ws, int slot_lo, int slot_hi, hipStream_t stream);
@@ -36,12 +33,16 @@ hipError_t launch_prep_stream(const uint16_t* q, const uint16_t* k, const uint16
 // Enqueues the chunked prefill on `stream`: prep (stage bit 0) and the state
 // recurrence with the output (stage bit 1); chunk_states may be null; seg
 // null runs each sequence's recurrence in one workgroup per column tile.
+// range > 0 runs one sequence range by range (both stages): prep and the
+// recurrence over `range` chunk slots at a time, the workspace regions
+// holding one range's slots and `carry` the state between ranges
+// ([h_v][128][128] fp32).
 hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* g, const float* beta, const int32_t* cu,
                             int n_seqs, int64_t total_tokens, int h_qk, int h_v,
                             const float* s0, float* out, float* s_final, float* chunk_states,
                             const ChunkWorkspace& ws, int n_slots, int stage_mask,
-                            const SegLaunch* seg, hipStream_t stream);
+                            const SegLaunch* seg, int range, float* carry, hipStream_t stream);
 
 // Body of the prefill entry points: host validation, workspace carving into
 // the regions above, and the launches (seg_chunks > 0: segment-parallel).

@@ -63,7 +63,7 @@ extern "C" gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const 
                                            const gdn_dims* dims,
                                            void* stream) {
     size_t need = 0;
-    gdn_status s = gdn_chunk_fwd_workspace_size(dims, &need);
+    gdn_status s = gdn_chunk_fwd_min_workspace_size(dims, &need);
     if (s != GDN_SUCCESS) return s;
     if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
         return gdn::fail(GDN_ERR_WORKSPACE,

@@ -563,9 +563,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 // no chunk and leave at once.
 __host__ __forceinline__ unsigned slots_x8(int n_slots) { return ((unsigned)n_slots + 7u) & ~7u; }
 
-// Value heads per prep workgroup: two when the value heads of a q/k head
-// pair up (an even number of them), else one.
-__host__ __forceinline__ int prep_heads(int h_qk, int h_v) { return (h_v / h_qk) % 2 == 0 ? 2 : 1; }
+// Value heads per prep workgroup (prep_value_heads in gdn_sizes.h).
+__host__ __forceinline__ int prep_heads(int h_qk, int h_v) { return prep_value_heads(h_qk, h_v); }
 
 }  // namespace
 

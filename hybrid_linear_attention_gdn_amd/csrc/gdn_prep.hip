@@ -6,8 +6,6 @@
 
 namespace gdn {
 
-int prep_heads_per_workgroup(int h_qk, int h_v) { return prep_heads(h_qk, h_v); }
-
 hipError_t launch_prep(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
                        const int32_t* cu, int n_seqs, int h_qk, int h_v, const ChunkWorkspace& ws, int slot_lo,
                        int slot_hi, hipStream_t stream)

@@ -29,4 +29,27 @@ constexpr size_t kJunkBytes = 1024;         // sink for the lanes of masked-off 
 // (LDS only, not a workspace region)
 constexpr size_t kWElems = 16 * 64 * 8;
 
+// Workspace bytes of one chunk slot (all heads): TU, P and the decay vectors
+// per value head, K^T and Q per q/k head.
+constexpr size_t chunk_slot_bytes(int h_qk, int h_v) {
+    return (size_t)h_v * ((kTuElems + kPElems) * 2 + kGElems * 4) + (size_t)h_qk * (kKtElems + kQfElems) * 2;
+}
+
+// Intermediates above which prep streams its stores past the caches, and
+// above which one sequence runs range by range.
+constexpr size_t kStreamWorkspaceBytes = (size_t)160 << 20;
+
+// Value heads per prep workgroup: two when the value heads of a q/k head
+// pair up (an even number of them), else one.
+constexpr int prep_value_heads(int h_qk, int h_v) { return (h_v / h_qk) % 2 == 0 ? 2 : 1; }
+
+// Chunk slots per range when one sequence runs range by range: one full
+// round of prep workgroups (four per CU on the 256 CUs of an MI355X), a
+// multiple of 8, at least 8.
+constexpr int range_slots(int h_qk, int h_v) {
+    const int per_slot = h_v / prep_value_heads(h_qk, h_v);      // prep workgroups per chunk slot
+    const int r = (4 * 256 / per_slot) & ~7;
+    return r < 8 ? 8 : r;
+}
+
 }  // namespace gdn

@@ -82,17 +82,49 @@ gdn_status check_dims(const gdn_dims* d) {
     return GDN_SUCCESS;
 }
 
-Layout workspace_layout(const gdn_dims* d, int32_t seg_chunks) {
-    const size_t units = (size_t)n_chunk_slots(d) * (size_t)d->n_heads_v;
-    const size_t qk_units = (size_t)n_chunk_slots(d) * (size_t)d->n_heads_qk;
-    Layout L;
-    size_t off = 0;
+namespace {
+
+// The intermediates' regions for `slots` chunk slots, then the sink.
+Layout slot_regions(const gdn_dims* d, int64_t slots, size_t& off) {
+    const size_t units = (size_t)slots * (size_t)d->n_heads_v;
+    const size_t qk_units = (size_t)slots * (size_t)d->n_heads_qk;
+    Layout L = {};
+    off = 0;
     L.tu = off; off += round_up(units * kTuElems * kHalf);
     L.p = off;  off += round_up(units * kPElems * kHalf);
     L.dg = off; off += round_up(units * kGElems * sizeof(float));
     L.kt = off; off += round_up(qk_units * kKtElems * kHalf);
     L.qf = off; off += round_up(qk_units * kQfElems * kHalf);
     L.junk = off; off += round_up(kJunkBytes);
+    return L;
+}
+
+}  // namespace
+
+Layout range_layout(const gdn_dims* d, int range) {
+    size_t off = 0;
+    Layout L = slot_regions(d, range, off);
+    L.maps = L.hstart = L.carry = off;
+    off += round_up((size_t)d->n_heads_v * kDim * kDim * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+int chunk_range(const gdn_dims* d) {
+    if (d->n_seqs != 1 ||
+        (size_t)n_chunk_slots(d) * chunk_slot_bytes(d->n_heads_qk, d->n_heads_v) <= kStreamWorkspaceBytes)
+        return 0;
+    const int64_t nch = (d->total_tokens + kChunk - 1) / kChunk;
+    const int range = (int)(nch < range_slots(d->n_heads_qk, d->n_heads_v) ? nch : range_slots(d->n_heads_qk, d->n_heads_v));
+    // (with few chunks of very many heads one range is the whole sequence,
+    //  and the single pass needs no more room)
+    return range_layout(d, range).total < workspace_layout(d).total ? range : 0;
+}
+
+Layout workspace_layout(const gdn_dims* d, int32_t seg_chunks) {
+    size_t off = 0;
+    Layout L = slot_regions(d, n_chunk_slots(d), off);
+    L.carry = off;
     L.maps = L.hstart = off;
     if (seg_chunks > 0) {
         const size_t per = (size_t)n_seg_slots(d, seg_chunks) * (size_t)d->n_heads_v * kDim * kDim * sizeof(float);
@@ -175,6 +207,15 @@ gdn_status gdn_chunk_fwd_workspace_size(const gdn_dims* dims, size_t* bytes) {
     const gdn_status s = gdn::check_dims(dims);
     if (s != GDN_SUCCESS) return s;
     *bytes = gdn::workspace_layout(dims).total;
+    return ok();
+}
+
+gdn_status gdn_chunk_fwd_min_workspace_size(const gdn_dims* dims, size_t* bytes) {
+    if (!bytes) return fail(GDN_ERR_INVALID_VALUE, "bytes is NULL");
+    const gdn_status s = gdn::check_dims(dims);
+    if (s != GDN_SUCCESS) return s;
+    const int range = gdn::chunk_range(dims);
+    *bytes = range ? gdn::range_layout(dims, range).total : gdn::workspace_layout(dims).total;
     return ok();
 }
 

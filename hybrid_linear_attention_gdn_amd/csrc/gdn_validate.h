@@ -32,9 +32,18 @@ int64_t n_seg_slots(const gdn_dims* d, int32_t seg_chunks);
 gdn_status check_dims(const gdn_dims* d);
 
 struct Layout {
-    size_t tu, p, dg, kt, qf, junk, maps, hstart, total;
+    size_t tu, p, dg, kt, qf, junk, maps, hstart, carry, total;
 };
+// Every chunk slot's intermediates (the single pass; with seg_chunks > 0
+// the segment maps and incoming states too).
 Layout workspace_layout(const gdn_dims* d, int32_t seg_chunks = 0);
+// Chunks per range when gdn_chunk_fwd runs the batch range by range (one
+// sequence whose intermediates exceed kStreamWorkspaceBytes: range_slots
+// of them, at most the sequence's chunks), else 0 (the single pass).
+int chunk_range(const gdn_dims* d);
+// The workspace of range-by-range execution: one range's intermediates and
+// the state carried between ranges.
+Layout range_layout(const gdn_dims* d, int range);
 
 // Device-content preconditions on host copies (see gdn_check_*_host in gdn.h).
 gdn_status check_cu_seqlens(const int32_t* cu, int32_t n_seqs, int64_t total_tokens);

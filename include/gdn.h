@@ -92,6 +92,17 @@ typedef struct {
 gdn_status gdn_chunk_fwd_workspace_size(const gdn_dims* dims, size_t* bytes);
 
 /*
+ * The smallest workspace gdn_chunk_fwd and gdn_chunk_fwd_noalloc accept for
+ * `dims` (gdn_chunk_fwd_workspace_size is always enough, and is what the
+ * other chunked entry points need).  It is smaller only for one sequence
+ * whose intermediates exceed 160 MiB, which gdn_chunk_fwd runs range by
+ * range: then it holds one range's intermediates (64 chunk slots at 32
+ * value / 16 q/k heads) and the fp32 state carried between ranges, e.g.
+ * 62 MB instead of 1.87 GB for 131072 tokens at 32 value / 16 q/k heads.
+ */
+gdn_status gdn_chunk_fwd_min_workspace_size(const gdn_dims* dims, size_t* bytes);
+
+/*
  * Chunked prefill (chunk length 64) over a packed batch of N sequences
  * (tokens cu_seqlens[n] .. cu_seqlens[n+1]-1).  Follows the three steps
  * of the "2080 Ti runs Qwen3.8-27B: a vLLM plugin" page, section 2, in two
@@ -111,14 +122,16 @@ gdn_status gdn_chunk_fwd_workspace_size(const gdn_dims* dims, size_t* bytes);
  *  out           float32 [T, H_v, d_v], written for every token.
  *  final_state   float32 [N, H_v, d_k, d_v] or NULL (not written); may alias
  *                initial_state (in-place state update).
- *  workspace     device buffer of at least gdn_chunk_fwd_workspace_size bytes.
+ *  workspace     device buffer of at least gdn_chunk_fwd_min_workspace_size
+ *                bytes (gdn_chunk_fwd_workspace_size is always enough).
  * Empty sequences are allowed (their final state equals the initial state).
  * A batch of one sequence whose intermediates exceed 160 MiB runs range by
  * range: prep and the recurrence alternate over ranges of chunks (as many
  * as one full round of prep workgroups covers), the state handed from range
  * to range in fp32 through the workspace, so that each range's
- * intermediates stay in the last-level cache.  The results are bit for bit
- * those of the single pass (gdn_chunk_fwd_stages with mask 1, then 2).
+ * intermediates stay in the last-level cache; the workspace then needs room
+ * for one range only.  The results are bit for bit those of the single
+ * pass (gdn_chunk_fwd_stages with mask 1, then 2).
  */
 gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
                          const float* g, const float* beta,
@@ -307,9 +320,10 @@ gdn_status gdn_recurrent_step_slots(const void* q, const void* k, const void* v,
  * The workspace is a fixed array of GDN_NOALLOC_SCRATCH_BYTES in the
  * library's device code, one per GPU, held until the process ends; the call
  * itself allocates nothing (no hipMalloc or hipFree, no allocating library
- * routine).  Batches whose gdn_chunk_fwd_workspace_size exceeds it return
- * GDN_ERR_WORKSPACE (128 MiB: up to about 9,100 tokens at 32 value / 16 q-k
- * heads; 4000 tokens use 57 MiB).  The first call on a device looks up the
+ * routine).  Batches whose gdn_chunk_fwd_min_workspace_size exceeds it
+ * return GDN_ERR_WORKSPACE (128 MiB: batches up to about 9,100 tokens at 32
+ * value / 16 q-k heads, 4000 tokens using 57 MiB, and one sequence of any
+ * length, which runs range by range in 62 MB).  The first call on a device looks up the
  * array's address there.  Every call on one GPU uses that GPU's single copy:
  * calls that overlap on one GPU (two streams, two threads) race and give
  * undefined results; serialise them.  Arguments, results and other errors as

@@ -97,6 +97,60 @@ def test_workspace_size_rejects_bad_dims(lib, d, code):
     assert lib.gdn_get_last_error()
 
 
+def min_ws_size(lib, d):
+    out = ctypes.c_size_t(0)
+    st = lib.gdn_chunk_fwd_min_workspace_size(ctypes.byref(d), ctypes.byref(out))
+    return st, out.value
+
+
+def test_min_workspace_size_for_one_long_sequence(lib):
+    """One sequence whose intermediates exceed 160 MiB runs range by range and
+    needs one range's intermediates (64 chunk slots at 32 value / 16 q/k
+    heads) plus the carried fp32 state; anything else needs the full
+    workspace."""
+    d = dims(n=1, T=131072, hqk=16, hv=32)
+    st, full = ws_size(lib, d)
+    st2, small = min_ws_size(lib, d)
+    assert st == 0 and st2 == 0
+    per_v = 3072 * 2 * 2 + 128 * 4
+    per_qk = 8192 * 2 * 2
+    expect = 64 * (32 * per_v + 16 * per_qk) + 1024 + 32 * 128 * 128 * 4
+    assert expect <= small < expect + 8 * 256
+    assert full > 1800e6 and small < 64e6
+    assert small <= gdn.GDN_NOALLOC_SCRATCH_BYTES          # the no-allocation entry point takes it
+    # 16 value / 8 q/k heads: ranges of 128 slots
+    st, small16 = min_ws_size(lib, dims(n=1, T=131072, hqk=8, hv=16))
+    per16 = 16 * per_v + 8 * per_qk
+    assert st == 0 and 128 * per16 <= small16 < 128 * per16 + 16 * 128 * 128 * 4 + 8 * 256 + 1024
+    # below 160 MiB of intermediates, or several sequences: the full workspace
+    for dd in (dims(n=1, T=4000, hqk=16, hv=32), dims(n=2, T=131072, hqk=16, hv=32),
+               dims(n=1, T=9400, hqk=16, hv=32)):
+        assert min_ws_size(lib, dd) == ws_size(lib, dd)
+    # very many heads over few chunks: one range would be the whole sequence
+    # and take more room than the single pass, so the single pass stays
+    dd = dims(n=1, T=128, hqk=1024, hv=2048)
+    assert min_ws_size(lib, dd) == ws_size(lib, dd)
+
+
+def test_min_workspace_size_is_what_gdn_chunk_fwd_checks(lib):
+    """gdn_chunk_fwd takes a range-sized workspace for one long sequence (and
+    refuses one byte less); the stage-by-stage call, which runs the single
+    pass, still needs the full size."""
+    d = dims(n=1, T=131072, hqk=16, hv=32)
+    small = min_ws_size(lib, d)[1]
+    assert chunk_call(lib, d, wsb=small - 1) == gdn.GDN_ERR_WORKSPACE
+    assert str(small) in lib.gdn_get_last_error().decode()
+    st = lib.gdn_chunk_fwd_stages(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, ctypes.byref(d),
+                                  FAKE, small, 1, None)
+    assert st == gdn.GDN_ERR_WORKSPACE
+    msg = lib.gdn_get_last_error().decode()
+    assert str(ws_size(lib, d)[1]) in msg
+    out = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_min_workspace_size(None, ctypes.byref(out)) == gdn.GDN_ERR_INVALID_VALUE
+    assert lib.gdn_chunk_fwd_min_workspace_size(ctypes.byref(d), None) == gdn.GDN_ERR_INVALID_VALUE
+    assert min_ws_size(lib, dims(dk=64, dv=64))[0] == gdn.GDN_ERR_NOT_SUPPORTED
+
+
 def test_workspace_size_null_args(lib):
     out = ctypes.c_size_t(0)
     assert lib.gdn_chunk_fwd_workspace_size(None, ctypes.byref(out)) == gdn.GDN_ERR_INVALID_VALUE

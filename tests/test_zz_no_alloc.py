@@ -3,7 +3,8 @@ fixed per-GPU scratch as its workspace gives the results of gdn_chunk_fwd
 with a caller workspace, bit for bit (same kernels, same workspace layout),
 on two calls in a row, the second on a smaller batch, so that whatever the
 first call left in the scratch cannot leak into the second; both also match
-the oracle.  Batches beyond the scratch are refused."""
+the oracle.  One long sequence runs range by range inside the scratch.
+Batches beyond the scratch are refused."""
 
 import numpy as np
 import pytest
@@ -61,3 +62,23 @@ def test_noalloc_in_place_state_and_rejects_oversized_batches():
     assert ei.value.status == gdn.GDN_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool(torch.all(yo == 7.0))
+
+
+def test_noalloc_runs_one_long_sequence_range_by_range():
+    """One sequence of 12037 tokens has 173 MB of intermediates, more than the
+    scratch, but gdn_chunk_fwd runs it range by range in a workspace of one
+    range (62 MB), which the scratch holds: the no-allocation call gives the
+    bits of gdn_chunk_fwd with a full caller workspace, then a small batch
+    after it still matches."""
+    x = gi.make_inputs([12037], 16, 32, 128, 128, seed=9, state_std=0.02)
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 12037, 16, 32) > gdn.GDN_NOALLOC_SCRATCH_BYTES
+    assert gdn.gdn_chunk_fwd_min_workspace_size(1, 12037, 16, 32) <= gdn.GDN_NOALLOC_SCRATCH_BYTES
+    d = DevInputs(x)
+    o1, f1 = _noalloc(d, d.s0)
+    o2, f2 = chunk_fwd(d, poison=True)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    y = gi.make_inputs([300, 65], 16, 32, 128, 128, seed=10, state_std=0.02)
+    dy = DevInputs(y)
+    o3, f3 = _noalloc(dy, dy.s0)
+    o4, f4 = chunk_fwd(dy, poison=True)
+    assert torch.equal(o3, o4) and torch.equal(f3, f4)
