@@ -107,12 +107,12 @@ MEASURED_TRAFFIC = {
     # warm and cold launches of the counter run)
     "gdn_chunk_state": {
         "sources": [CSRC + "gdn_chunk.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
-        "sources_sha256_prefix": "42a19baa479b3e80",
+        "sources_sha256_prefix": "5a5f01c49b081f41",
         "bytes": (44852 * 2 + 66056) * 1024,
     },
     "gdn_chunk_prep": {
         "sources": [CSRC + "gdn_prep.h", CSRC + "gdn_prep.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
-        "sources_sha256_prefix": "35ab5e43f7e424d5",
+        "sources_sha256_prefix": "dbda2d0008d2e21d",
         "bytes": (32688 * 2 + 57456) * 1024,
     },
 }
