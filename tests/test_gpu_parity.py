@@ -453,6 +453,8 @@ def test_streaming_prep_matches_ordinary_prep_bitwise():
 
 @pytest.mark.parametrize("hqk,hv,T,init,final", [
     (16, 32, 12037, True, True),      # 189 chunks: ranges of 64, 64, 61 (two value heads per prep workgroup)
+    (16, 32, 12288, True, True),      # 192 chunks: three full ranges
+    (16, 32, 12289, True, True),      # 193 chunks: the last range is one chunk of one token
     (16, 32, 12037, False, False),    # zero initial state; no final state wanted (the carry still runs)
     (8, 16, 24000, True, True),       # ranges of 128 chunks
     (2, 6, 76013, True, True),        # three value heads per q/k head: one per prep workgroup, ranges of 168
