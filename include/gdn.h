@@ -81,7 +81,8 @@ typedef struct {
 } gdn_dims;
 
 /*
- * Workspace bytes gdn_chunk_fwd needs for `dims` (device memory the caller
+ * Workspace bytes that gdn_chunk_fwd, gdn_chunk_fwd_stages and
+ * gdn_chunk_fwd_snapshots accept for `dims` (device memory the caller
  * allocates; contents undefined before and after a call).  It holds the
  * intra-chunk products of the chunkwise form that the preparation kernel
  * hands to the recurrence (Tm diag(beta), the output's intra-chunk matrix,
