@@ -54,7 +54,7 @@ if ROOT not in sys.path:
 PEAK_MFMA_F16 = 2.5e15      # dense fp16/bf16 matrix-core FLOP/s (MI355X)
 PEAK_HBM = 8.0e12           # HBM3E bytes/s (MI355X)
 PAGES_MS_T4000 = 1.35       # pages' hand-written CUDA kernel, 2x RTX 2080 Ti (context only)
-BOX_CPU_SHARE = 16          # host cores a one-GPU machine allots to the GPU's process
+CPU_SHARE_PER_GPU = 16      # host cores one GPU's process may use (the rest serve the node's other GPUs)
 
 H_V, H_QK, D, C = 32, 16, 128, 64
 STATE_BYTES = H_V * D * D * 4          # one fp32 state of one sequence (all value heads)
@@ -183,12 +183,12 @@ def time_graph(fn, n_inner, reps, torch):
 
 
 def host_cores() -> int:
-    """Cores this process may run on, up to the box's share for one GPU."""
+    """Cores this process may run on, up to one GPU's share of the host."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(n, BOX_CPU_SHARE))
+    return max(1, min(n, CPU_SHARE_PER_GPU))
 
 
 def cpu_baseline(x, budget_s: float):
@@ -536,7 +536,7 @@ def main():
                          "(gdn_chunk_fwd_segmented) at 32/16 and 16/8 heads, print one JSON line and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the layer on a single MI355X "
+        print("bench.py measures one GPU only: the layer runs on a single MI355X "
               "(heads or sequences would shard across GPUs with no exchange); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
