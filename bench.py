@@ -107,7 +107,7 @@ MEASURED_TRAFFIC = {
     # warm and cold launches of the counter run)
     "gdn_chunk_state": {
         "sources": [CSRC + "gdn_chunk.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
-        "sources_sha256_prefix": "5a5f01c49b081f41",
+        "sources_sha256_prefix": "8ec2fed4bfb52407",
         "bytes": (44852 * 2 + 66056) * 1024,
     },
     "gdn_chunk_prep": {

@@ -943,7 +943,7 @@ hipError_t launch_chunk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
     // workgroups (64 chunks at 32 value / 16 q/k heads), so that no round
     // runs part-empty.  Measured at T = 131072 against the single pass (prep
     // with streaming stores, then the recurrence with every operand from
-    // HBM), over several boxes: 2.76-2.88 -> 2.68-2.80 ms per layer after a
+    // HBM), on several MI355X: 2.76-2.88 -> 2.68-2.80 ms per layer after a
     // cache flush, -2% to +7% back to back, and 2.13 -> 1.94 ms at 16 value
     // / 8 q/k heads.
     if (range > 0) {
