@@ -107,13 +107,13 @@ MEASURED_TRAFFIC = {
     # warm and cold launches of the counter run)
     "gdn_chunk_state": {
         "sources": [CSRC + "gdn_chunk.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
-        "sources_sha256_prefix": "8ec2fed4bfb52407",
+        "sources_sha256_prefix": "1d1416fe02e3643c",
         "bytes": (44852 * 2 + 66056) * 1024,
     },
     "gdn_chunk_prep": {
         "sources": [CSRC + "gdn_prep.h", CSRC + "gdn_prep.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
-        "sources_sha256_prefix": "dbda2d0008d2e21d",
-        "bytes": (32688 * 2 + 57456) * 1024,
+        "sources_sha256_prefix": "e87cb96d2b813a07",
+        "bytes": (32679 * 2 + 57456) * 1024,
     },
 }
 

@@ -83,8 +83,12 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 // fp32 value split as hi + lo in fp16: hi = x rounded toward zero to fp16
 // (two values per packed conversion), lo = fp16(x - hi), where x - hi is
 // exact in fp32 and |x - hi| < ulp16(hi): 21 significant bits between them
-// for |x| in the fp16 normal range.  12 VALU instructions per four values
-// (a round-to-nearest hi took 16: the compiler converted it twice).
+// for |x| in the fp16 normal range.  lo is formed as fma(hi, m, x) with
+// m = -1 hidden from the optimiser, which otherwise folds the product into
+// a subtraction: the mixed-precision fma then takes hi as fp16 straight
+// from the packed register and rounds into an fp16 half, 7 VALU
+// instructions per four values instead of 12 (widen, subtract, pack), with
+// the same result (x - hi is exact, so either way it is rounded once).
 struct Split16 {
     f16x4 hi, lo;
 };
@@ -94,10 +98,14 @@ typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ Split16 split16(f32x4 x) {
     const f16x2 h01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(x[0], x[1]));
     const f16x2 h23 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(x[2], x[3]));
+    float m = -1.f;
+    asm("" : "+s"(m));
     Split16 s;
     s.hi = f16x4{h01[0], h01[1], h23[0], h23[1]};
-    s.lo = f16x4{static_cast<f16>(x[0] - static_cast<float>(h01[0])), static_cast<f16>(x[1] - static_cast<float>(h01[1])),
-                 static_cast<f16>(x[2] - static_cast<float>(h23[0])), static_cast<f16>(x[3] - static_cast<float>(h23[1]))};
+    s.lo = f16x4{static_cast<f16>(__builtin_fmaf(static_cast<float>(h01[0]), m, x[0])),
+                 static_cast<f16>(__builtin_fmaf(static_cast<float>(h01[1]), m, x[1])),
+                 static_cast<f16>(__builtin_fmaf(static_cast<float>(h23[0]), m, x[2])),
+                 static_cast<f16>(__builtin_fmaf(static_cast<float>(h23[1]), m, x[3]))};
     return s;
 }
 
