@@ -107,7 +107,7 @@ MEASURED_TRAFFIC = {
     # warm and cold launches of the counter run)
     "gdn_chunk_state": {
         "sources": [CSRC + "gdn_chunk.hip", CSRC + "gdn_device.h", CSRC + "gdn_sizes.h"],
-        "sources_sha256_prefix": "1d1416fe02e3643c",
+        "sources_sha256_prefix": "8d090f561ab555ed",
         "bytes": (44852 * 2 + 66056) * 1024,
     },
     "gdn_chunk_prep": {

@@ -15,12 +15,13 @@
 //
 // Every exponent is a difference G_r - G_s with s <= r, hence <= 0.
 //
-// Intermediates live in the caller's workspace in matrix-core fragment
-// order, written by each producer exactly as its consumer's operand needs:
-//   prep  -> -W as A fragments of (W H), U as accumulators of U' = U - W H,
-//            K^T as A fragments of the state update, Q and P as A fragments
-//            of the output's (Q H0) and (P U')
-//   state -> chunk state H0 and U' as B fragments of (Q H0) and (P U')
+// Prep's results live in the caller's workspace in matrix-core fragment
+// order, written exactly as their consumers' operands need: Tm diag(beta)
+// (TU), from which the state kernel forms -W (A fragments of W H0) and U
+// on chip; K^T as A fragments of the state update; Q and P as A fragments
+// of the output's (Q H0) and (P U'); the decay vectors.  Within the state
+// kernel the chain wave hands the chunk state H0 and U' to the output wave
+// through LDS, as B fragments of (Q H0) and (P U').
 // Contraction slot maps (lane group gq = lane / 16, slot s = 0..7):
 //   dim a(gq, s)   = 32 qq + 16 (s / 4) + 4 gq + s % 4   for K-step qq over d_k
 //   pos p(gq, s)   = 32 qq + 16 (s / 4) + 4 gq + s % 4   for K-step qq over positions
