@@ -43,7 +43,7 @@ def _draw(seed):
     return x, dict(heads=(hqk, hv), lengths=lengths, g_mean=g_mean, state=state, k_scale=k_scale)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(96))
 def test_chunk_random_batch(seed):
     x, desc = _draw(seed)
     print(f"[case] sweep chunk {seed}: {desc}", flush=True)
@@ -57,7 +57,7 @@ def test_chunk_random_batch(seed):
     check_detail(f"sweep{seed}", o, ro, f, rf, x.cu_seqlens)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(48))
 def test_recurrent_random_batch(seed):
     """R requests of n tokens each (the step's fixed tokens per request), with
     every per-token state saved, against the oracle's per-token states."""
