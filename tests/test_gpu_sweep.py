@@ -6,7 +6,9 @@ in), decay strength, whether q alone or q and k carry the 1/sqrt(d_k)
 scale, and whether there is an initial state.  The chunked prefill and the
 recurrent step are checked against the fp64 oracle with the same gates as
 the named workloads: whole-tensor, per (sequence, value head) and per
-boundary row.
+boundary row.  The slot-pool step is checked against the slot-pool oracle
+with the gates of its own tests: stored states within the state bound, every
+slot the call must not write unchanged bit for bit.
 """
 
 import numpy as np
@@ -21,6 +23,8 @@ torch = pytest.importorskip("torch")
 
 from gpu_util import (OUT_TOL, STATE_TOL, DevInputs, check_detail, chunk_fwd,  # noqa: E402
                       recurrent_step, rel_l2)
+from oracle.slots import slots_step  # noqa: E402
+from test_gpu_slots import check_pool, run_slots  # noqa: E402
 
 # (q/k heads, value heads): one, two, three, four and eight value heads per
 # q/k head, including the odd groupings that run one value head per prep
@@ -76,3 +80,40 @@ def test_recurrent_random_batch(seed):
     for t in range(R * n):
         assert rel_l2(snaps[t], rs[t]) <= STATE_TOL, t
     check_detail(f"sweep_step{seed}", out.cpu().numpy(), ro, s_out.cpu().numpy(), rf, x.cu_seqlens)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_slots_random_batch(seed):
+    """R requests of 0..M tokens (M up to 20: two staging blocks) over a pool
+    whose read and write slots are a random permutation of its slots, some
+    writes skipped (-1), the incoming column given by random device-side
+    accepted counts or column 0, fp32 or fp16 storage."""
+    rng = np.random.default_rng(9000 + seed)
+    hqk, hv = HEADS[seed % len(HEADS)]
+    R, M = int(rng.integers(1, 11)), int(rng.integers(1, 21))
+    lengths = [int(rng.integers(0, M + 1)) for _ in range(R)]
+    if sum(lengths) == 0:
+        lengths[0] = 1
+    f16 = bool(rng.random() < 0.5)
+    x = gi.make_inputs(lengths, hqk, hv, 128, 128, seed=9000 + seed, state_std=0.02,
+                       g_mean=float(rng.choice([0.0, -2.0])), name=f"sweep_slots{seed}")
+    P = R * (M + 1) + int(rng.integers(0, 8))
+    pool = gi.state_pool(x, P - R, f16=f16, seed=9000 + seed)
+    table = rng.permutation(P)[:R * (M + 1)].reshape(R, M + 1).astype(np.int32)
+    table[:, 1:][rng.random((R, M)) < 0.15] = -1
+    acc = None
+    if rng.random() < 0.7:
+        acc = rng.integers(0, M + 1, size=R).astype(np.int32)
+        acc[table[np.arange(R), acc] < 0] = 0       # the incoming column names a slot
+    print(f"[case] sweep slots {seed}: heads {hqk}/{hv} lengths {lengths} M={M} P={P} "
+          f"f16={f16} accepted={acc}", flush=True)
+    out, gpool = run_slots(x, pool, table, acc)
+    ro, rpool = slots_step(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, pool, table, acc)
+    assert np.isfinite(out).all()
+    e = rel_l2(out, ro)
+    print(f"[result] sweep slots {seed}: out {e:.3e}", flush=True)
+    assert e <= OUT_TOL
+    written = set()
+    for r in range(R):
+        written.update(int(t) for t in table[r, 1:1 + lengths[r]] if t >= 0)
+    check_pool(gpool, rpool, pool, written)
