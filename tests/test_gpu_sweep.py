@@ -24,6 +24,7 @@ torch = pytest.importorskip("torch")
 from gpu_util import (OUT_TOL, STATE_TOL, DevInputs, check_detail, chunk_fwd,  # noqa: E402
                       recurrent_step, rel_l2)
 from oracle.slots import slots_step  # noqa: E402
+from test_gpu_parity import _segmented, _snapshots  # noqa: E402
 from test_gpu_slots import check_pool, run_slots  # noqa: E402
 
 # (q/k heads, value heads): one, two, three, four and eight value heads per
@@ -33,11 +34,11 @@ HEADS = [(1, 1), (2, 4), (4, 8), (2, 6), (1, 3), (16, 32), (2, 16), (3, 12)]
 SPECIAL = [0, 1, 2, 63, 64, 65, 127, 128, 129]
 
 
-def _draw(seed):
+def _draw(seed, heads=HEADS, max_seqs=10, max_len=600):
     rng = np.random.default_rng(7000 + seed)
-    hqk, hv = HEADS[seed % len(HEADS)]
-    n = int(rng.integers(1, 11))
-    lengths = [int(rng.choice(SPECIAL)) if rng.random() < 0.35 else int(rng.integers(1, 600))
+    hqk, hv = heads[seed % len(heads)]
+    n = int(rng.integers(1, max_seqs + 1))
+    lengths = [int(rng.choice(SPECIAL)) if rng.random() < 0.35 else int(rng.integers(1, max_len))
                for _ in range(n)]
     g_mean = float(rng.choice([0.0, -2.0, 2.0]))
     state = bool(rng.random() < 0.6)
@@ -117,3 +118,48 @@ def test_slots_random_batch(seed):
     for r in range(R):
         written.update(int(t) for t in table[r, 1:1 + lengths[r]] if t >= 0)
     check_pool(gpool, rpool, pool, written)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_segmented_random_batch(seed):
+    """gdn_chunk_fwd_segmented on a random batch with a random segment length
+    (1 chunk up to one segment per sequence)."""
+    x, desc = _draw(200 + seed)
+    sc = int(np.random.default_rng(7500 + seed).choice([1, 2, 3, 5, 8, 16, 64]))
+    print(f"[case] sweep segmented {seed}: sc={sc} {desc}", flush=True)
+    out, fin = _segmented(x, DevInputs(x), sc)
+    ro, rf, _ = oracle.forward_inputs(x, precision="f64")
+    o, f = out.cpu().numpy(), fin.cpu().numpy()
+    assert np.isfinite(o).all() and np.isfinite(f).all()
+    eo, ef = rel_l2(o, ro), rel_l2(f, rf)
+    print(f"[result] sweep segmented {seed}: out {eo:.3e} state {ef:.3e}", flush=True)
+    assert eo <= OUT_TOL and ef <= STATE_TOL
+    check_detail(f"sweep_seg{seed}", o, ro, f, rf, x.cu_seqlens)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_snapshots_random_batch(seed):
+    """gdn_chunk_fwd_snapshots on a random batch (at most six value heads and
+    six sequences, so that the oracle's per-token states fit in host memory):
+    every chunk's state against the oracle's state after the same token, the
+    last one equal to the final state bit for bit, every slot no chunk maps
+    to left untouched."""
+    x, desc = _draw(300 + seed, heads=[(1, 1), (2, 4), (1, 3), (2, 6)], max_seqs=6, max_len=300)
+    print(f"[case] sweep snapshots {seed}: {desc}", flush=True)
+    out, fin, cs = _snapshots(x, DevInputs(x))
+    _, _, rs = oracle.forward_inputs(x, precision="f64", record_states=True)
+    cs_np, fin_np = cs.cpu().numpy(), fin.cpu().numpy()
+    written = set()
+    for n, L in enumerate(x.lengths):
+        start, L = int(x.cu_seqlens[n]), int(L)
+        nch = (L + 63) // 64
+        for c in range(nch):
+            slot = n + start // 64 + c
+            t_end = start + min(64 * (c + 1), L) - 1
+            assert rel_l2(cs_np[slot], rs[t_end]) <= STATE_TOL, (n, c)
+            written.add(slot)
+        if nch:
+            np.testing.assert_array_equal(cs_np[n + start // 64 + nch - 1], fin_np[n])
+    for slot in range(cs_np.shape[0]):
+        if slot not in written:
+            assert np.isnan(cs_np[slot]).all(), slot
