@@ -129,30 +129,39 @@ __device__ __forceinline__ void state_copy(Stage& st, const ChunkWorkspace& ws, 
     //  of this template reject the builtin, and typed 4-byte copies tripped a
     //  code-generation fault of the ROCm 7.2 compiler in this kernel)
     constexpr int kChains = Stage::kTiles;
-    const f16* ksrc = ws.kt + s.ku * kKtElems;
-    const f16* tsrc = ws.tu + s.vu * kTuElems;
-    const float* gsrc = ws.dg + s.vu * kGElems;
+    // Sources as a wave-uniform base plus a 32-bit per-lane byte offset, the
+    // addressing form that needs no 64-bit vector add per copy (measured: the
+    // copy wave's vector instructions per chunk 59 -> 28, recurrence after a
+    // cache flush at T = 4000 60.5 -> 58.2 us).  Row offsets stay below 2^32:
+    // at most 63 rows of at most 65535 value heads x 256 bytes.
+    const char* kb = reinterpret_cast<const char*>(ws.kt + s.ku * kKtElems);
+    const char* tb = reinterpret_cast<const char*>(ws.tu + s.vu * kTuElems);
+    const char* gb = reinterpret_cast<const char*>(ws.dg + s.vu * kGElems);
+    unsigned lo = 16u * lane;
+    asm("" : "+v"(lo));   // kept 32-bit: hoisted, it became a 64-bit offset added per copy
 #pragma unroll
     for (int piece = 0; piece < 16; ++piece)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ksrc + (piece * 64 + lane) * 8),
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kb + 4096 * (piece >> 2) + (lo + 1024u * (piece & 3))),
                                          reinterpret_cast<void*>(st.k + piece * 512), 16, 0, 0);
 #pragma unroll
     for (int piece = 0; piece < 6; ++piece)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tsrc + (piece * 64 + lane) * 8),
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tb + 4096 * (piece >> 2) + (lo + 1024u * (piece & 3))),
                                          reinterpret_cast<void*>(st.tu + piece * 512), 16, 0, 0);
 #pragma unroll
     for (int half = 0; half < 2; ++half)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gsrc + kChunk * half + lane),
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gb + ((lo >> 2) + 4u * kChunk * half)),
                                          reinterpret_cast<void*>(st.dg + kChunk * half), 4, 0, 0);
+    const unsigned rbytes = (unsigned)(row_stride * 2);
 #pragma unroll
-    for (int r = 0; r < kChains; ++r)
+    for (int r = 0; r < kChains; ++r) {
+        const char* vb = reinterpret_cast<const char*>(s.vrow + kVRowElems * ct[r]);
 #pragma unroll
         for (int piece = 0; piece < 2; ++piece) {
-            const int row = min(32 * piece + (lane >> 1), s.len - 1);
-            const uint16_t* src = s.vrow + (size_t)row * row_stride + kVRowElems * ct[r] + 8 * (lane & 1);
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+            const unsigned row = (unsigned)min(32 * piece + (lane >> 1), s.len - 1);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vb + (row * rbytes + 16u * (lane & 1))),
                                              reinterpret_cast<void*>(st.v[r] + piece * 512), 16, 0, 0);
         }
+    }
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -205,9 +214,10 @@ __device__ __forceinline__ void touch_shared(const ChunkWorkspace& ws, const Chu
 }
 
 __device__ __forceinline__ void touch_values(const ChunkSrc& s, int ct, size_t row_stride, int lane, float* sink) {
-    const int row = min(4 * (lane >> 2) + (ct & 3), s.len - 1);
-    const uint16_t* vl = s.vrow + (size_t)row * row_stride + kVRowElems * ct;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vl), reinterpret_cast<void*>(sink), 4, 0, 0);
+    const unsigned row = (unsigned)min(4 * (lane >> 2) + (ct & 3), s.len - 1);
+    const char* vb = reinterpret_cast<const char*>(s.vrow + kVRowElems * ct);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vb + row * (unsigned)(row_stride * 2)),
+                                     reinterpret_cast<void*>(sink), 4, 0, 0);
 }
 
 // Q's 16 fragments of one chunk, as sixteen 16-byte register loads.
